@@ -1,0 +1,293 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` raises AssertionError when the oracle departs from a value
+that does not come from the oracle itself: a hand-worked example, a closed
+form, a 50-digit brute force, an exhaustive brute-force ranking or the
+worked example printed on the SGLang page "logprob、finish reason 与 output
+processing" (section "logprob 的数值形态").  The pins read the oracle's
+functions through the module object at call time, so a test can plant a
+mistake in the oracle (monkeypatch) and check that some pin catches it.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+
+import oracle.logprob_oracle as LO
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ brute forces
+
+def brute_top_ids(xs, k):
+    """Repeated argmax over a Python list, scanning ids upward and replacing
+    only on a strictly larger value: ties keep the lowest id; -0.0 == +0.0."""
+    remaining = list(range(len(xs)))
+    out = []
+    for _ in range(min(k, len(xs))):
+        best = None
+        for i in remaining:
+            if best is None or xs[i] > xs[best]:
+                best = i
+        out.append(best)
+        remaining.remove(best)
+    return out
+
+
+def mp_logprobs(xs, dps=50):
+    """log p_i = x_i - log(sum_j e^{x_j}) at ``dps`` digits (finite xs only)."""
+    with mpmath.workdps(dps):
+        s = mpmath.fsum(mpmath.e ** mpmath.mpf(float(x)) for x in xs)
+        lse = mpmath.log(s)
+        return [mpmath.mpf(float(x)) - lse for x in xs], lse
+
+
+# ------------------------------------------------------------------ offsets / mapping
+
+def pin_offsets_hand_example():
+    # L = (3, 1, 2), echo = (T, F, T) -> counts (3, 1, 2), offsets (0, 3, 4, 6)
+    counts, out_off = LO.output_counts_and_offsets([0, 3, 4, 6], [True, False, True])
+    assert counts.dtype == np.uint32 and out_off.dtype == np.uint32
+    assert counts.tolist() == [3, 1, 2], counts
+    assert out_off.tolist() == [0, 3, 4, 6], out_off
+    # no echo: one row per request; all echo: the input offsets themselves
+    _, o = LO.output_counts_and_offsets([0, 5, 6, 9], [False] * 3)
+    assert o.tolist() == [0, 1, 2, 3], o
+    _, o = LO.output_counts_and_offsets([0, 5, 6, 9], [True] * 3)
+    assert o.tolist() == [0, 5, 6, 9], o
+    assert LO.kernel_row_offsets([0, 5, 6, 9], False).tolist() == [0, 1, 2, 3]
+    assert LO.kernel_row_offsets([0, 5, 6, 9], True).tolist() == [0, 5, 6, 9]
+
+
+def pin_mapping_hand_example():
+    # off (0,3,4,6), echo (T,F,T): request 0 reads rows 0,1,2 and predicts
+    # tokens[1], tokens[2], sampled[0]; request 1 reads row 3 -> sampled[1];
+    # request 2 reads rows 4,5 -> tokens[5], sampled[2].
+    tokens = [100, 101, 102, 103, 104, 105]
+    sampled = [900, 901, 902]
+    tasks = LO.row_tasks([0, 3, 4, 6], [True, False, True], [7, 3, 1], tokens, sampled, True)
+    got = [(t.src_row, t.chosen, t.top_n) for t in tasks]
+    want = [(0, 101, 7), (1, 102, 7), (2, 900, 7), (3, 901, 3), (4, 105, 1), (5, 902, 1)]
+    assert got == want, got
+    # a non-echo request with full logits reads its last row
+    tasks = LO.row_tasks([0, 3, 4, 6], [False, False, True], [1, 1, 1], tokens, sampled, True)
+    got = [(t.src_row, t.chosen) for t in tasks]
+    assert got == [(2, 900), (3, 901), (4, 105), (5, 902)], got
+    # no full logits: row n of next_token_logits, chosen = sampled
+    tasks = LO.row_tasks([0, 3, 4, 6], [False] * 3, [2, 2, 2], tokens, sampled, False)
+    assert [(t.src_row, t.chosen) for t in tasks] == [(0, 900), (1, 901), (2, 902)]
+    # L_n = 1 with echo: its only row predicts the sampled token
+    tasks = LO.row_tasks([0, 1], [True], [2], [7], [8], True)
+    assert [(t.src_row, t.chosen) for t in tasks] == [(0, 8)]
+
+
+# ------------------------------------------------------------------ log-softmax
+
+def pin_logsoftmax_bruteforce(rows):
+    """Oracle float64 log-softmax against a 50-digit evaluation."""
+    for xs in rows:
+        lp, lse = LO.log_softmax_f64(np.asarray(xs, dtype=np.float32))
+        ref, ref_lse = mp_logprobs(np.asarray(xs, dtype=np.float32).tolist())
+        assert abs(lse - float(ref_lse)) <= 1e-12 * max(1.0, abs(float(ref_lse))), (xs, lse)
+        for a, b in zip(lp, ref):
+            assert abs(a - float(b)) <= 1e-12 * max(1.0, abs(float(b))), (xs, a, b)
+
+
+def pin_logsoftmax_closed_forms():
+    # uniform row -> -ln V
+    for v in (1, 3, 111, 32000, 256000):
+        lp, _ = LO.log_softmax_f64(np.full(v, 0.75, dtype=np.float32))
+        assert np.allclose(lp, -math.log(v), rtol=0, atol=1e-12), v
+    assert abs(-math.log(256000) - (-12.452933)) < 1e-6
+    # two tokens at distance d: -log1p(e^-d) and -d - log1p(e^-d)
+    for a, b in ((1.0, 0.0), (5.5, -3.25), (-20.0, -20.5), (0.0, -60.0)):
+        lp, _ = LO.log_softmax_f64(np.array([a, b], dtype=np.float32))
+        d = a - b
+        assert abs(lp[0] - (-math.log1p(math.exp(-d)))) < 1e-14, (a, b, lp)
+        assert abs(lp[1] - (-d - math.log1p(math.exp(-d)))) < 1e-12, (a, b, lp)
+    # a row holding one finite entry among -inf: that entry has logprob 0
+    lp, _ = LO.log_softmax_f64(np.array([-np.inf, 2.5, -np.inf], dtype=np.float32))
+    assert lp[1] == 0.0 and np.isneginf(lp[0]) and np.isneginf(lp[2])
+
+
+def pin_logsoftmax_invariants(rows):
+    for xs in rows:
+        x = np.asarray(xs, dtype=np.float32)
+        lp, _ = LO.log_softmax_f64(x)
+        assert np.all(lp <= 1e-15), lp              # a logprob is <= 0
+        assert abs(np.sum(np.exp(lp)) - 1.0) < 1e-12
+        for c in (-50.0, 3.5, 1e3):
+            xs2 = x.astype(np.float64) + c            # exact in float64
+            lp2, _ = LO.log_softmax_f64(xs2)
+            assert np.allclose(lp, lp2, rtol=0, atol=1e-9 * max(1.0, abs(c))), c
+
+
+def pin_worked_example():
+    """The SGLang page's printed example: rebuilt rows give the printed values."""
+    with open(os.path.join(GOLDEN, "sglang_worked_example.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    for pos in (0, 1):
+        (t1, a), (t2, b) = g["top_logprobs"][pos]
+        rest = math.log((1.0 - math.exp(a) - math.exp(b)) / 8.0)
+        row = np.array([a, b] + [rest] * 8, dtype=np.float64)
+        lp, lse = LO.log_softmax_f64(row)
+        assert abs(lse) < 1e-12, lse
+        assert abs(lp[0] - a) < 1e-12 and abs(lp[1] - b) < 1e-12
+        # top-2 through the full row path (float32 input)
+        lp_out, id_out = LO.compute_row(row.astype(np.float32), 0, 2, 8)
+        assert id_out[:2].tolist() == [0, 1], id_out
+        assert abs(lp_out[0] - a) < 1e-6 and abs(lp_out[1] - b) < 1e-6, lp_out
+        assert id_out[7] == 0 and abs(lp_out[7] - g["token_logprobs"][pos]) < 1e-6
+        assert id_out[2:7].tolist() == [LO.PAD_ID] * 5
+    pct = g["stated_percent"]
+    assert round(100 * math.exp(g["top_logprobs"][1][0][1])) == pct[" cat"]
+    assert round(100 * math.exp(g["top_logprobs"][1][1][1])) == pct[" dog"]
+    (_, a), (_, b) = g["top_logprobs"][2]
+    assert math.exp(a) + math.exp(b) > 1.0        # position 3 is not a distribution
+
+
+# ------------------------------------------------------------------ ranking / rows
+
+def pin_ranking_exhaustive(alphabet, vmax):
+    for v in range(1, vmax + 1):
+        for combo in itertools.product(alphabet, repeat=v):
+            xs = list(combo)
+            x = np.array(xs, dtype=np.float32)
+            want_all = brute_top_ids(xs, v)
+            got_all = LO.rank_descending(x)[:v].tolist()
+            assert got_all == want_all, (xs, got_all, want_all)
+            finite = np.isfinite(x).any()
+            for k in range(0, 8):
+                lp_out, id_out = LO.compute_row(x, v - 1, k, 8)
+                kk = min(k, v)
+                if k == 0:
+                    assert id_out.tolist() == [LO.PAD_ID] * 8
+                    continue
+                assert id_out[:kk].tolist() == want_all[:kk], (xs, k, id_out)
+                assert id_out[kk:7].tolist() == [LO.PAD_ID] * (7 - kk)
+                assert np.all(np.isneginf(lp_out[kk:7]))
+                assert id_out[7] == v - 1
+                if finite:
+                    lp, _ = LO.log_softmax_f64(x)
+                    want = lp[want_all[:kk]].astype(np.float32)
+                    assert np.array_equal(lp_out[:kk], want), (xs, lp_out)
+
+
+def pin_ranking_special_cases():
+    rng = np.random.default_rng(7)
+    # all-equal row: ids 0..min(top_n, V)-1
+    for v in (1, 3, 7, 8, 111):
+        lp_out, id_out = LO.compute_row(np.full(v, -1.5, dtype=np.float32), 0, 7, 8)
+        kk = min(7, v)
+        assert id_out[:kk].tolist() == list(range(kk)), id_out
+        assert np.allclose(lp_out[:kk], -math.log(v), atol=1e-6)
+    # one boosted token ranks first
+    x = rng.standard_normal(1000).astype(np.float32)
+    x[417] = 50.0
+    _, id_out = LO.compute_row(x, 3, 7, 8)
+    assert id_out[0] == 417
+    # -inf never enters the top-k while enough finite entries exist
+    x = np.full(20, -np.inf, dtype=np.float32)
+    x[[3, 9, 11]] = [1.0, 2.0, 0.5]
+    lp_out, id_out = LO.compute_row(x, 0, 5, 8)
+    assert id_out[:5].tolist() == [9, 3, 11, 0, 1], id_out
+    assert np.all(np.isneginf(lp_out[3:5])) and np.isneginf(lp_out[7])
+    # the chosen token also among the top columns holds the same value
+    x = rng.standard_normal(50).astype(np.float32)
+    lp_out, id_out = LO.compute_row(x, int(np.argmax(x)), 3, 8)
+    assert id_out[0] == id_out[7] and lp_out[0] == lp_out[7]
+    # an all -inf row: NaN logprobs, ids by the tie rule
+    lp_out, id_out = LO.compute_row(np.full(4, -np.inf, dtype=np.float32), 2, 7, 8)
+    assert id_out[:4].tolist() == [0, 1, 2, 3] and np.all(np.isnan(lp_out[:4]))
+    assert id_out[4:7].tolist() == [LO.PAD_ID] * 3 and np.isnan(lp_out[7])
+
+
+def pin_ranking_invariants(rows, k=7):
+    for xs in rows:
+        x = np.asarray(xs, dtype=np.float32)
+        _, id_out = LO.compute_row(x, 0, k, 8)
+        ids = [i for i in id_out[:7].tolist() if i != LO.PAD_ID]
+        vals = x[ids].astype(np.float64)
+        assert np.all(np.diff(vals) <= 0), vals
+        for i in range(len(ids) - 1):
+            if vals[i] == vals[i + 1]:
+                assert ids[i] < ids[i + 1]
+        # nothing outside the list beats its last member
+        if ids:
+            last_v, last_i = vals[-1], ids[-1]
+            out = np.setdiff1d(np.arange(x.shape[0]), ids)
+            assert not np.any((x[out] > last_v) | ((x[out] == last_v) & (out < last_i)))
+
+
+def pin_batch_hand_example():
+    """End to end over a tiny batch, expected values from closed forms.
+
+    V = 4.  Request 0: echo, 3 tokens, top_n 2.  Request 1: no echo, 1 token,
+    top_n 0.  Request 2: echo, 2 tokens, top_n 1.  Row r holds a spike s_r at
+    id (r mod 4) over zeros, so lse_r = log(e^{s_r} + 3).
+    """
+    V = 4
+    spikes = [2.0, -1.0, 0.5, 3.0, 1.0, 4.0]
+    logits = np.zeros((6, V), dtype=np.float32)
+    for r, s in enumerate(spikes):
+        logits[r, r % V] = s
+    ntl = logits[[2, 3, 5]]
+    tokens = np.array([0, 1, 2, 3, 0, 2], dtype=np.uint32)
+    sampled = np.array([3, 1, 0], dtype=np.uint32)
+    lp, ids, off = LO.compute_log_probabilities_ragged(
+        np.array([0, 3, 4, 6], dtype=np.uint32), logits, ntl, tokens, sampled,
+        [2, 0, 1], [True, False, True])
+    assert off.tolist() == [0, 3, 4, 6]
+    lse = [math.log(math.exp(s) + 3.0) for s in spikes]
+    P = LO.PAD_ID
+    # (row, chosen, expected top ids)
+    expect = {0: (0, 1, [0, 1]), 1: (1, 2, [0, 2]), 2: (2, 3, [2, 0]),
+              4: (4, 2, [0]), 5: (5, 0, [1])}
+    for o, (r, chosen, top) in expect.items():
+        for j, t in enumerate(top):
+            want = (spikes[r] if t == r % V else 0.0) - lse[r]
+            assert ids[o, j] == t and abs(lp[o, j] - want) < 1e-6, (o, j, ids[o], lp[o])
+        assert ids[o, len(top):7].tolist() == [P] * (7 - len(top))
+        want = (spikes[r] if chosen == r % V else 0.0) - lse[r]
+        assert ids[o, 7] == chosen and abs(lp[o, 7] - want) < 1e-6, (o, ids[o], lp[o])
+    assert ids[3].tolist() == [P] * 8 and np.all(np.isneginf(lp[3]))   # top_n = 0
+
+
+def pin_errors():
+    ok = dict(input_row_offsets=np.array([0, 2, 3], np.uint32),
+              logits=np.zeros((3, 5), np.float32), next_token_logits=np.zeros((2, 5), np.float32),
+              tokens=np.array([1, 2, 3], np.uint32), sampled_tokens=np.array([4, 0], np.uint32),
+              batch_top_n=[1, 7], batch_echo=[True, False])
+    LO.compute_log_probabilities_ragged(**ok)
+
+    def expect(code, **kw):
+        args = dict(ok)
+        args.update(kw)
+        try:
+            LO.compute_log_probabilities_ragged(**args)
+        except LO.OracleError as e:
+            assert e.code == code, (code, e.code)
+            return
+        raise AssertionError(f"no error, expected {code}")
+
+    expect("LP_ERR_TOP_N_NEGATIVE", batch_top_n=[-1, 1])
+    expect("LP_ERR_TOP_N_TOO_LARGE", batch_top_n=[8, 1])
+    expect("LP_ERR_ECHO_NEEDS_LOGITS", logits=None)
+    expect("LP_ERR_OFFSETS", input_row_offsets=np.array([0, 3, 3], np.uint32))
+    expect("LP_ERR_OFFSETS", input_row_offsets=np.array([1, 2, 3], np.uint32))
+    expect("LP_ERR_SHAPE", logits=np.zeros((4, 5), np.float32))
+    expect("LP_ERR_SHAPE", logits=np.zeros((3, 6), np.float32))
+    expect("LP_ERR_SHAPE", batch_echo=[True])
+    expect("LP_ERR_TOKEN_RANGE", sampled_tokens=np.array([5, 0], np.uint32))
+    expect("LP_ERR_TOKEN_RANGE", tokens=np.array([1, 2, 9], np.uint32))
+    # levels widen the cap: 15 is fine at levels 4
+    args = dict(ok)
+    args["batch_top_n"] = [15, 1]
+    lp, ids, _ = LO.compute_log_probabilities_ragged(levels=4, **args)
+    assert lp.shape == (3, 16)

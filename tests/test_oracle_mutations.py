@@ -1,0 +1,141 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each mutant below replaces one oracle function with a plausible slip (a wrong
+sign, index, tie rule or dropped term).  The test passes only if running the
+pins against the mutated oracle raises AssertionError, i.e. the pins are
+strong enough to catch that class of mistake.  Everything runs on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle.logprob_oracle as LO
+import tests.oracle_pins as P
+
+_orig = {name: getattr(LO, name) for name in (
+    "rank_descending", "log_softmax_f64", "row_tasks", "output_counts_and_offsets",
+    "compute_row", "kernel_row_offsets")}
+
+
+def _rank_ties_high_id_first(row_f32):
+    x = np.asarray(row_f32, dtype=np.float32).astype(np.float64)
+    x = np.where(x == 0, 0.0, x)
+    n = x.shape[0]
+    return np.lexsort((-np.arange(n), -x))
+
+
+def _rank_negzero_below_poszero(row_f32):
+    x = np.asarray(row_f32, dtype=np.float32).astype(np.float64)
+    key = np.where((x == 0) & np.signbit(x), -1e-300, x)
+    return np.argsort(-key, kind="stable")
+
+
+def _lsm_no_shift(row):
+    x = np.asarray(row, dtype=np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        lse = np.log(np.sum(np.exp(x)))
+        return x - lse, float(lse)
+
+
+def _lsm_wrong_sign(row):
+    lp, lse = _orig["log_softmax_f64"](row)
+    return -lp, lse
+
+
+def _lsm_dropped_max(row):
+    x = np.asarray(row, dtype=np.float64)
+    m = np.max(x)
+    with np.errstate(invalid="ignore"):
+        lse = np.log(np.sum(np.exp(x - m)))
+        return x - lse, float(lse)
+
+
+def _tasks_chosen_same_position(off, echo, top_n, tokens, sampled, has_logits):
+    tasks = _orig["row_tasks"](off, echo, top_n, tokens, sampled, has_logits)
+    out, o = [], 0
+    counts, _ = _orig["output_counts_and_offsets"](off, echo)
+    for n, c in enumerate(counts):
+        length = int(off[n + 1] - off[n])
+        for k in range(int(c)):
+            p = length - int(c) + k
+            t = tasks[o]
+            out.append(LO.RowTask(t.src_row, int(tokens[int(off[n]) + p]), t.top_n))
+            o += 1
+    return out
+
+
+def _tasks_first_rows(off, echo, top_n, tokens, sampled, has_logits):
+    tasks = _orig["row_tasks"](off, echo, top_n, tokens, sampled, has_logits)
+    counts, _ = _orig["output_counts_and_offsets"](off, echo)
+    koff = _orig["kernel_row_offsets"](off, has_logits)
+    out, o = [], 0
+    for n, c in enumerate(counts):
+        for k in range(int(c)):
+            t = tasks[o]
+            out.append(LO.RowTask(int(koff[n]) + k, t.chosen, t.top_n))
+            o += 1
+    return out
+
+
+def _counts_swapped(off, echo):
+    return _orig["output_counts_and_offsets"](off, [not bool(e) for e in echo])
+
+
+def _row_pad_zero(row, chosen, top_n, cols):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols)
+    ids = ids.copy()
+    ids[ids == LO.PAD_ID] = 0
+    return lp, ids
+
+
+def _row_last_col_top1(row, chosen, top_n, cols):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols)
+    if top_n > 0:
+        lp = lp.copy()
+        lp[cols - 1] = lp[0]
+    return lp, ids
+
+
+def _row_ignores_top_n(row, chosen, top_n, cols):
+    return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols)
+
+
+MUTANTS = {
+    "ties_high_id_first": ("rank_descending", _rank_ties_high_id_first),
+    "negzero_ranks_low": ("rank_descending", _rank_negzero_below_poszero),
+    "lse_no_shift": ("log_softmax_f64", _lsm_no_shift),
+    "logprob_sign": ("log_softmax_f64", _lsm_wrong_sign),
+    "lse_dropped_max": ("log_softmax_f64", _lsm_dropped_max),
+    "chosen_same_position": ("row_tasks", _tasks_chosen_same_position),
+    "echo_first_rows": ("row_tasks", _tasks_first_rows),
+    "counts_swapped": ("output_counts_and_offsets", _counts_swapped),
+    "pad_id_zero": ("compute_row", _row_pad_zero),
+    "chosen_col_is_top1": ("compute_row", _row_last_col_top1),
+    "top_n_ignored": ("compute_row", _row_ignores_top_n),
+}
+
+
+def _run_all_pins():
+    rng = np.random.default_rng(3)
+    P.pin_offsets_hand_example()
+    P.pin_mapping_hand_example()
+    P.pin_logsoftmax_bruteforce([[0.5, -1.0, 3.0], [2.0]])
+    P.pin_logsoftmax_closed_forms()
+    P.pin_logsoftmax_invariants([rng.standard_normal(300).astype(np.float32)])
+    P.pin_worked_example()
+    P.pin_ranking_exhaustive([-np.inf, 0.0, 1.0], 4)
+    P.pin_ranking_exhaustive([-0.0, 0.0, 1.0], 4)
+    P.pin_ranking_special_cases()
+    P.pin_batch_hand_example()
+    P.pin_errors()
+
+
+def test_pins_pass_on_true_oracle():
+    _run_all_pins()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(LO, attr, fn)
+    with pytest.raises(AssertionError):
+        _run_all_pins()

@@ -1,0 +1,188 @@
+/*
+ * liblogprob -- ragged batched token log-probabilities on MI355X (gfx950).
+ *
+ * For every selected fp32 logits row the library computes, over the whole
+ * vocabulary, the log-softmax, the top-n (n <= 7) log-probabilities with their
+ * token ids, and the log-probability of the chosen token in one extra slot.
+ *
+ * Pages the contract follows:
+ *   [MAX] "MAX Python SDK 中 log_probabilities 模块解析：ragged 批量 Token 对数概率的
+ *         计算图构建与执行"
+ *   [SGL] "logprob、finish reason 与 output processing"
+ *
+ * Layout and conventions shared by every call:
+ *   - batch B requests; request n owns token rows [off[n], off[n+1]) of the
+ *     full logits ([MAX] §compute_log_probabilities_ragged, the row-offset
+ *     argument); L_n = off[n+1] - off[n] >= 1; T = off[B].
+ *   - output rows: an echo request gets L_n rows, any other request one row;
+ *     output_row_offsets = [0, cumsum(counts)] as uint32 ([MAX] §ragged 数据编排).
+ *   - each output row has C = 2^levels columns (8 at levels = 3): columns
+ *     0..C-2 hold the top-n log-probabilities in descending order of the raw
+ *     fp32 logit (lowest token id first among equal logits, -0.0 == +0.0);
+ *     the last column holds the chosen token ([MAX] §log_probabilities_ragged_graph,
+ *     §compute_top 的结果组装).  Columns at or beyond min(top_n, V) hold
+ *     (-inf, 0xFFFFFFFF); rows of top_n == 0 requests hold that padding in all
+ *     C columns and their logits are never read.
+ *   - echo row k of request n reads logits row off[n+1] - count_n + k and its
+ *     chosen token is the next prompt token tokens[off[n] + p + 1] (p the
+ *     prompt position of the row), or the sampled token for the request's last
+ *     row ([SGL] §input logprob 和 output logprob 来自哪里).  Without full
+ *     logits, request n reads row n of next_token_logits and its chosen token
+ *     is sampled_tokens[n].
+ *   - every device pointer is caller-allocated device memory; the library
+ *     allocates no device memory.  Calls never throw; they return lp_status.
+ *   - a logits row must hold no NaN or +inf; -inf entries are allowed and rank
+ *     lowest.  An all -inf row yields NaN log-probabilities.
+ */
+#ifndef LIBLOGPROB_H
+#define LIBLOGPROB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lp_plan lp_plan; /* opaque host object */
+
+typedef enum lp_status {
+    LP_OK = 0,
+    LP_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
+    LP_ERR_OFFSETS = 2,           /* off[0] != 0, or some L_n == 0 (offsets must strictly increase) */
+    LP_ERR_SHAPE = 3,             /* row counts or sizes disagree ([MAX] entry assertions) */
+    LP_ERR_TOP_N_NEGATIVE = 4,    /* some top_n < 0 ([MAX] §compute_top 的结果组装) */
+    LP_ERR_TOP_N_TOO_LARGE = 5,   /* some top_n > 2^levels - 1 ([MAX] §图支持的最大 top-n) */
+    LP_ERR_ECHO_NEEDS_LOGITS = 6, /* echo requested without full logits ([MAX] §echo 的前置条件) */
+    LP_ERR_TOKEN_RANGE = 7,       /* a token or sampled token >= vocab */
+    LP_ERR_UNSUPPORTED = 8,       /* levels != 3, or a split outside 1..64 */
+    LP_ERR_WORKSPACE = 9,         /* workspace NULL or smaller than the plan asks */
+    LP_ERR_HIP = 10,              /* a HIP runtime call failed; see lp_last_hip_error() */
+    LP_ERR_NOMEM = 11             /* host allocation failed */
+} lp_status;
+
+/* Facts about a plan (all host values). */
+typedef struct lp_plan_info {
+    uint32_t batch;           /* B */
+    uint32_t vocab;           /* V */
+    uint32_t levels;          /* 3 */
+    uint32_t columns;         /* 2^levels = 8 */
+    uint64_t out_rows;        /* R = output_row_offsets[B] */
+    uint64_t read_rows;       /* output rows whose request has top_n > 0 (logits rows read) */
+    uint32_t split;           /* vocabulary segments per row: 1 = single-pass row kernel,
+                                 > 1 = split-vocab partial kernel + merge kernel */
+    uint32_t has_logits;      /* 1 if full logits are given */
+    uint64_t workspace_bytes; /* device scratch lp_compute_ragged needs */
+} lp_plan_info;
+
+/*
+ * lp_plan_ragged -- host-only planning (no HIP call, no device memory).
+ *
+ * [MAX] §compute_log_probabilities_ragged and §ragged 数据编排: validates the
+ * per-request arguments, computes the echo-dependent output row counts and
+ * their uint32 offsets, and chooses the kernel variant (split).
+ *
+ *   batch              B (may be 0: nothing to compute)
+ *   vocab              V >= 1
+ *   levels             must be 3 (C = 8 columns, top_n <= 7)
+ *   input_row_offsets  host, B+1 uint32, off[0] = 0, strictly increasing
+ *   batch_echo         host, B bytes, nonzero = echo
+ *   batch_top_n        host, B int32 in [0, 7]
+ *   has_logits         nonzero if full (T, V) logits will be given; then
+ *                      logits_rows must equal T.  Zero: only (B, V)
+ *                      next_token_logits exist and no request may echo.
+ *   plan_out           receives a new plan; free it with lp_plan_destroy
+ *   output_row_offsets host out, B+1 uint32 (may be NULL)
+ *   out_rows           host out, R (may be NULL)
+ *   workspace_bytes    host out, bytes of device workspace (may be NULL)
+ *
+ * On error *plan_out is set to NULL and nothing else is written.
+ */
+lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
+                         const uint32_t *input_row_offsets, const uint8_t *batch_echo,
+                         const int32_t *batch_top_n, int has_logits, uint64_t logits_rows,
+                         lp_plan **plan_out, uint32_t *output_row_offsets,
+                         uint64_t *out_rows, uint64_t *workspace_bytes);
+
+/* Fills *info.  LP_ERR_NULL_ARG if either pointer is NULL. */
+lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info);
+
+/*
+ * Overrides the plan's split (vocabulary segments per row, 1..64) and updates
+ * its workspace size.  The result does not depend on the split beyond fp32
+ * rounding of the log-probabilities: ids and offsets are identical.
+ */
+lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
+
+/*
+ * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of
+ * 4 uint32 to desc_out: {logits row read, chosen token, top_n, 0}, in output
+ * row order.  tokens: host, T uint32 (may be NULL when no request echoes);
+ * sampled_tokens: host, B uint32.  LP_ERR_TOKEN_RANGE if an id >= V.
+ */
+lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
+                              const uint32_t *sampled_tokens, uint32_t *desc_out);
+
+/*
+ * lp_stage_ragged -- builds the row descriptors on the host (tokens and
+ * sampled tokens are host arrays, as in [MAX] §compute_log_probabilities_ragged)
+ * and enqueues their copy into the device workspace on `stream` (a
+ * hipStream_t; NULL = default stream).  The plan's pinned staging buffer is
+ * reused; a second call waits until the previous copy from it has finished.
+ */
+lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens,
+                          const uint32_t *sampled_tokens, void *workspace,
+                          uint64_t workspace_bytes, void *stream);
+
+/*
+ * lp_launch_ragged -- enqueues the device work on `stream`, reading the
+ * descriptors a previous lp_stage_ragged put in `workspace`.
+ *
+ *   logits             device, (T, V) fp32 row-major contiguous; NULL iff the
+ *                      plan has no full logits
+ *   next_token_logits  device, (B, V) fp32 row-major; read only when the plan
+ *                      has no full logits (may be NULL otherwise)
+ *   out_logprobs       device out, (R, 8) fp32
+ *   out_token_ids      device out, (R, 8) uint32
+ *   workspace          device, >= workspace_bytes of the plan, 256-byte aligned
+ *
+ * Enqueue only: no host synchronisation.  Device buffers must stay alive
+ * until the stream reaches the end of the enqueued work.
+ */
+lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
+                           const float *next_token_logits, float *out_logprobs,
+                           uint32_t *out_token_ids, void *workspace,
+                           uint64_t workspace_bytes, void *stream);
+
+/* lp_compute_ragged = lp_stage_ragged followed by lp_launch_ragged. */
+lp_status lp_compute_ragged(lp_plan *plan, const float *logits,
+                            const float *next_token_logits, const uint32_t *tokens,
+                            const uint32_t *sampled_tokens, float *out_logprobs,
+                            uint32_t *out_token_ids, void *workspace,
+                            uint64_t workspace_bytes, void *stream);
+
+/* Frees the plan.  Waits for a pending descriptor copy from its staging
+ * buffer first.  NULL is a no-op. */
+void lp_plan_destroy(lp_plan *plan);
+
+/* Static text for a status ("LP_OK", "LP_ERR_SHAPE", ...). */
+const char *lp_status_string(lp_status status);
+
+/* The hipError_t of the last failing HIP call in this thread (0 if none). */
+int lp_last_hip_error(void);
+
+/*
+ * Measurement aid: a plain streaming read of n fp32 values (each read once,
+ * 16-byte loads) that writes one partial sum per workgroup into
+ * partial_out[grid].  It gives the practical HBM read ceiling on the same
+ * bytes the log-probability kernels stream.  *grid_out receives the
+ * workgroup count used (partial_out must hold that many floats: at most 65536).
+ */
+lp_status lp_bench_stream_read(const float *x, uint64_t n, float *partial_out,
+                               uint32_t *grid_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLOGPROB_H */

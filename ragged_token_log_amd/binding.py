@@ -1,0 +1,298 @@
+"""Thin ctypes binding over liblogprob (argument marshalling only).
+
+Every step of the computation runs in the library: the host plan in its C++
+code and everything per logit in its HIP kernels.  PyTorch is used here for
+device memory and the stream, nothing else.  If the library is not built,
+loading raises immediately; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblogprob.so")
+
+STATUS_NAMES = {
+    0: "LP_OK", 1: "LP_ERR_NULL_ARG", 2: "LP_ERR_OFFSETS", 3: "LP_ERR_SHAPE",
+    4: "LP_ERR_TOP_N_NEGATIVE", 5: "LP_ERR_TOP_N_TOO_LARGE", 6: "LP_ERR_ECHO_NEEDS_LOGITS",
+    7: "LP_ERR_TOKEN_RANGE", 8: "LP_ERR_UNSUPPORTED", 9: "LP_ERR_WORKSPACE",
+    10: "LP_ERR_HIP", 11: "LP_ERR_NOMEM",
+}
+
+# every symbol include/liblogprob.h declares
+EXPORTED = (
+    "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_descriptors",
+    "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
+    "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
+)
+
+LEVELS = 3
+COLUMNS = 8
+MAX_TOP_N = 7
+PAD_ID = 0xFFFFFFFF
+
+
+class LogprobError(RuntimeError):
+    """A non-OK lp_status from the library."""
+
+    def __init__(self, code: int, where: str, hip_error: int = 0):
+        self.code = code
+        self.name = STATUS_NAMES.get(code, f"status {code}")
+        extra = f" (hipError {hip_error})" if hip_error else ""
+        super().__init__(f"{where}: {self.name}{extra}")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_uint32), ("vocab", ctypes.c_uint32),
+        ("levels", ctypes.c_uint32), ("columns", ctypes.c_uint32),
+        ("out_rows", ctypes.c_uint64), ("read_rows", ctypes.c_uint64),
+        ("split", ctypes.c_uint32), ("has_logits", ctypes.c_uint32),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Loads liblogprob.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m ragged_token_log_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
+    P = ctypes.POINTER
+    lib.lp_plan_ragged.argtypes = [u32, u32, u32, P(u32), P(ctypes.c_uint8), P(i32),
+                                   ctypes.c_int, u64, P(vp), P(u32), P(u64), P(u64)]
+    lib.lp_plan_get_info.argtypes = [vp, P(PlanInfo)]
+    lib.lp_plan_set_split.argtypes = [vp, u32]
+    lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
+    lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
+    lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
+    lib.lp_compute_ragged.argtypes = [vp, vp, vp, P(u32), P(u32), vp, vp, vp, u64, vp]
+    lib.lp_plan_destroy.argtypes = [vp]
+    lib.lp_plan_destroy.restype = None
+    lib.lp_status_string.argtypes = [ctypes.c_int]
+    lib.lp_status_string.restype = ctypes.c_char_p
+    lib.lp_last_hip_error.argtypes = []
+    lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
+    for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
+                 "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
+                 "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        hip = load().lp_last_hip_error() if status == 10 else 0
+        raise LogprobError(status, where, hip)
+
+
+def _u32(a, n=None):
+    arr = np.ascontiguousarray(np.asarray(a), dtype=np.uint32) if a is not None else None
+    if arr is not None and n is not None and arr.shape[0] != n:
+        raise LogprobError(3, "array length")
+    return arr
+
+
+def _ptr(arr, ctype):
+    if arr is None:
+        return None
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _dev_ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    return ctypes.c_void_p(stream.cuda_stream) if stream is not None else None
+
+
+class Plan:
+    """lp_plan_ragged: host planning for one ragged batch (no GPU needed)."""
+
+    def __init__(self, input_row_offsets, batch_echo, batch_top_n, vocab: int,
+                 has_logits: bool, logits_rows: int | None = None, levels: int = LEVELS):
+        lib = load()
+        off = np.ascontiguousarray(np.asarray(input_row_offsets), dtype=np.uint32)
+        if off.ndim != 1 or off.shape[0] < 1:
+            raise LogprobError(3, "input_row_offsets must be 1-D with batch+1 entries")
+        batch = off.shape[0] - 1
+        echo = np.ascontiguousarray(np.asarray(batch_echo, dtype=bool).astype(np.uint8))
+        top_n = np.ascontiguousarray(np.asarray(batch_top_n), dtype=np.int32)
+        if echo.shape[0] != batch or top_n.shape[0] != batch:
+            raise LogprobError(3, "batch_echo / batch_top_n length != batch")
+        if logits_rows is None:
+            logits_rows = int(off[-1]) if has_logits else batch
+        self._lib = lib
+        self._h = ctypes.c_void_p()
+        out_off = np.zeros(batch + 1, dtype=np.uint32)
+        rows = ctypes.c_uint64()
+        ws = ctypes.c_uint64()
+        _check(lib.lp_plan_ragged(batch, int(vocab), int(levels), _ptr(off, ctypes.c_uint32),
+                                  _ptr(echo, ctypes.c_uint8), _ptr(top_n, ctypes.c_int32),
+                                  1 if has_logits else 0, int(logits_rows),
+                                  ctypes.byref(self._h), _ptr(out_off, ctypes.c_uint32),
+                                  ctypes.byref(rows), ctypes.byref(ws)), "lp_plan_ragged")
+        self.batch = batch
+        self.vocab = int(vocab)
+        self.has_logits = bool(has_logits)
+        self.out_off = out_off
+        self.out_rows = int(rows.value)
+        self.input_row_offsets = off
+
+    # ---------------------------------------------------------------- facts
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check(self._lib.lp_plan_get_info(self._h, ctypes.byref(inf)), "lp_plan_get_info")
+        return {f: getattr(inf, f) for f, _ in PlanInfo._fields_}
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.info()["workspace_bytes"])
+
+    @property
+    def split(self) -> int:
+        return int(self.info()["split"])
+
+    def set_split(self, split: int):
+        _check(self._lib.lp_plan_set_split(self._h, int(split)), "lp_plan_set_split")
+
+    def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
+        """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
+        tok = _u32(tokens) if tokens is not None else None
+        smp = _u32(sampled_tokens, self.batch)
+        out = np.zeros((self.out_rows, 4), dtype=np.uint32)
+        _check(self._lib.lp_plan_descriptors(self._h, _ptr(tok, ctypes.c_uint32),
+                                             _ptr(smp, ctypes.c_uint32),
+                                             _ptr(out, ctypes.c_uint32)), "lp_plan_descriptors")
+        return out
+
+    # ---------------------------------------------------------------- device work
+    def stage(self, tokens, sampled_tokens, workspace, stream=None):
+        tok = _u32(tokens) if tokens is not None else None
+        smp = _u32(sampled_tokens, self.batch)
+        _check(self._lib.lp_stage_ragged(self._h, _ptr(tok, ctypes.c_uint32),
+                                         _ptr(smp, ctypes.c_uint32), _dev_ptr(workspace),
+                                         _nbytes(workspace), _stream_ptr(stream)),
+               "lp_stage_ragged")
+
+    def launch(self, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
+               stream=None):
+        _check(self._lib.lp_launch_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
+                                          _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
+                                          _dev_ptr(workspace), _nbytes(workspace),
+                                          _stream_ptr(stream)), "lp_launch_ragged")
+
+    def compute(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
+                out_token_ids, workspace, stream=None):
+        tok = _u32(tokens) if tokens is not None else None
+        smp = _u32(sampled_tokens, self.batch)
+        _check(self._lib.lp_compute_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
+                                           _ptr(tok, ctypes.c_uint32), _ptr(smp, ctypes.c_uint32),
+                                           _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
+                                           _dev_ptr(workspace), _nbytes(workspace),
+                                           _stream_ptr(stream)), "lp_compute_ragged")
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            self._lib.lp_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else int(t.numel() * t.element_size())
+
+
+def status_string(code: int) -> str:
+    return load().lp_status_string(int(code)).decode()
+
+
+# -------------------------------------------------------------------- torch front end
+
+def _check_logits(t, rows, vocab, name, torch):
+    if t.dim() != 2:
+        raise LogprobError(3, f"{name} must be 2-D")
+    if t.dtype != torch.float32:
+        raise LogprobError(3, f"{name} must be float32")
+    if t.device.type != "cuda":
+        raise LogprobError(3, f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise LogprobError(3, f"{name} must be contiguous")
+    if rows is not None and t.shape[0] != rows:
+        raise LogprobError(3, f"{name} has {t.shape[0]} rows, expected {rows}")
+    if vocab is not None and t.shape[1] != vocab:
+        raise LogprobError(3, f"{name} vocab {t.shape[1]} != {vocab}")
+
+
+def alloc_outputs(plan: Plan, device, torch):
+    lp = torch.empty((plan.out_rows, COLUMNS), dtype=torch.float32, device=device)
+    ids = torch.empty((plan.out_rows, COLUMNS), dtype=torch.uint32, device=device)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
+    return lp, ids, ws
+
+
+def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens,
+                                     sampled_tokens, batch_top_n, batch_echo, *,
+                                     split: int | None = None, stream=None):
+    """Ragged batched token log-probabilities on the GPU.
+
+    Arguments follow the MAX page's ``compute_log_probabilities_ragged``
+    (section "compute_log_probabilities_ragged：执行计算并组装结果"):
+    ``logits`` (tokens, vocab) float32 on the GPU, or None when no request
+    echoes; ``next_token_logits`` (batch, vocab) float32 on the GPU;
+    ``input_row_offsets``, ``tokens``, ``sampled_tokens``, ``batch_top_n`` and
+    ``batch_echo`` are host sequences.
+
+    Returns ``(logprobs (R, 8) float32, token_ids (R, 8) uint32,
+    output_row_offsets (batch+1,) uint32 numpy)``, the tensors on the GPU.
+    """
+    import torch
+
+    off = np.asarray(input_row_offsets)
+    if off.ndim != 1:
+        raise LogprobError(3, "input_row_offsets must be 1-D")
+    batch = off.shape[0] - 1
+    _check_logits(next_token_logits, batch, None, "next_token_logits", torch)
+    vocab = int(next_token_logits.shape[1])
+    if logits is not None:
+        _check_logits(logits, None, vocab, "logits", torch)
+        if logits.device != next_token_logits.device:
+            raise LogprobError(3, "logits and next_token_logits on different devices")
+    plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
+                None if logits is None else int(logits.shape[0]))
+    try:
+        if split is not None:
+            plan.set_split(split)
+        device = next_token_logits.device
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
+        lp, ids, ws = alloc_outputs(plan, device, torch)
+        plan.compute(logits, next_token_logits, tokens, sampled_tokens, lp, ids, ws, stream)
+        out_off = plan.out_off.copy()
+    finally:
+        plan.close()   # waits only for the descriptor upload, not the kernels
+    return lp, ids, out_off

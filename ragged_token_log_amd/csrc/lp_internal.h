@@ -1,0 +1,72 @@
+// Internal definitions shared by the host plan (plan.cpp) and the device code
+// (logprob_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/liblogprob.h"
+
+namespace lp {
+
+constexpr uint32_t kLevels = 3;
+constexpr uint32_t kCols = 1u << kLevels;     // 8 output columns
+constexpr uint32_t kTopSlots = kCols - 1;     // 7 ranked slots + 1 chosen slot
+constexpr uint32_t kPadId = 0xFFFFFFFFu;
+constexpr uint32_t kMaxSplit = 64;
+
+// One output row as the device sees it (16 bytes, one dwordx4 load).
+struct RowDesc {
+    uint32_t src_row;   // logits row to read (row of `logits` or of next_token_logits)
+    uint32_t chosen;    // token whose log-probability goes in the last column
+    uint32_t top_n;     // 0 => padding only, logits not read
+    uint32_t reserved;
+};
+static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
+
+// Partial result of one (row, vocabulary segment) in the split variant:
+// the segment's running max and scaled sum, and its 7 best order keys.
+struct PartialRec {
+    float m;
+    float s;
+    uint64_t keys[kTopSlots];
+};
+static_assert(sizeof(PartialRec) == 64, "PartialRec is 64 bytes");
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace lp
+
+struct lp_plan {
+    uint32_t batch = 0;
+    uint32_t vocab = 0;
+    uint32_t levels = 0;
+    uint32_t has_logits = 0;
+    uint64_t logits_rows = 0;
+    std::vector<uint32_t> in_off;    // B+1
+    std::vector<uint32_t> out_off;   // B+1
+    std::vector<uint8_t> echo;       // B
+    std::vector<int32_t> top_n;      // B
+    uint64_t out_rows = 0;
+    uint64_t read_rows = 0;
+    uint32_t split = 1;
+    uint64_t desc_bytes = 0;         // R * 16, rounded to 256
+    uint64_t partial_bytes = 0;      // R * split * 64 when split > 1
+    uint64_t workspace_bytes = 0;
+    // pinned staging for the descriptor upload (allocated on first stage)
+    void *staging = nullptr;
+    uint64_t staging_bytes = 0;
+    void *staging_event = nullptr;   // hipEvent_t recorded after the last upload
+    bool staging_pending = false;
+};
+
+namespace lp {
+// Fills `out` (R descriptors) from host token arrays; no HIP calls.
+lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
+                            const uint32_t *sampled, RowDesc *out);
+// Recomputes workspace sizes after a split change.
+void size_workspace(lp_plan &p);
+// Releases pinned staging (defined with the device code).
+void release_staging(lp_plan &p);
+}  // namespace lp

@@ -1,0 +1,209 @@
+// Host-side planning for ragged batched token log-probabilities.
+//
+// Follows [MAX] "MAX Python SDK 中 log_probabilities 模块解析：ragged 批量 Token
+// 对数概率的计算图构建与执行":
+//   §compute_log_probabilities_ragged -- argument checks at the call boundary;
+//   §ragged 数据编排 -- which logits and row offsets the device op reads, and
+//     the echo-dependent output counts with their uint32 running-sum offsets;
+//   §图支持的最大 top-n / §compute_top 的结果组装 -- the top_n range;
+//   §echo 的前置条件 -- echo needs the full logits.
+// The chosen token of each row follows [SGL] "logprob、finish reason 与 output
+// processing", §input logprob 和 output logprob 来自哪里: a prompt position's
+// logits predict the next prompt token, and the last position predicts the
+// sampled token.
+//
+// Nothing here calls HIP, so planning and descriptor building run (and are
+// tested) on a machine without a GPU.
+#include <cstring>
+#include <new>
+
+#include "lp_internal.h"
+
+namespace lp {
+
+void size_workspace(lp_plan &p) {
+    p.desc_bytes = align_up(p.out_rows * sizeof(RowDesc), 256);
+    p.partial_bytes = p.split > 1 ? p.out_rows * p.split * sizeof(PartialRec) : 0;
+    p.workspace_bytes = p.desc_bytes + p.partial_bytes;
+}
+
+// Vocabulary segments per row.  Rows are independent, so a launch with many
+// rows runs one workgroup per row; a launch with too few rows to occupy the
+// chip splits each row into segments (each at least kMinSegment elements) and
+// merges their partial results in a second kernel.
+static uint32_t choose_split(uint64_t read_rows, uint32_t vocab) {
+    constexpr uint64_t kTargetWorkgroups = 512;  // 2 per CU on 256 CUs
+    constexpr uint32_t kMinSegment = 8192;
+    if (read_rows == 0 || read_rows >= kTargetWorkgroups) return 1;
+    uint64_t s = (kTargetWorkgroups + read_rows - 1) / read_rows;
+    uint64_t by_vocab = vocab / kMinSegment;
+    if (by_vocab < 1) by_vocab = 1;
+    if (s > by_vocab) s = by_vocab;
+    if (s > kMaxSplit) s = kMaxSplit;
+    return static_cast<uint32_t>(s);
+}
+
+lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
+                            const uint32_t *sampled, RowDesc *out) {
+    if (p.batch > 0 && sampled == nullptr) return LP_ERR_NULL_ARG;
+    bool any_echo = false;
+    for (uint32_t n = 0; n < p.batch; ++n) any_echo |= p.echo[n] != 0;
+    if (any_echo && tokens == nullptr) return LP_ERR_NULL_ARG;
+    const uint64_t total = p.in_off[p.batch];
+    if (tokens != nullptr)
+        for (uint64_t i = 0; i < total; ++i)
+            if (tokens[i] >= p.vocab) return LP_ERR_TOKEN_RANGE;
+    for (uint32_t n = 0; n < p.batch; ++n)
+        if (sampled[n] >= p.vocab) return LP_ERR_TOKEN_RANGE;
+
+    for (uint32_t n = 0; n < p.batch; ++n) {
+        const uint64_t len = p.in_off[n + 1] - p.in_off[n];
+        const uint64_t count = p.out_off[n + 1] - p.out_off[n];
+        // the rows the op reads: the last `count` rows of the request's range
+        const uint64_t src_end = p.has_logits ? p.in_off[n + 1] : uint64_t(n) + 1;
+        for (uint64_t k = 0; k < count; ++k) {
+            const uint64_t o = p.out_off[n] + k;
+            const uint64_t pos = len - count + k;   // prompt position of this row
+            RowDesc d;
+            d.src_row = static_cast<uint32_t>(src_end - count + k);
+            d.chosen = (pos + 1 < len) ? tokens[p.in_off[n] + pos + 1] : sampled[n];
+            d.top_n = static_cast<uint32_t>(p.top_n[n]);
+            d.reserved = 0;
+            out[o] = d;
+        }
+    }
+    return LP_OK;
+}
+
+}  // namespace lp
+
+extern "C" {
+
+lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
+                         const uint32_t *input_row_offsets, const uint8_t *batch_echo,
+                         const int32_t *batch_top_n, int has_logits, uint64_t logits_rows,
+                         lp_plan **plan_out, uint32_t *output_row_offsets,
+                         uint64_t *out_rows, uint64_t *workspace_bytes) {
+    if (plan_out == nullptr) return LP_ERR_NULL_ARG;
+    *plan_out = nullptr;
+    if (input_row_offsets == nullptr) return LP_ERR_NULL_ARG;
+    if (batch > 0 && (batch_echo == nullptr || batch_top_n == nullptr)) return LP_ERR_NULL_ARG;
+    if (levels != lp::kLevels) return LP_ERR_UNSUPPORTED;
+    if (vocab < 1) return LP_ERR_SHAPE;
+
+    // offsets: start at 0, every request non-empty
+    if (input_row_offsets[0] != 0) return LP_ERR_OFFSETS;
+    for (uint32_t n = 0; n < batch; ++n)
+        if (input_row_offsets[n + 1] <= input_row_offsets[n]) return LP_ERR_OFFSETS;
+    const uint64_t total = input_row_offsets[batch];
+    if (has_logits) {
+        if (logits_rows != total) return LP_ERR_SHAPE;
+    } else if (logits_rows != batch) {
+        return LP_ERR_SHAPE;
+    }
+    for (uint32_t n = 0; n < batch; ++n) {
+        if (batch_top_n[n] < 0) return LP_ERR_TOP_N_NEGATIVE;
+        if (batch_top_n[n] > int32_t(lp::kTopSlots)) return LP_ERR_TOP_N_TOO_LARGE;
+    }
+    for (uint32_t n = 0; n < batch; ++n)
+        if (batch_echo[n] && !has_logits) return LP_ERR_ECHO_NEEDS_LOGITS;
+
+    lp_plan *p = new (std::nothrow) lp_plan();
+    if (p == nullptr) return LP_ERR_NOMEM;
+    try {
+        p->batch = batch;
+        p->vocab = vocab;
+        p->levels = levels;
+        p->has_logits = has_logits ? 1 : 0;
+        p->logits_rows = logits_rows;
+        p->in_off.assign(input_row_offsets, input_row_offsets + batch + 1);
+        p->echo.resize(batch);
+        p->top_n.resize(batch);
+        p->out_off.resize(size_t(batch) + 1);
+        uint64_t acc = 0, read = 0;
+        p->out_off[0] = 0;
+        for (uint32_t n = 0; n < batch; ++n) {
+            p->echo[n] = batch_echo[n] ? 1 : 0;
+            p->top_n[n] = batch_top_n[n];
+            const uint64_t count = p->echo[n] ? uint64_t(input_row_offsets[n + 1]) -
+                                                    input_row_offsets[n]
+                                              : 1;
+            acc += count;
+            if (batch_top_n[n] > 0) read += count;
+            if (acc > 0xFFFFFFFFull) {
+                delete p;
+                return LP_ERR_SHAPE;   // output offsets are uint32
+            }
+            p->out_off[n + 1] = static_cast<uint32_t>(acc);
+        }
+        p->out_rows = acc;
+        p->read_rows = read;
+    } catch (...) {
+        delete p;
+        return LP_ERR_NOMEM;
+    }
+    p->split = lp::choose_split(p->read_rows, vocab);
+    lp::size_workspace(*p);
+
+    if (output_row_offsets != nullptr)
+        std::memcpy(output_row_offsets, p->out_off.data(), (size_t(batch) + 1) * 4);
+    if (out_rows != nullptr) *out_rows = p->out_rows;
+    if (workspace_bytes != nullptr) *workspace_bytes = p->workspace_bytes;
+    *plan_out = p;
+    return LP_OK;
+}
+
+lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
+    if (plan == nullptr || info == nullptr) return LP_ERR_NULL_ARG;
+    info->batch = plan->batch;
+    info->vocab = plan->vocab;
+    info->levels = plan->levels;
+    info->columns = lp::kCols;
+    info->out_rows = plan->out_rows;
+    info->read_rows = plan->read_rows;
+    info->split = plan->split;
+    info->has_logits = plan->has_logits;
+    info->workspace_bytes = plan->workspace_bytes;
+    return LP_OK;
+}
+
+lp_status lp_plan_set_split(lp_plan *plan, uint32_t split) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (split < 1 || split > lp::kMaxSplit) return LP_ERR_UNSUPPORTED;
+    plan->split = split;
+    lp::size_workspace(*plan);
+    return LP_OK;
+}
+
+lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
+                              const uint32_t *sampled_tokens, uint32_t *desc_out) {
+    if (plan == nullptr || (desc_out == nullptr && plan->out_rows > 0)) return LP_ERR_NULL_ARG;
+    return lp::build_descriptors(*plan, tokens, sampled_tokens,
+                                 reinterpret_cast<lp::RowDesc *>(desc_out));
+}
+
+void lp_plan_destroy(lp_plan *plan) {
+    if (plan == nullptr) return;
+    lp::release_staging(*plan);
+    delete plan;
+}
+
+const char *lp_status_string(lp_status status) {
+    switch (status) {
+        case LP_OK: return "LP_OK";
+        case LP_ERR_NULL_ARG: return "LP_ERR_NULL_ARG";
+        case LP_ERR_OFFSETS: return "LP_ERR_OFFSETS";
+        case LP_ERR_SHAPE: return "LP_ERR_SHAPE";
+        case LP_ERR_TOP_N_NEGATIVE: return "LP_ERR_TOP_N_NEGATIVE";
+        case LP_ERR_TOP_N_TOO_LARGE: return "LP_ERR_TOP_N_TOO_LARGE";
+        case LP_ERR_ECHO_NEEDS_LOGITS: return "LP_ERR_ECHO_NEEDS_LOGITS";
+        case LP_ERR_TOKEN_RANGE: return "LP_ERR_TOKEN_RANGE";
+        case LP_ERR_UNSUPPORTED: return "LP_ERR_UNSUPPORTED";
+        case LP_ERR_WORKSPACE: return "LP_ERR_WORKSPACE";
+        case LP_ERR_HIP: return "LP_ERR_HIP";
+        case LP_ERR_NOMEM: return "LP_ERR_NOMEM";
+    }
+    return "LP_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host planning agrees with the oracle.  No GPU call is made here."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import gen
+import oracle.logprob_oracle as LO
+import ragged_token_log_amd as R
+from ragged_token_log_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "liblogprob.h")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    R.load()
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    assert sorted(binding.EXPORTED) == declared
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lp_[a-z_0-9]+)\b", out))
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code, name in binding.STATUS_NAMES.items():
+        assert R.status_string(code) == name
+
+
+def _random_batch(rng, batch, vocab, has_logits, p_echo=0.5):
+    lengths = rng.integers(1, 9, size=batch)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    echo = (rng.random(batch) < p_echo) if has_logits else np.zeros(batch, bool)
+    top_n = rng.integers(0, 8, size=batch)
+    tokens = rng.integers(0, vocab, size=int(off[-1])).astype(np.uint32)
+    sampled = rng.integers(0, vocab, size=batch).astype(np.uint32)
+    return off, echo, top_n, tokens, sampled
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    has_logits = bool(seed % 3)
+    batch = int(rng.integers(1, 12))
+    off, echo, top_n, tokens, sampled = _random_batch(rng, batch, 50, has_logits)
+    plan = R.Plan(off, echo, top_n, 50, has_logits)
+    counts, out_off = LO.output_counts_and_offsets(off, echo)
+    assert plan.out_off.dtype == np.uint32 and np.array_equal(plan.out_off, out_off)
+    assert plan.out_rows == int(out_off[-1])
+    desc = plan.descriptors(tokens, sampled)
+    tasks = LO.row_tasks(off, echo, top_n, tokens, sampled, has_logits)
+    want = np.array([[t.src_row, t.chosen, t.top_n, 0] for t in tasks], dtype=np.uint32)
+    assert np.array_equal(desc, want)
+    info = plan.info()
+    assert info["read_rows"] == sum(int(c) for c, t in zip(counts, top_n) if t > 0)
+    assert info["columns"] == 8 and info["levels"] == 3
+
+
+def test_plan_on_named_workloads():
+    for name, make in gen.WORKLOADS.items():
+        c = make()
+        plan = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, c.has_logits)
+        _, out_off = LO.output_counts_and_offsets(c.offsets, c.echo)
+        assert np.array_equal(plan.out_off, out_off), name
+        desc = plan.descriptors(c.tokens, c.sampled)
+        tasks = LO.row_tasks(c.offsets, c.echo, c.top_n, c.tokens, c.sampled, c.has_logits)
+        assert np.array_equal(desc[:, 0], [t.src_row for t in tasks]), name
+        assert np.array_equal(desc[:, 1], [t.chosen for t in tasks]), name
+        assert plan.info()["split"] >= 1
+
+
+def test_split_and_workspace():
+    plan = R.Plan([0, 1, 2], [0, 0], [7, 7], 128256, False)
+    s = plan.split
+    assert s > 1                      # two rows cannot fill the chip
+    ws = plan.workspace_bytes
+    assert ws == 256 + 2 * s * 64
+    plan.set_split(1)
+    assert plan.split == 1 and plan.workspace_bytes == 256
+    with pytest.raises(R.LogprobError) as e:
+        plan.set_split(65)
+    assert e.value.name == "LP_ERR_UNSUPPORTED"
+    big = R.Plan(np.arange(2001, dtype=np.uint32), np.ones(2000, bool), np.full(2000, 5), 32000,
+                 True)
+    assert big.split == 1
+
+
+def _expect(name, fn):
+    with pytest.raises(R.LogprobError) as e:
+        fn()
+    assert e.value.name == name, e.value.name
+
+
+def test_error_codes_match_oracle_readings():
+    off = [0, 2, 3]
+    _expect("LP_ERR_TOP_N_NEGATIVE", lambda: R.Plan(off, [1, 0], [-1, 1], 5, True))
+    _expect("LP_ERR_TOP_N_TOO_LARGE", lambda: R.Plan(off, [1, 0], [8, 1], 5, True))
+    _expect("LP_ERR_ECHO_NEEDS_LOGITS", lambda: R.Plan(off, [1, 0], [1, 1], 5, False))
+    _expect("LP_ERR_OFFSETS", lambda: R.Plan([0, 3, 3], [1, 0], [1, 1], 5, True))
+    _expect("LP_ERR_OFFSETS", lambda: R.Plan([1, 2, 3], [1, 0], [1, 1], 5, True))
+    _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [1, 0], [1, 1], 5, True, logits_rows=4))
+    _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [0, 0], [1, 1], 5, False, logits_rows=3))
+    _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [1, 0], [1, 1], 0, True))
+    _expect("LP_ERR_UNSUPPORTED", lambda: R.Plan(off, [1, 0], [1, 1], 5, True, levels=4))
+    plan = R.Plan(off, [1, 0], [1, 7], 5, True)
+    _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([1, 2, 5], [4, 0]))
+    _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([1, 2, 3], [4, 5]))
+    _expect("LP_ERR_NULL_ARG", lambda: plan.descriptors(None, [4, 0]))   # echo needs tokens
+    # the oracle rejects the same calls with the same names
+    ok = dict(input_row_offsets=np.array(off, np.uint32), logits=np.zeros((3, 5), np.float32),
+              next_token_logits=np.zeros((2, 5), np.float32), tokens=np.array([1, 2, 3], np.uint32),
+              sampled_tokens=np.array([4, 0], np.uint32), batch_top_n=[1, 7], batch_echo=[True, False])
+    for code, kw in (("LP_ERR_TOP_N_NEGATIVE", {"batch_top_n": [-1, 1]}),
+                     ("LP_ERR_TOP_N_TOO_LARGE", {"batch_top_n": [8, 1]}),
+                     ("LP_ERR_ECHO_NEEDS_LOGITS", {"logits": None}),
+                     ("LP_ERR_OFFSETS", {"input_row_offsets": np.array([0, 3, 3], np.uint32)}),
+                     ("LP_ERR_TOKEN_RANGE", {"tokens": np.array([1, 2, 5], np.uint32)})):
+        args = dict(ok, **kw)
+        with pytest.raises(LO.OracleError) as e:
+            LO.compute_log_probabilities_ragged(**args)
+        assert e.value.code == code
+
+
+def test_empty_batch():
+    plan = R.Plan([0], [], [], 10, True)
+    assert plan.out_rows == 0 and plan.out_off.tolist() == [0]
+    assert plan.descriptors([], []).shape == (0, 4)
+
+
+def test_no_echo_request_with_full_logits_needs_no_tokens():
+    plan = R.Plan([0, 4, 6], [0, 0], [3, 3], 9, True)
+    d = plan.descriptors(None, [1, 2])
+    assert d[:, :2].tolist() == [[3, 1], [5, 2]]

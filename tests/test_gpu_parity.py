@@ -1,0 +1,220 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Ids and output offsets must match bit for bit; logprobs within 1e-5 absolute
+(NaN and infinities exactly).  Small cases compare every element; the full
+prefill and tie-stress workloads compare sampled rows with the oracle and
+check every row through properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle.logprob_oracle as LO
+from tests.gpu_helpers import (DeviceRows, assert_parity, check_all_rows_properties, log, oracle,
+                               run_library)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def R():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_token_log_amd as lib
+    lib.load()
+    return lib
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _special_rows(rng, n, vocab):
+    """Rows covering the degenerate cases: all-equal, +-0.0, -inf heavy, all
+    -inf, one finite entry, a boosted token, heavy ties."""
+    rows = []
+    kinds = ["normal", "equal", "zeros", "ninf_heavy", "all_ninf", "one_finite", "boost",
+             "ties", "ninf_prefix"]
+    for i in range(n):
+        k = kinds[i % len(kinds)]
+        if k == "normal":
+            x = rng.standard_normal(vocab).astype(np.float32) * 2
+        elif k == "equal":
+            x = np.full(vocab, -0.5, np.float32)
+        elif k == "zeros":
+            x = np.where(rng.random(vocab) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+            x[rng.random(vocab) < 0.2] = -1.0
+        elif k == "ninf_heavy":
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[rng.random(vocab) < 0.9] = -np.inf
+        elif k == "all_ninf":
+            x = np.full(vocab, -np.inf, np.float32)
+        elif k == "one_finite":
+            x = np.full(vocab, -np.inf, np.float32)
+            x[rng.integers(vocab)] = 3.0
+        elif k == "boost":
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[rng.integers(vocab)] += 30.0
+        elif k == "ties":
+            x = (rng.integers(-3, 4, vocab) * 0.5).astype(np.float32)
+        else:  # a long -inf run at the start, then values
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[: vocab * 3 // 4] = -np.inf
+        rows.append(x)
+    return np.stack(rows)
+
+
+def _edge_batch(seed, vocab):
+    rng = np.random.default_rng(seed)
+    lengths = np.array([1, 3, 1, 5, 2, 7, 1, 4])
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    echo = np.array([1, 1, 0, 1, 0, 1, 1, 0], bool)
+    top_n = np.array([7, 0, 5, 1, 7, 3, 2, 6])
+    logits = _special_rows(rng, int(off[-1]), vocab)
+    ntl = logits[off[1:].astype(np.int64) - 1]
+    tokens = rng.integers(0, vocab, int(off[-1])).astype(np.uint32)
+    sampled = rng.integers(0, vocab, len(lengths)).astype(np.uint32)
+    return off, logits, ntl, tokens, sampled, top_n, echo
+
+
+@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 111, 1000, 1027, 4099, 8193, 20011])
+@pytest.mark.parametrize("split", [None, 1, 2, 5])
+def test_edge_cases(R, vocab, split):
+    log(f"edge cases vocab={vocab} split={split}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _edge_batch(vocab * 7 + 1, vocab)
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo)
+    got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split)
+    assert_parity(*got, ref, f"edge vocab={vocab} split={split}")
+
+
+@pytest.mark.parametrize("split", [None, 1, 3])
+def test_no_echo_next_token_path(R, split):
+    c = gen.no_echo_next_token()
+    ntl = gen.host_logits(c)
+    log(f"no_echo_next_token split={split}")
+    ref = oracle(c.offsets, None, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    got = run_library(R, torch, c.offsets, None, _dev(ntl), c.tokens, c.sampled, c.top_n, c.echo,
+                      split)
+    assert_parity(*got, ref, "no_echo_next_token")
+
+
+@pytest.mark.parametrize("split", [None, 2])
+def test_ragged_echo_mix(R, split):
+    c = gen.ragged_echo_mix()
+    logits = gen.host_logits(c)
+    ntl = gen.next_token_rows(c, logits)
+    log(f"ragged_echo_mix rows={c.total_tokens} split={split}")
+    ref = oracle(c.offsets, logits, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    got = run_library(R, torch, c.offsets, _dev(logits), _dev(ntl), c.tokens, c.sampled, c.top_n,
+                      c.echo, split)
+    assert_parity(*got, ref, "ragged_echo_mix")
+
+
+@pytest.mark.parametrize("split", [None, 1, 16])
+def test_decode_peaked(R, split):
+    c = gen.decode_peaked()
+    ntl = gen.host_logits(c)
+    log(f"decode_peaked split={split}")
+    ref = oracle(c.offsets, None, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    got = run_library(R, torch, c.offsets, None, _dev(ntl), c.tokens, c.sampled, c.top_n, c.echo,
+                      split)
+    assert_parity(*got, ref, "decode_peaked")
+    # the boosted token is the sampled token and ranks first
+    assert np.array_equal(got[1][:, 0], c.sampled) and np.array_equal(got[1][:, 7], c.sampled)
+
+
+def _full_size(R, c, n_sample, seed):
+    dev = torch.device("cuda")
+    logits = gen.device_logits(c, dev, torch)
+    ntl = logits.index_select(0, torch.from_numpy(c.offsets[1:].astype(np.int64) - 1).to(dev))
+    torch.cuda.synchronize()
+    log(f"{c.name}: rows={c.total_tokens} vocab={c.vocab} generated")
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        c.offsets, logits, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    torch.cuda.synchronize()
+    log(f"{c.name}: library done")
+    nrows = lp.shape[0]
+    rng = np.random.default_rng(seed)
+    rows = sorted(set(rng.choice(nrows, size=min(n_sample, nrows), replace=False).tolist())
+                  | {0, nrows - 1})
+    if c.dist.get("kind") == "quant":      # every all-equal row too
+        tasks = LO.row_tasks(c.offsets, c.echo, c.top_n, c.tokens, c.sampled, True)
+        eq = c.dist["equal_rows"]
+        rows = sorted(set(rows) | {o for o, t in enumerate(tasks) if eq[t.src_row]})
+    ref = oracle(c.offsets, DeviceRows(logits), DeviceRows(ntl), c.tokens, c.sampled, c.top_n,
+                 c.echo, rows=rows)
+    log(f"{c.name}: oracle done on {len(rows)} rows")
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), out_off, ref, c.name, rows=rows)
+    desc = LO.row_tasks(c.offsets, c.echo, c.top_n, c.tokens, c.sampled, True)
+    check_all_rows_properties(torch, logits, desc, lp, ids, c.vocab)
+    log(f"{c.name}: all-row properties hold")
+    del logits, ntl, lp, ids
+    torch.cuda.empty_cache()
+
+
+def test_prefill_echo_large_full_size(R):
+    _full_size(R, gen.prefill_echo_large(), 40, 41)
+
+
+def test_tie_edge_stress_full_size(R):
+    _full_size(R, gen.tie_edge_stress(), 60, 51)
+
+
+def test_deterministic_and_split_independent(R):
+    c = gen.ragged_echo_mix(seed=9, batch=6, lmin=30, lmax=90)
+    logits = _dev(gen.host_logits(c))
+    ntl = logits.index_select(0, torch.from_numpy(c.offsets[1:].astype(np.int64) - 1).cuda())
+    args = (c.offsets, logits, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    a = run_library(R, torch, *args)
+    b = run_library(R, torch, *args)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    for s in (2, 4, 64):
+        d = run_library(R, torch, *args, split=s)
+        assert np.array_equal(a[1], d[1]), s
+        np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
+
+
+def test_outputs_stay_in_bounds_and_plan_is_reusable(R):
+    c = gen.ragged_echo_mix(seed=10, batch=5, lmin=5, lmax=40, vocab=3001)
+    logits_np = gen.host_logits(c)
+    logits = _dev(logits_np)
+    ntl = _dev(gen.next_token_rows(c, logits_np))
+    plan = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, True)
+    n = plan.out_rows
+    canary_lp = torch.full((n + 4, 8), 123.0, device="cuda")
+    canary_id = torch.full((n + 4, 8), 77, dtype=torch.uint32, device="cuda")
+    ws = torch.empty(plan.workspace_bytes + 4096, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for trial in range(3):
+        rng = np.random.default_rng(trial)
+        tokens = rng.integers(0, c.vocab, c.total_tokens).astype(np.uint32)
+        sampled = rng.integers(0, c.vocab, c.batch).astype(np.uint32)
+        plan.compute(logits, ntl, tokens, sampled, canary_lp, canary_id, ws, stream)
+        torch.cuda.synchronize()
+        ref = oracle(c.offsets, logits_np, gen.next_token_rows(c, logits_np), tokens, sampled,
+                     c.top_n, c.echo)
+        lp = canary_lp.cpu().numpy()
+        ids = canary_id.cpu().numpy()
+        assert np.all(lp[n:] == 123.0) and np.all(ids[n:] == 77)
+        assert_parity(lp[:n], ids[:n], plan.out_off, ref, f"reuse trial {trial}")
+    plan.close()
+
+
+def test_errors_reported_before_launch(R):
+    c = gen.no_echo_next_token()
+    ntl = _dev(gen.host_logits(c))
+    with pytest.raises(R.LogprobError) as e:
+        R.compute_log_probabilities_ragged(c.offsets, None, ntl, c.tokens,
+                                           np.array([0, 1, 2, 32000], np.uint32), c.top_n, c.echo)
+    assert e.value.name == "LP_ERR_TOKEN_RANGE"
+    plan = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, False)
+    lp, ids, ws = R.alloc_outputs(plan, ntl.device, torch)
+    small = ws[:0]
+    with pytest.raises(R.LogprobError) as e:
+        plan.compute(None, ntl, c.tokens, c.sampled, lp, ids, small, torch.cuda.current_stream())
+    assert e.value.name == "LP_ERR_WORKSPACE"
+    with pytest.raises(R.LogprobError):
+        R.compute_log_probabilities_ragged(c.offsets, None, ntl.double(), c.tokens, c.sampled,
+                                           c.top_n, c.echo)

@@ -77,6 +77,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ragged_echo_mix")
     ap.add_argument("--split", type=int, default=None, help="force the plan's split")
+    ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
     args = ap.parse_args()
@@ -108,6 +109,8 @@ def main():
     plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits)
     if args.split:
         plan.set_split(args.split)
+    if args.waves:
+        plan.set_waves(args.waves)
     info = plan.info()
     lp, ids, ws = R.alloc_outputs(plan, dev, torch)
     plan.stage(case.tokens, case.sampled, ws, stream)   # descriptors resident in HBM
@@ -160,11 +163,12 @@ def main():
         "data": "synthetic (seeded draws with the workload's shapes and distributions)",
         "config": {"workload": case.name, "batch": case.batch, "vocab": case.vocab,
                    "out_rows": int(info["out_rows"]), "read_rows": read_rows,
-                   "split": int(info["split"]), "logits_copies_cycled": n_copies},
+                   "split": int(info["split"]), "waves": int(info["waves"]),
+                   "logits_copies_cycled": n_copies},
         "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "row_kernel" if info["split"] == 1 else "row_kernel+merge_kernel",
+                     "kernel": "row_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "avg_launch_us": avg_launch_ms * 1e3,
                      "p10_launch_us": float(np.percentile(launch_ms, 10)) * 1e3,
@@ -180,6 +184,8 @@ def main():
             p2 = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits)
             if args.split:
                 p2.set_split(args.split)
+            if args.waves:
+                p2.set_waves(args.waves)
             src = copies[i % n_copies]
             p2.compute(src if case.has_logits else None, None if case.has_logits else src,
                        case.tokens, case.sampled, lp, ids, ws, stream)

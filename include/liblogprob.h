@@ -69,9 +69,11 @@ typedef struct lp_plan_info {
     uint32_t columns;         /* 2^levels = 8 */
     uint64_t out_rows;        /* R = output_row_offsets[B] */
     uint64_t read_rows;       /* output rows whose request has top_n > 0 (logits rows read) */
-    uint32_t split;           /* vocabulary segments per row: 1 = single-pass row kernel,
-                                 > 1 = split-vocab partial kernel + merge kernel */
+    uint32_t split;           /* vocabulary segments per row: 1 = one workgroup per row;
+                                 > 1 = one workgroup per segment plus a merge kernel */
     uint32_t has_logits;      /* 1 if full logits are given */
+    uint32_t waves;           /* waves per workgroup (4, 8 or 16) */
+    uint32_t reserved;
     uint64_t workspace_bytes; /* device scratch lp_compute_ragged needs */
 } lp_plan_info;
 
@@ -114,6 +116,10 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info);
  */
 lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
 
+/* Overrides the waves per workgroup (4, 8 or 16); LP_ERR_UNSUPPORTED otherwise.
+ * Results do not depend on it beyond fp32 rounding of the log-probabilities. */
+lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
+
 /*
  * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of
  * 4 uint32 to desc_out: {logits row read, chosen token, top_n, 0}, in output
@@ -146,7 +152,9 @@ lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens,
  *   out_token_ids      device out, (R, 8) uint32
  *   workspace          device, >= workspace_bytes of the plan, 256-byte aligned
  *
- * Enqueue only: no host synchronisation.  Device buffers must stay alive
+ * One kernel launch (two when split > 1).  Enqueue only: no host
+ * synchronisation.  Launches that share a workspace must be ordered (same
+ * stream): split launches keep partial results there.  Device buffers must stay alive
  * until the stream reaches the end of the enqueued work.
  */
 lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 
 # every symbol include/liblogprob.h declares
 EXPORTED = (
-    "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_descriptors",
+    "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
+    "lp_plan_descriptors",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
@@ -51,6 +52,7 @@ class PlanInfo(ctypes.Structure):
         ("levels", ctypes.c_uint32), ("columns", ctypes.c_uint32),
         ("out_rows", ctypes.c_uint64), ("read_rows", ctypes.c_uint64),
         ("split", ctypes.c_uint32), ("has_logits", ctypes.c_uint32),
+        ("waves", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -74,6 +76,7 @@ def load():
                                    ctypes.c_int, u64, P(vp), P(u32), P(u64), P(u64)]
     lib.lp_plan_get_info.argtypes = [vp, P(PlanInfo)]
     lib.lp_plan_set_split.argtypes = [vp, u32]
+    lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
     lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
@@ -85,7 +88,7 @@ def load():
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
-                 "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
+                 "lp_plan_set_waves", "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -168,6 +171,9 @@ class Plan:
 
     def set_split(self, split: int):
         _check(self._lib.lp_plan_set_split(self._h, int(split)), "lp_plan_set_split")
+
+    def set_waves(self, waves: int):
+        _check(self._lib.lp_plan_set_waves(self._h, int(waves)), "lp_plan_set_waves")
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
         """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
@@ -257,7 +263,8 @@ def alloc_outputs(plan: Plan, device, torch):
 
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens,
                                      sampled_tokens, batch_top_n, batch_echo, *,
-                                     split: int | None = None, stream=None):
+                                     split: int | None = None, waves: int | None = None,
+                                     stream=None):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -287,6 +294,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     try:
         if split is not None:
             plan.set_split(split)
+        if waves is not None:
+            plan.set_waves(waves)
         device = next_token_logits.device
         if stream is None:
             stream = torch.cuda.current_stream(device)

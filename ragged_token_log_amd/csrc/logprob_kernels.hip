@@ -11,33 +11,33 @@
 // each logit exactly once with 16-byte loads and doing as little per element
 // as possible:
 //
-//  * Each row (or row segment) is one workgroup of kWaves waves.  Waves take
-//    interleaved chunks of 64 lanes x kU float4.  Per chunk a lane reduces its
-//    16 values to a chunk max, updates a running (m, s) with s = sum e^(x-m)
-//    (exp2 with log2(e) folded in after an exact subtraction), and compares
-//    one order key -- built from the chunk max and the lane's first token id --
-//    against the wave's threshold.
+//  * Each row (or row segment) is one workgroup of 4, 8 or 16 waves.  Waves
+//    take interleaved chunks of 64 lanes x kU float4.  Per chunk a lane
+//    reduces its 16 values to a chunk max, updates a running (m, s) with
+//    s = sum e^(x-m) (exp2 with log2(e) applied after an exact subtraction),
+//    and compares one order key -- built from the chunk max and the lane's
+//    first token id -- against the wave's threshold T.
 //  * Ranking uses a 64-bit order key: the fp32 bits mapped to an unsigned
 //    order (with -0.0 folded onto +0.0) in the high word, the complemented
 //    token id in the low word.  A larger key is a better (value, id) pair, so
-//    ties go to the lowest id and every merge in the kernel uses one total
-//    order.
-//  * A wave keeps candidates (keys above its threshold T) in an LDS buffer.
-//    When it fills, the wave selects its 7 best keys (7 rounds of a wave-wide
-//    max) and raises T to the 7th.  Any T that 7 real keys reach is a valid
-//    cut, so the first chunk seeds T from the 7th largest lane maximum and
-//    waves of one workgroup share their T through LDS.  After the first chunk
-//    only a handful of chunks per row take this slow path.
-//  * The waves' (m, s) pairs and candidate lists merge through LDS; the
+//    ties go to the lowest id and every merge uses one total order.
+//  * Each wave keeps its exact top-7 keys so far spread over lanes 0..6, and
+//    T = the 7th of them, raised further to any T another wave of the
+//    workgroup has published in LDS (a key that 7 real elements beat can
+//    never enter).  A chunk that beats T has its keys merged into the list:
+//    one by one (a lane-parallel shift) when they are few, else by one
+//    wave-wide selection over the chunk and the list.
+//  * The waves' (m, s) pairs and top-7 lists merge through LDS; the
 //    epilogue writes lp = x - (m + ln s) for the 7 slots and the chosen token.
 //  * With too few rows to fill 256 CUs, a row is split into segments, one
-//    workgroup each; segments write (m, s, 7 keys) records and a merge kernel
-//    (one wave per row) combines them in a fixed order and runs the epilogue.
+//    workgroup each, which write (m, s, 7 keys) records; a second kernel (one
+//    wave per row) merges a row's records in segment order and writes it.
 //
 // No MFMA: there is no contraction here.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 
 #include "lp_internal.h"
 
@@ -45,11 +45,8 @@ namespace lp {
 namespace dev {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;            // waves per workgroup
-constexpr int kThreads = kWave * kWaves;
 constexpr int kU = 4;                // float4 loads per lane per chunk
-constexpr int kChunkF4 = kWave * kU; // float4 per wave-chunk
-constexpr int kCap = 256;            // candidate keys per wave buffer
+constexpr int kChunkF4 = kWave * kU; // float4 per wave-chunk (1024 elements)
 constexpr int kSlots = int(kTopSlots);
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -73,23 +70,53 @@ __device__ __forceinline__ uint32_t key_id(uint64_t k) { return ~uint32_t(k); }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // ------------------------------------------------------------------ wave helpers
+//
+// Wave-wide reductions use DPP inside each row of 16 lanes (swap neighbours,
+// swap pairs, mirror half-rows, mirror rows) and then read the four row
+// results with readlane, so no step goes through the LDS crossbar.
 
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-    return (uint64_t(hi) << 32) | lo;
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kCtrl, 0xF, 0xF, false));
 }
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return uint32_t(__builtin_amdgcn_readlane(int(v), lane));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __uint_as_float(readlane_u32(__float_as_uint(v), lane));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    return (uint64_t(readlane_u32(uint32_t(v >> 32), lane)) << 32) | readlane_u32(uint32_t(v), lane);
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) { return readlane_u64(v, 0); }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) k = umax64(k, __shfl_xor(k, o));
-    return k;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)),
+               max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
@@ -101,6 +128,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // (m, s) with s = sum e^(x - m): merge (m2, s2) into (m, s).  A max of -inf
 // (nothing finite seen) contributes nothing and never forms -inf - -inf.
+// Symmetric in its two operands, so both lanes of a butterfly agree bit for bit.
 __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
     const float M = fmaxf(m, m2);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
@@ -108,32 +136,49 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
     m = M;
 }
 
+template <int kCtrl>
+__device__ __forceinline__ void lse_dpp_step(float &m, float &s) {
+    const float m2 = dpp_f32<kCtrl>(m);
+    const float s2 = dpp_f32<kCtrl>(s);
+    lse_merge(m, s, m2, s2);
+}
+
+// Every lane ends with the wave's (m, s), merged in a fixed order.
 __device__ __forceinline__ void wave_lse(float &m, float &s) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o);
-        const float s2 = __shfl_xor(s, o);
-        lse_merge(m, s, m2, s2);
-    }
+    lse_dpp_step<kDppXor1>(m, s);
+    lse_dpp_step<kDppXor2>(m, s);
+    lse_dpp_step<kDppHalfMirror>(m, s);
+    lse_dpp_step<kDppMirror>(m, s);
+    float M = readlane_f32(m, 0), S = readlane_f32(s, 0);
+    lse_merge(M, S, readlane_f32(m, 16), readlane_f32(s, 16));
+    float M2 = readlane_f32(m, 32), S2 = readlane_f32(s, 32);
+    lse_merge(M2, S2, readlane_f32(m, 48), readlane_f32(s, 48));
+    lse_merge(M, S, M2, S2);
+    m = M;
+    s = S;
 }
 
 // Best 7 keys of up to kPer*64 keys held kPer per lane (0 = empty).  Returns,
-// in lane r < 7, the r-th best key (0 if fewer exist); every lane gets the
-// count of nonzero keys found in *count.
+// in lane r < 7, the r-th best key (0 if fewer exist); *count gets how many
+// were found.  Each round finds the largest high word across the wave, then
+// the largest low word among keys with that high word (keys are unique).
 template <int kPer>
 __device__ __forceinline__ uint64_t wave_select7(uint64_t (&e)[kPer], int lane, uint32_t *count) {
     uint64_t mine = 0;
     uint32_t found = 0;
-#pragma unroll
+#pragma unroll 1
     for (int r = 0; r < kSlots; ++r) {
         uint64_t b = e[0];
 #pragma unroll
         for (int i = 1; i < kPer; ++i) b = umax64(b, e[i]);
-        b = uniform64(wave_max_u64(b));
-        if (b == 0) break;  // uniform: nothing left
+        const uint32_t bh = uint32_t(b >> 32);
+        const uint32_t H = wave_max_u32(bh);
+        if (H == 0) break;  // uniform: nothing left
+        const uint32_t L = wave_max_u32(bh == H ? uint32_t(b) : 0u);
+        const uint64_t win = (uint64_t(H) << 32) | L;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) e[i] = (e[i] == b) ? 0ull : e[i];  // keys are unique
-        if (lane == r) mine = b;
+        for (int i = 0; i < kPer; ++i) e[i] = (e[i] == win) ? 0ull : e[i];
+        if (lane == r) mine = win;
         ++found;
     }
     *count = found;
@@ -142,66 +187,141 @@ __device__ __forceinline__ uint64_t wave_select7(uint64_t (&e)[kPer], int lane, 
 
 // ------------------------------------------------------------------ candidates
 
-struct WaveCands {
-    uint64_t *buf;  // this wave's kCap keys in LDS
-    uint32_t n;     // keys held (wave-uniform)
-    uint64_t T;     // keep only keys > T (wave-uniform)
+constexpr int kInsertMax = 24;       // above this many candidates in a chunk, merge in bulk
+constexpr int kDppShr1 = 0x111;      // row_shr:1: lane i reads lane i-1 of its row of 16
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64_or0(uint64_t v) {
+    return (uint64_t(dpp_u32<kCtrl>(uint32_t(v >> 32))) << 32) | dpp_u32<kCtrl>(uint32_t(v));
+}
+
+// A wave's exact top-7 keys so far, spread over lanes: lane r < 7 holds the
+// r-th best (0 = empty), other lanes hold 0.  T (wave-uniform) is the 7th
+// key, or a larger bound that another wave of the workgroup published.
+struct WaveTop {
+    uint64_t L;
+    uint64_t T;
 };
 
-// Keeps the 7 best keys at buf[0..7) and raises T to the 7th.
-__device__ __forceinline__ void compress(WaveCands &c, int lane) {
-    constexpr int kPer = kCap / kWave;
-    uint64_t e[kPer];
+// Inserts a wave-uniform key that is not in the list yet, all slots at once:
+// slots holding smaller keys shift down by one lane (row_shr:1) and the first
+// of them takes k.
+__device__ __forceinline__ void top_insert(WaveTop &w, uint64_t k, int lane) {
+    const uint64_t prev = dpp_u64_or0<kDppShr1>(w.L);   // slot above (lane 0: none)
+    const bool below = k > w.L;
+    const bool take_k = lane == 0 || prev > k;
+    const uint64_t nl = below ? (take_k ? k : prev) : w.L;
+    w.L = lane < kSlots ? nl : 0ull;
+    w.T = umax64(w.T, readlane_u64(w.L, kSlots - 1));
+}
+
+// The smallest value a key above T can have; a cheap superset test for
+// candidates (below the key of -inf, nothing is excluded).
+__device__ __forceinline__ float threshold_value(uint64_t T) {
+    return uint32_t(T >> 32) >= 0x007FFFFFu ? key_value(T) : -INFINITY;
+}
+
+// Exact merge of candidate keys (those above T) into the list by one
+// wave-wide selection over the candidates and the list together.  A key
+// already in the list may also be among the candidates: the selection removes
+// every copy of the key it picks, so duplicates count once.
+template <int kN>
+__device__ __forceinline__ void bulk_merge(WaveTop &w, uint64_t (&f)[kN + 1], int lane) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < c.n ? c.buf[idx] : 0ull;
-    }
+    for (int j = 0; j < kN; ++j) f[j] = f[j] > w.T ? f[j] : 0ull;
+    f[kN] = w.L;
     uint32_t found;
-    const uint64_t mine = wave_select7<kPer>(e, lane, &found);
-    if (lane < int(found)) c.buf[lane] = mine;
-    c.n = found;
-    if (found == uint32_t(kSlots)) {
-        const uint64_t seventh = uniform64(__shfl(mine, kSlots - 1));
-        c.T = umax64(c.T, seventh);
-    }
+    w.L = wave_select7<kN + 1>(f, lane, &found);
+    w.T = umax64(w.T, readlane_u64(w.L, kSlots - 1));
 }
 
-// Appends the keys of lanes where `pred` holds.
-__device__ __forceinline__ void push(WaveCands &c, uint64_t key, bool pred, int lane) {
-    uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    if (c.n + uint32_t(__popcll(mask)) > uint32_t(kCap)) {
-        compress(c, lane);
-        pred = pred && key > c.T;
-        mask = __ballot(pred);
-        if (mask == 0) return;
+// Inserts the keys of one column (one key per lane) that are above T.
+// Returns false, inserting nothing, when that would exceed the budget.
+__device__ __forceinline__ bool insert_column(WaveTop &w, uint64_t k, uint32_t &budget, int lane) {
+    uint64_t mask = __ballot(k > w.T);
+    if (mask == 0) return true;
+    const uint32_t n = uint32_t(__popcll(mask));
+    if (n > budget) return false;
+    budget -= n;
+    while (mask != 0) {
+        const int l = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        top_insert(w, readlane_u64(k, l), lane);
     }
-    const uint32_t pos = c.n + lanes_below(mask);
-    if (pred) c.buf[pos] = key;
-    c.n += uint32_t(__popcll(mask));
+    return true;
 }
 
-// First full chunk of a wave: 7 distinct elements (the maxima of 7 lanes) are
-// at least the 7th largest lane maximum t, so every key below (t, any id) can
-// be dropped.  Sets T just under the smallest key of value t.
-__device__ __forceinline__ void seed_threshold(WaveCands &c, float lane_max) {
+__device__ __forceinline__ float f4_get(const float4 &v, int q) {
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
+// Raises T from the lanes' running maxima: if 7 lanes have each seen an
+// element of value >= t (counting lanes that tie), no element below t can be
+// in the top 7, so T may rise to just under the smallest key of value t.
+// Every lane's running max must be a real element of this wave's range.
+__device__ __forceinline__ void tighten_from_lane_max(WaveTop &w, float lane_max) {
     float v = lane_max;
     float t = -INFINITY;
     uint32_t cnt = 0;
-#pragma unroll
+#pragma unroll 1
     for (int r = 0; r < kSlots; ++r) {
         const float mx = wave_max_f32(v);
-        const uint64_t eq = __ballot(v == mx);
-        cnt += uint32_t(__popcll(eq));
+        cnt += uint32_t(__popcll(__ballot(v == mx)));
         t = mx;
         if (cnt >= uint32_t(kSlots)) break;
         v = (v == mx) ? -INFINITY : v;
     }
     if (cnt >= uint32_t(kSlots)) {
-        const uint64_t k = uniform64(order_key(t, kPadId));  // low word 0: smallest key of value t
-        if (k > 0) c.T = umax64(c.T, k - 1);
+        const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
+        if (k > 0) w.T = umax64(w.T, k - 1);
     }
+}
+
+// Merges a chunk's keys above T into the list.  A wave's first chunk first
+// seeds T from the lanes' maxima.  A float compare against T's value skips
+// the columns with no candidate; the others are inserted while few
+// candidates arrive, else (heavy ties) the chunk is merged in bulk, one
+// float4 column group at a time.  Keys are rebuilt in the bulk path from
+// register copies the compiler cannot see through, so the common path never
+// keeps a chunk's keys alive.
+template <int kU_>
+__device__ __forceinline__ void chunk_merge(WaveTop &w, const float4 (&x)[kU_], uint32_t first_id,
+                                            float lane_max, int lane) {
+    if (w.T == 0) tighten_from_lane_max(w, lane_max);
+    uint32_t budget = uint32_t(kInsertMax);
+    const float tv = threshold_value(w.T);
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < 4 * kU_; ++j) {
+        const int u = j >> 2, q = j & 3;
+        const float v = f4_get(x[u], q);
+        if (__ballot(v >= tv) == 0) continue;
+        const uint64_t k = order_key(v, first_id + 4u * uint32_t(u * kWave) + q);
+        if (!insert_column(w, k, budget, lane)) {
+            ok = false;
+            break;
+        }
+    }
+    if (ok) return;
+#pragma unroll
+    for (int u = 0; u < kU_; ++u) {
+        float y[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(y[q]));
+        const uint32_t id = first_id + 4u * uint32_t(u * kWave);
+        uint64_t f[5];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f[q] = order_key(y[q], id + uint32_t(q));
+        bulk_merge<4>(w, f, lane);
+    }
+}
+
+// One key per lane (head / tail elements).
+__device__ __forceinline__ void single_merge(WaveTop &w, uint64_t k, int lane) {
+    uint32_t budget = uint32_t(kInsertMax);
+    if (insert_column(w, k, budget, lane)) return;
+    uint64_t f[2] = {k, 0ull};
+    bulk_merge<1>(w, f, lane);
 }
 
 // ------------------------------------------------------------------ row kernel
@@ -214,7 +334,7 @@ struct RowArgs {
     uint32_t out_rows;
     const RowDesc *desc;
     float *out_lp;             // split == 1: (R, 8)
-    uint32_t *out_id;
+    uint32_t *out_id;          // split == 1: (R, 8)
     PartialRec *partials;      // split > 1: (R, split)
 };
 
@@ -239,11 +359,12 @@ __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, u
     }
 }
 
-__global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
-    __shared__ uint64_t s_buf[kWaves][kCap];
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
+    constexpr int kThreads = kWaves * kWave;
+    __shared__ uint64_t s_keys[kWaves * kSlots];
     __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
-    __shared__ uint32_t s_n[kWaves];
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
@@ -252,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
     const uint32_t seg = blockIdx.x - o * a.split;
     const RowDesc d = a.desc[o];
 
-    if (d.top_n == 0) {  // padding-only row: no logits read
+    if (d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
         if (a.split == 1 && wave == 0) write_padding(a.out_lp, a.out_id, o, lane);
         return;
     }
@@ -266,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
     if (tid == 0) s_T = 0;
     __syncthreads();
 
-    WaveCands c{s_buf[wave], 0u, 0ull};
+    WaveTop w{0ull, 0ull};
     float m = -INFINITY, s = 0.0f;
 
     // aligned body: float4 loads from a 16-byte aligned element a0
@@ -280,13 +401,13 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
     const float4 *body = reinterpret_cast<const float4 *>(row + a0);
 
-    auto load_chunk = [&](float4 (&x)[kU], uint32_t ch) {
+    auto load_chunk = [&](float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
         const float4 *p = body + uint64_t(ch) * kChunkF4 + lane;
 #pragma unroll
         for (int u = 0; u < kU; ++u) x[u] = p[u * kWave];
     };
 
-    auto process_chunk = [&](const float4 (&x)[kU], uint32_t ch) {
+    auto process_chunk = [&](const float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
         float cm = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
 #pragma unroll
         for (int u = 1; u < kU; ++u)
@@ -305,26 +426,15 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
         s = s * fast_exp2((m - ms) * kLog2e) + csum;
         m = mn;
 
+        // any element of this lane's chunk has a key <= order_key(cm, first_id)
         const uint32_t first_id = a0 + 4u * (ch * uint32_t(kChunkF4) + uint32_t(lane));
         const uint64_t kc = order_key(cm, first_id);
-        if (__ballot(kc > c.T) == 0) return;              // common case
-        c.T = umax64(c.T, uniform64(*(volatile uint64_t *)&s_T));
-        if (__ballot(kc > c.T) == 0) return;
-        const uint64_t t_before = c.T;
-        if (c.T == 0) seed_threshold(c, cm);
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const uint32_t id = a0 + 4u * (ch * uint32_t(kChunkF4) + uint32_t(u * kWave + lane));
-            const uint64_t k0 = order_key(x[u].x, id + 0);
-            push(c, k0, k0 > c.T, lane);
-            const uint64_t k1 = order_key(x[u].y, id + 1);
-            push(c, k1, k1 > c.T, lane);
-            const uint64_t k2 = order_key(x[u].z, id + 2);
-            push(c, k2, k2 > c.T, lane);
-            const uint64_t k3 = order_key(x[u].w, id + 3);
-            push(c, k3, k3 > c.T, lane);
-        }
-        if (c.T != t_before && lane == 0) atomicMax((unsigned long long *)&s_T, c.T);
+        if (__ballot(kc > w.T) == 0) return;              // common case
+        const uint64_t t_before = w.T;
+        w.T = umax64(w.T, uniform64(*(volatile uint64_t *)&s_T));
+        if (__ballot(kc > w.T) == 0) return;
+        chunk_merge<kU>(w, x, first_id, m, lane);
+        if (w.T != t_before && lane == 0) atomicMax((unsigned long long *)&s_T, w.T);
     };
 
     // two chunks in flight per wave
@@ -348,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
     // head (before a0) and tail (after the last full chunk): one element per
     // thread per pass
     {
-        c.T = umax64(c.T, uniform64(*(volatile uint64_t *)&s_T));
+        w.T = umax64(w.T, uniform64(*(volatile uint64_t *)&s_T));
         const uint32_t nh = a0 - v0;
         const uint32_t tail0 = a0 + nchunks * uint32_t(kChunkF4) * 4u;
         const uint32_t nrest = nh + (v1 - tail0);
@@ -356,45 +466,45 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowArgs a) {
             const uint32_t r = base + uint32_t(tid);
             const bool valid = r < nrest;
             const uint32_t e = (r < nh) ? v0 + r : tail0 + (r - nh);
-            const float x = valid ? row[e] : -INFINITY;
+            float x = -INFINITY;
+            if (valid) x = row[e];
             const float mn = fmaxf(m, x);
             const float ms = (mn == -INFINITY) ? 0.0f : mn;
             s = s * fast_exp2((m - ms) * kLog2e) + fast_exp2((x - ms) * kLog2e);
             m = mn;
-            const uint64_t k = valid ? order_key(x, e) : 0ull;
-            push(c, k, valid && k > c.T, lane);
+            single_merge(w, valid ? order_key(x, e) : 0ull, lane);
         }
     }
 
-    // per wave: (m, s) across lanes, candidates down to <= 7
+    // per wave: (m, s) across lanes and the wave's 7 keys into LDS
     wave_lse(m, s);
-    if (c.n > uint32_t(kSlots)) compress(c, lane);
+    if (lane < kSlots) s_keys[wave * kSlots + lane] = w.L;
     if (lane == 0) {
         s_m[wave] = m;
         s_s[wave] = s;
-        s_n[wave] = c.n;
     }
     __syncthreads();
     if (wave != 0) return;
 
-    // workgroup merge in wave 0
+    // workgroup merge in wave 0: the kWaves * 7 keys spread over the lanes
     constexpr int kPer = (kWaves * kSlots + kWave - 1) / kWave;
     uint64_t e[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int idx = lane + kWave * i;
-        const int w = idx / kSlots, j = idx - (idx / kSlots) * kSlots;
-        e[i] = (w < kWaves && uint32_t(j) < s_n[w < kWaves ? w : 0]) ? s_buf[w < kWaves ? w : 0][j] : 0ull;
+        e[i] = idx < kWaves * kSlots ? s_keys[idx < kWaves * kSlots ? idx : 0] : 0ull;
     }
     uint32_t found;
     const uint64_t mine = wave_select7<kPer>(e, lane, &found);
-    float M = lane < kWaves ? s_m[lane < kWaves ? lane : 0] : -INFINITY;
-    float S = lane < kWaves ? s_s[lane < kWaves ? lane : 0] : 0.0f;
+    float M = -INFINITY, S = 0.0f;
+    if (lane < kWaves) {
+        M = s_m[lane];
+        S = s_s[lane];
+    }
     wave_lse(M, S);
 
     if (a.split == 1) {
-        const float lse = M + logf(S);
-        write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, lse, row, d.chosen);
+        write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, M + logf(S), row, d.chosen);
     } else {
         PartialRec *rec = a.partials + uint64_t(o) * a.split + seg;
         if (lane == 0) {
@@ -418,11 +528,11 @@ struct MergeArgs {
     uint32_t *out_id;
 };
 
-// One wave per output row: combines the row's `split` segment records in
-// segment order, then writes the row.
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+// Split variant, second launch: one wave per output row combines the row's
+// segment records in segment order, then writes the row.
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int lane = int(threadIdx.x) & (kWave - 1);
-    const uint32_t o = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const uint32_t o = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (o >= a.out_rows) return;
     const RowDesc d = a.desc[o];
     if (d.top_n == 0) {
@@ -430,13 +540,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         return;
     }
     const PartialRec *recs = a.partials + uint64_t(o) * a.split;
-    float M = -INFINITY, S = 0.0f;
+    float m = -INFINITY, s = 0.0f;
     if (uint32_t(lane) < a.split) {
-        M = recs[lane].m;
-        S = recs[lane].s;
+        m = recs[lane].m;
+        s = recs[lane].s;
     }
-    wave_lse(M, S);
-
+    wave_lse(m, s);
     constexpr int kPer = (int(kMaxSplit) * kSlots + kWave - 1) / kWave;
     const uint32_t nkeys = a.split * uint32_t(kSlots);
     uint64_t e[kPer];
@@ -446,10 +555,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         e[i] = idx < nkeys ? recs[idx / kSlots].keys[idx % kSlots] : 0ull;
     }
     uint32_t found;
-    const uint64_t mine = wave_select7<kPer>(e, lane, &found);
+    const uint64_t top = wave_select7<kPer>(e, lane, &found);
     const float *row = a.src + uint64_t(d.src_row) * a.vocab;
-    const float lse = M + logf(S);
-    write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, lse, row, d.chosen);
+    write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), row, d.chosen);
 }
 
 // ------------------------------------------------------------------ streaming-read probe
@@ -553,13 +661,13 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     if (src == nullptr) return LP_ERR_NULL_ARG;
     lp_status st = lp::check_workspace(plan, workspace, workspace_bytes);
     if (st != LP_OK) return st;
+    const uint32_t waves = plan->waves;
     const uint64_t blocks = plan->out_rows * plan->split;
-    if (blocks * lp::dev::kThreads >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
+    if (blocks * waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto *desc = static_cast<const lp::RowDesc *>(workspace);
-    auto *partials = reinterpret_cast<lp::PartialRec *>(static_cast<char *>(workspace) +
-                                                        plan->desc_bytes);
+    char *ws = static_cast<char *>(workspace);
+    auto *desc = reinterpret_cast<const lp::RowDesc *>(ws);
+    auto *partials = reinterpret_cast<lp::PartialRec *>(ws + plan->desc_bytes);
     lp::dev::RowArgs ra;
     ra.src = src;
     ra.vocab = plan->vocab;
@@ -571,8 +679,14 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ra.out_lp = out_logprobs;
     ra.out_id = out_token_ids;
     ra.partials = partials;
-    hipLaunchKernelGGL(lp::dev::row_kernel, dim3(static_cast<uint32_t>(blocks)),
-                       dim3(lp::dev::kThreads), 0, s, ra);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    if (waves == 16)
+        hipLaunchKernelGGL(lp::dev::row_kernel<16>, grid, dim3(16 * 64), 0, s, ra);
+    else if (waves == 8)
+        hipLaunchKernelGGL(lp::dev::row_kernel<8>, grid, dim3(8 * 64), 0, s, ra);
+    else
+        hipLaunchKernelGGL(lp::dev::row_kernel<4>, grid, dim3(4 * 64), 0, s, ra);
     LP_HIP_TRY(hipGetLastError());
     if (plan->split > 1) {
         lp::dev::MergeArgs ma;
@@ -584,10 +698,8 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
         ma.partials = partials;
         ma.out_lp = out_logprobs;
         ma.out_id = out_token_ids;
-        const uint32_t mblocks =
-            static_cast<uint32_t>((plan->out_rows + lp::dev::kWaves - 1) / lp::dev::kWaves);
-        hipLaunchKernelGGL(lp::dev::merge_kernel, dim3(mblocks), dim3(lp::dev::kThreads), 0, s,
-                           ma);
+        const uint32_t mblocks = static_cast<uint32_t>((plan->out_rows + 3) / 4);
+        hipLaunchKernelGGL(lp::dev::merge_kernel, dim3(mblocks), dim3(256), 0, s, ma);
         LP_HIP_TRY(hipGetLastError());
     }
     return LP_OK;

@@ -27,6 +27,7 @@ static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
 
 // Partial result of one (row, vocabulary segment) in the split variant:
 // the segment's running max and scaled sum, and its 7 best order keys.
+// Workspace layout: [R descriptors, padded to 256 B][R x split records].
 struct PartialRec {
     float m;
     float s;
@@ -51,6 +52,7 @@ struct lp_plan {
     uint64_t out_rows = 0;
     uint64_t read_rows = 0;
     uint32_t split = 1;
+    uint32_t waves = 4;              // waves per workgroup: 4, 8 or 16
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 64 when split > 1
     uint64_t workspace_bytes = 0;

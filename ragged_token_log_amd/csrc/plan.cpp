@@ -27,20 +27,35 @@ void size_workspace(lp_plan &p) {
     p.workspace_bytes = p.desc_bytes + p.partial_bytes;
 }
 
-// Vocabulary segments per row.  Rows are independent, so a launch with many
-// rows runs one workgroup per row; a launch with too few rows to occupy the
-// chip splits each row into segments (each at least kMinSegment elements) and
-// merges their partial results in a second kernel.
-static uint32_t choose_split(uint64_t read_rows, uint32_t vocab) {
-    constexpr uint64_t kTargetWorkgroups = 512;  // 2 per CU on 256 CUs
-    constexpr uint32_t kMinSegment = 8192;
-    if (read_rows == 0 || read_rows >= kTargetWorkgroups) return 1;
-    uint64_t s = (kTargetWorkgroups + read_rows - 1) / read_rows;
+// Kernel shape: waves per workgroup and vocabulary segments per row.  Rows
+// are independent, so a launch with many rows runs one workgroup of 4 waves
+// per row.  Fewer rows get more waves per row, so each row is streamed by
+// more loads in flight; too few rows to occupy 256 CUs even then are split
+// into segments (one workgroup each, at least kMinSegment elements), whose
+// partial results a second kernel merges.
+static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
+                           uint32_t *split) {
+    constexpr uint64_t kManyRows = 1024;
+    constexpr uint64_t kSomeRows = 384;
+    constexpr uint64_t kCUs = 256;
+    constexpr uint32_t kMinSegment = 32768;
+    *split = 1;
+    if (read_rows >= kManyRows || read_rows == 0) {
+        *waves = 4;
+        return;
+    }
+    if (read_rows >= kSomeRows) {
+        *waves = 8;
+        return;
+    }
+    *waves = 16;
+    if (read_rows >= kCUs) return;
+    uint64_t s = (kCUs + read_rows - 1) / read_rows;
     uint64_t by_vocab = vocab / kMinSegment;
     if (by_vocab < 1) by_vocab = 1;
     if (s > by_vocab) s = by_vocab;
     if (s > kMaxSplit) s = kMaxSplit;
-    return static_cast<uint32_t>(s);
+    *split = static_cast<uint32_t>(s);
 }
 
 lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
@@ -142,7 +157,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         delete p;
         return LP_ERR_NOMEM;
     }
-    p->split = lp::choose_split(p->read_rows, vocab);
+    lp::choose_variant(p->read_rows, vocab, &p->waves, &p->split);
     lp::size_workspace(*p);
 
     if (output_row_offsets != nullptr)
@@ -162,6 +177,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
     info->out_rows = plan->out_rows;
     info->read_rows = plan->read_rows;
     info->split = plan->split;
+    info->waves = plan->waves;
     info->has_logits = plan->has_logits;
     info->workspace_bytes = plan->workspace_bytes;
     return LP_OK;
@@ -172,6 +188,13 @@ lp_status lp_plan_set_split(lp_plan *plan, uint32_t split) {
     if (split < 1 || split > lp::kMaxSplit) return LP_ERR_UNSUPPORTED;
     plan->split = split;
     lp::size_workspace(*plan);
+    return LP_OK;
+}
+
+lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (waves != 4 && waves != 8 && waves != 16) return LP_ERR_UNSUPPORTED;
+    plan->waves = waves;
     return LP_OK;
 }
 

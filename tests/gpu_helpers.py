@@ -27,9 +27,10 @@ class DeviceRows:
         return self.t[int(r)].cpu().numpy()
 
 
-def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None):
+def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None,
+                waves=None):
     lp, ids, out_off = R.compute_log_probabilities_ragged(
-        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split)
+        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves)
     torch.cuda.synchronize()
     return lp.cpu().numpy(), ids.cpu().numpy(), out_off
 

@@ -91,6 +91,13 @@ def test_split_and_workspace():
     with pytest.raises(R.LogprobError) as e:
         plan.set_split(65)
     assert e.value.name == "LP_ERR_UNSUPPORTED"
+    plan.set_waves(8)
+    assert plan.info()["waves"] == 8
+    plan.set_waves(16)
+    assert plan.info()["waves"] == 16
+    with pytest.raises(R.LogprobError) as e:
+        plan.set_waves(6)
+    assert e.value.name == "LP_ERR_UNSUPPORTED"
     big = R.Plan(np.arange(2001, dtype=np.uint32), np.ones(2000, bool), np.full(2000, 5), 32000,
                  True)
     assert big.split == 1

@@ -201,6 +201,21 @@ class Plan:
                                           _dev_ptr(workspace), _nbytes(workspace),
                                           _stream_ptr(stream)), "lp_launch_ragged")
 
+    def launcher(self, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
+                 stream=None):
+        """A zero-argument callable doing lp_launch_ragged with these buffers,
+        its ctypes arguments converted once (for tight launch loops)."""
+        fn = self._lib.lp_launch_ragged
+        args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _dev_ptr(out_logprobs),
+                _dev_ptr(out_token_ids), _dev_ptr(workspace), ctypes.c_uint64(_nbytes(workspace)),
+                _stream_ptr(stream))
+
+        def launch():
+            st = fn(*args)
+            if st != 0:
+                _check(st, "lp_launch_ragged")
+        return launch
+
     def compute(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
                 out_token_ids, workspace, stream=None):
         tok = _u32(tokens) if tokens is not None else None

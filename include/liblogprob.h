@@ -73,7 +73,7 @@ typedef struct lp_plan_info {
                                  > 1 = one workgroup per segment plus a merge kernel */
     uint32_t has_logits;      /* 1 if full logits are given */
     uint32_t waves;           /* waves per workgroup (4, 8 or 16) */
-    uint32_t reserved;
+    uint32_t depth;           /* 16-byte-load chunks in flight per wave (2 or 4) */
     uint64_t workspace_bytes; /* device scratch lp_compute_ragged needs */
 } lp_plan_info;
 
@@ -119,6 +119,10 @@ lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
 /* Overrides the waves per workgroup (4, 8 or 16); LP_ERR_UNSUPPORTED otherwise.
  * Results do not depend on it beyond fp32 rounding of the log-probabilities. */
 lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
+
+/* Overrides the chunks in flight per wave (2 or 4); LP_ERR_UNSUPPORTED
+ * otherwise.  Results are identical for either value. */
+lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
 
 /*
  * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of

@@ -25,7 +25,7 @@ STATUS_NAMES = {
 # every symbol include/liblogprob.h declares
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
-    "lp_plan_descriptors",
+    "lp_plan_set_depth", "lp_plan_descriptors",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
@@ -52,7 +52,7 @@ class PlanInfo(ctypes.Structure):
         ("levels", ctypes.c_uint32), ("columns", ctypes.c_uint32),
         ("out_rows", ctypes.c_uint64), ("read_rows", ctypes.c_uint64),
         ("split", ctypes.c_uint32), ("has_logits", ctypes.c_uint32),
-        ("waves", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("waves", ctypes.c_uint32), ("depth", ctypes.c_uint32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -77,6 +77,7 @@ def load():
     lib.lp_plan_get_info.argtypes = [vp, P(PlanInfo)]
     lib.lp_plan_set_split.argtypes = [vp, u32]
     lib.lp_plan_set_waves.argtypes = [vp, u32]
+    lib.lp_plan_set_depth.argtypes = [vp, u32]
     lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
     lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
@@ -88,7 +89,7 @@ def load():
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
-                 "lp_plan_set_waves", "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
+                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -174,6 +175,9 @@ class Plan:
 
     def set_waves(self, waves: int):
         _check(self._lib.lp_plan_set_waves(self._h, int(waves)), "lp_plan_set_waves")
+
+    def set_depth(self, depth: int):
+        _check(self._lib.lp_plan_set_depth(self._h, int(depth)), "lp_plan_set_depth")
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
         """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
@@ -279,7 +283,7 @@ def alloc_outputs(plan: Plan, device, torch):
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens,
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
-                                     stream=None):
+                                     depth: int | None = None, stream=None):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -311,6 +315,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
             plan.set_split(split)
         if waves is not None:
             plan.set_waves(waves)
+        if depth is not None:
+            plan.set_depth(depth)
         device = next_token_logits.device
         if stream is None:
             stream = torch.cuda.current_stream(device)

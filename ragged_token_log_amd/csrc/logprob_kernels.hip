@@ -120,12 +120,33 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
                max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    v += dpp_u32<kDppXor1>(v);
+    v += dpp_u32<kDppXor2>(v);
+    v += dpp_u32<kDppHalfMirror>(v);
+    v += dpp_u32<kDppMirror>(v);
+    return (readlane_u32(v, 0) + readlane_u32(v, 16)) + (readlane_u32(v, 32) + readlane_u32(v, 48));
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders this wave's LDS accesses around an LDS counter: the workgroup-scope
+// fences restricted to LDS wait only for outstanding LDS operations, never
+// for the wave's in-flight global loads.
+__device__ __forceinline__ void lds_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
+__device__ __forceinline__ void lds_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
+
+// Lane 0 adds 1 to an LDS counter; every lane gets the previous value.
+__device__ __forceinline__ uint32_t lds_arrive(uint32_t *counter, int lane) {
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return readlane_u32(prev, 0);
+}
 
 // Logits are read exactly once: nontemporal 16-byte loads (the `nt` form of
 // global_load_dwordx4) stream them without displacing reusable cache lines;
@@ -287,8 +308,37 @@ __device__ __forceinline__ void tighten_from_lane_max(WaveTop &w, float lane_max
     }
 }
 
-// Merges a chunk's keys above T into the list.  A wave's first chunk first
-// seeds T from the lanes' maxima.  A float compare against T's value skips
+// Seeds T from the first-chunk maxima of all waves of the workgroup
+// (vals: kN values per lane, -inf where a wave had no chunk): the 7th largest,
+// counting ties, is reached by 7 distinct real elements unless it is -inf,
+// and a -inf bound excludes nothing.  Every wave computes the same T.
+template <int kN>
+__device__ __forceinline__ void seed_from_maxima(WaveTop &w, float (&v)[kN]) {
+    float t = -INFINITY;
+    uint32_t cnt = 0;
+#pragma unroll 1
+    for (int r = 0; r < kSlots; ++r) {
+        float lm = v[0];
+#pragma unroll
+        for (int i = 1; i < kN; ++i) lm = fmaxf(lm, v[i]);
+        const float mx = wave_max_f32(lm);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < kN; ++i) c += v[i] == mx ? 1u : 0u;
+        cnt += wave_sum_u32(c);
+        t = mx;
+        if (cnt >= uint32_t(kSlots)) break;
+#pragma unroll
+        for (int i = 0; i < kN; ++i) v[i] = v[i] == mx ? -INFINITY : v[i];
+    }
+    if (cnt >= uint32_t(kSlots)) {
+        const uint64_t k = order_key(t, kPadId);
+        if (k > 0) w.T = umax64(w.T, k - 1);
+    }
+}
+
+// Merges a chunk's keys above T into the list.  A wave whose T is still 0
+// first seeds it from its own lanes' maxima.  A float compare against T's value skips
 // the columns with no candidate; the others are inserted while few
 // candidates arrive, else (heavy ties) the chunk is merged in bulk, one
 // float4 column group at a time.  Keys are rebuilt in the bulk path from
@@ -369,12 +419,14 @@ __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, u
     }
 }
 
-template <int kWaves>
+template <int kWaves, int kDepth>
 __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
     __shared__ uint64_t s_keys[kWaves * kSlots];
+    __shared__ float s_lmax[kWaves * kWave];
     __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
+    __shared__ uint32_t s_seeded, s_done;
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
@@ -393,9 +445,6 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint64_t seg_start = uint64_t(seg) * a.seg_len;
     const uint32_t v0 = seg_start < V ? uint32_t(seg_start) : V;
     const uint32_t v1 = (uint64_t(v0) + a.seg_len < V) ? v0 + a.seg_len : V;
-
-    if (tid == 0) s_T = 0;
-    __syncthreads();
 
     WaveTop w{0ull, 0ull};
     float m = -INFINITY, s = 0.0f;
@@ -417,7 +466,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         for (int u = 0; u < kU; ++u) x[u] = stream_load(p + u * kWave);
     };
 
-    auto process_chunk = [&](const float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+    // LSE update for one chunk; returns the lane's chunk max
+    auto lse_chunk = [&](const float4 (&x)[kU]) __attribute__((always_inline)) {
         float cm = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
 #pragma unroll
         for (int u = 1; u < kU; ++u)
@@ -435,7 +485,11 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         for (int u = 1; u < kU; ++u) csum += acc[u];
         s = s * fast_exp2((m - ms) * kLog2e) + csum;
         m = mn;
+        return cm;
+    };
 
+    // top-k part for one chunk whose lane maxima are cm
+    auto topk_chunk = [&](const float4 (&x)[kU], uint32_t ch, float cm) __attribute__((always_inline)) {
         // any element of this lane's chunk has a key <= order_key(cm, first_id)
         const uint32_t first_id = a0 + 4u * (ch * uint32_t(kChunkF4) + uint32_t(lane));
         const uint64_t kc = order_key(cm, first_id);
@@ -447,21 +501,52 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         if (w.T != t_before && lane == 0) atomicMax((unsigned long long *)&s_T, w.T);
     };
 
-    // two chunks in flight per wave
+    auto process_chunk = [&](const float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+        const float cm = lse_chunk(x);
+        topk_chunk(x, ch, cm);
+    };
+
+    // kDepth chunks in flight per wave (register buffers used in rotation).
+    // Each wave publishes its first chunk's lane maxima; the last wave to do
+    // so seeds one threshold for the whole workgroup from all of them, while
+    // the others carry on (no wave waits for another).
     {
-        float4 xa[kU], xb[kU];
+        float4 xb[kDepth][kU];
         uint32_t ch = uint32_t(wave);
-        if (ch < nchunks) load_chunk(xa, ch);
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            if (ch + uint32_t(d * kWaves) < nchunks) load_chunk(xb[d], ch + uint32_t(d * kWaves));
+        if (tid == 0) {
+            s_T = 0;
+            s_seeded = 0;
+            s_done = 0;
+        }
+        __syncthreads();
+        float cm0 = -INFINITY;
+        if (ch < nchunks) cm0 = lse_chunk(xb[0]);
+        s_lmax[wave * kWave + lane] = cm0;
+        lds_release();
+        if (lds_arrive(&s_seeded, lane) == uint32_t(kWaves - 1)) {
+            lds_acquire();
+            float v[kWaves];
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) v[i] = s_lmax[i * kWave + lane];
+            seed_from_maxima<kWaves>(w, v);
+            if (lane == 0) atomicMax((unsigned long long *)&s_T, w.T);
+        }
+        if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
+        constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
+        if (ch + kAhead < nchunks) load_chunk(xb[0], ch + kAhead);
+        ch += kWaves;
+        // buffer d % kDepth holds chunk ch on the d-th step of each round
         while (ch < nchunks) {
-            const uint32_t ch2 = ch + kWaves;
-            if (ch2 < nchunks) load_chunk(xb, ch2);
-            process_chunk(xa, ch);
-            ch = ch2;
-            if (ch >= nchunks) break;
-            const uint32_t ch3 = ch + kWaves;
-            if (ch3 < nchunks) load_chunk(xa, ch3);
-            process_chunk(xb, ch);
-            ch = ch3;
+#pragma unroll
+            for (int d = 1; d <= kDepth; ++d) {
+                if (ch >= nchunks) break;
+                process_chunk(xb[d % kDepth], ch);
+                if (ch + kAhead < nchunks) load_chunk(xb[d % kDepth], ch + kAhead);
+                ch += kWaves;
+            }
         }
     }
 
@@ -486,17 +571,19 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         }
     }
 
-    // per wave: (m, s) across lanes and the wave's 7 keys into LDS
+    // per wave: (m, s) across lanes and the wave's 7 keys into LDS; the last
+    // wave of the workgroup to get here merges them
     wave_lse(m, s);
     if (lane < kSlots) s_keys[wave * kSlots + lane] = w.L;
     if (lane == 0) {
         s_m[wave] = m;
         s_s[wave] = s;
     }
-    __syncthreads();
-    if (wave != 0) return;
+    lds_release();
+    if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
+    lds_acquire();
 
-    // workgroup merge in wave 0: the kWaves * 7 keys spread over the lanes
+    // workgroup merge: the kWaves * 7 keys spread over the lanes
     constexpr int kPer = (kWaves * kSlots + kWave - 1) / kWave;
     uint64_t e[kPer];
 #pragma unroll
@@ -691,12 +778,17 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ra.partials = partials;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<uint32_t>(blocks));
-    if (waves == 16)
-        hipLaunchKernelGGL(lp::dev::row_kernel<16>, grid, dim3(16 * 64), 0, s, ra);
-    else if (waves == 8)
-        hipLaunchKernelGGL(lp::dev::row_kernel<8>, grid, dim3(8 * 64), 0, s, ra);
-    else
-        hipLaunchKernelGGL(lp::dev::row_kernel<4>, grid, dim3(4 * 64), 0, s, ra);
+    const bool deep = plan->depth == 4;
+    if (waves == 16) {
+        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<16, 4>), grid, dim3(16 * 64), 0, s, ra);
+        else hipLaunchKernelGGL((lp::dev::row_kernel<16, 2>), grid, dim3(16 * 64), 0, s, ra);
+    } else if (waves == 8) {
+        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<8, 4>), grid, dim3(8 * 64), 0, s, ra);
+        else hipLaunchKernelGGL((lp::dev::row_kernel<8, 2>), grid, dim3(8 * 64), 0, s, ra);
+    } else {
+        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<4, 4>), grid, dim3(4 * 64), 0, s, ra);
+        else hipLaunchKernelGGL((lp::dev::row_kernel<4, 2>), grid, dim3(4 * 64), 0, s, ra);
+    }
     LP_HIP_TRY(hipGetLastError());
     if (plan->split > 1) {
         lp::dev::MergeArgs ma;

@@ -53,6 +53,7 @@ struct lp_plan {
     uint64_t read_rows = 0;
     uint32_t split = 1;
     uint32_t waves = 4;              // waves per workgroup: 4, 8 or 16
+    uint32_t depth = 2;              // chunks in flight per wave: 2 or 4
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 64 when split > 1
     uint64_t workspace_bytes = 0;

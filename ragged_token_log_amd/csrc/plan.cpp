@@ -178,6 +178,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
     info->read_rows = plan->read_rows;
     info->split = plan->split;
     info->waves = plan->waves;
+    info->depth = plan->depth;
     info->has_logits = plan->has_logits;
     info->workspace_bytes = plan->workspace_bytes;
     return LP_OK;
@@ -195,6 +196,13 @@ lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (waves != 4 && waves != 8 && waves != 16) return LP_ERR_UNSUPPORTED;
     plan->waves = waves;
+    return LP_OK;
+}
+
+lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (depth != 2 && depth != 4) return LP_ERR_UNSUPPORTED;
+    plan->depth = depth;
     return LP_OK;
 }
 

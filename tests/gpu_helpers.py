@@ -28,9 +28,9 @@ class DeviceRows:
 
 
 def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None,
-                waves=None):
+                waves=None, depth=None):
     lp, ids, out_off = R.compute_log_probabilities_ragged(
-        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves)
+        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves, depth=depth)
     torch.cuda.synchronize()
     return lp.cpu().numpy(), ids.cpu().numpy(), out_off
 

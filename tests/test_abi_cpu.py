@@ -95,6 +95,10 @@ def test_split_and_workspace():
     assert plan.info()["waves"] == 8
     plan.set_waves(16)
     assert plan.info()["waves"] == 16
+    plan.set_depth(4)
+    assert plan.info()["depth"] == 4
+    with pytest.raises(R.LogprobError):
+        plan.set_depth(3)
     with pytest.raises(R.LogprobError) as e:
         plan.set_waves(6)
     assert e.value.name == "LP_ERR_UNSUPPORTED"

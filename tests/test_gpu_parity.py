@@ -80,14 +80,14 @@ def _edge_batch(seed, vocab):
 
 
 @pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 111, 1000, 1027, 4099, 8193, 20011, 70001])
-@pytest.mark.parametrize("split,waves", [(None, None), (1, 4), (2, 8), (5, 4), (64, 8), (1, 16),
-                                         (3, 16)])
-def test_edge_cases(R, vocab, split, waves):
-    log(f"edge cases vocab={vocab} split={split} waves={waves}")
+@pytest.mark.parametrize("split,waves,depth", [(None, None, None), (1, 4, 2), (2, 8, 4), (5, 4, 4),
+                                               (64, 8, 2), (1, 16, 4), (3, 16, 2)])
+def test_edge_cases(R, vocab, split, waves, depth):
+    log(f"edge cases vocab={vocab} split={split} waves={waves} depth={depth}")
     off, logits, ntl, tokens, sampled, top_n, echo = _edge_batch(vocab * 7 + 1, vocab)
     ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo)
     got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split,
-                      waves)
+                      waves, depth)
     assert_parity(*got, ref, f"edge vocab={vocab} split={split} waves={waves}")
 
 
@@ -99,13 +99,13 @@ def test_adversarial_orders(R):
     rows = np.stack([base, base[::-1].copy(), np.tile(base[:1000], vocab // 1000),
                      np.round(base * 2) / 2])
     off = np.arange(5, dtype=np.uint32)
-    for split, waves in ((1, 4), (1, 8), (3, 4), (1, 16), (2, 16)):
+    for split, waves, depth in ((1, 4, 2), (1, 8, 4), (3, 4, 4), (1, 16, 2), (2, 16, 4)):
         ref = oracle(off, rows, rows, np.zeros(4, np.uint32), np.array([0, 1, 2, 3], np.uint32),
                      np.full(4, 7), np.ones(4, bool))
         got = run_library(R, torch, off, _dev(rows), _dev(rows), np.zeros(4, np.uint32),
                           np.array([0, 1, 2, 3], np.uint32), np.full(4, 7), np.ones(4, bool),
-                          split, waves)
-        assert_parity(*got, ref, f"adversarial split={split} waves={waves}")
+                          split, waves, depth)
+        assert_parity(*got, ref, f"adversarial split={split} waves={waves} depth={depth}")
 
 
 @pytest.mark.parametrize("split", [None, 1, 3])
@@ -131,14 +131,14 @@ def test_ragged_echo_mix(R, split):
     assert_parity(*got, ref, "ragged_echo_mix")
 
 
-@pytest.mark.parametrize("split,waves", [(None, None), (1, 4), (16, 8), (1, 16)])
-def test_decode_peaked(R, split, waves):
+@pytest.mark.parametrize("split,waves,depth", [(None, None, None), (1, 4, 2), (16, 8, 4), (1, 16, 4)])
+def test_decode_peaked(R, split, waves, depth):
     c = gen.decode_peaked()
     ntl = gen.host_logits(c)
-    log(f"decode_peaked split={split} waves={waves}")
+    log(f"decode_peaked split={split} waves={waves} depth={depth}")
     ref = oracle(c.offsets, None, ntl, c.tokens, c.sampled, c.top_n, c.echo)
     got = run_library(R, torch, c.offsets, None, _dev(ntl), c.tokens, c.sampled, c.top_n, c.echo,
-                      split, waves)
+                      split, waves, depth)
     assert_parity(*got, ref, "decode_peaked")
     # the chosen slot holds the sampled (boosted) token in every row
     assert np.array_equal(got[1][:, 7], c.sampled)
@@ -189,9 +189,9 @@ def test_deterministic_and_split_independent(R):
     a = run_library(R, torch, *args)
     b = run_library(R, torch, *args)
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
-    for s, w in ((2, 4), (4, 8), (64, 4), (1, 8), (1, 16), (5, 16)):
-        d = run_library(R, torch, *args, split=s, waves=w)
-        assert np.array_equal(a[1], d[1]), (s, w)
+    for s, w, dp in ((2, 4, 2), (4, 8, 4), (64, 4, 4), (1, 8, 2), (1, 16, 4), (5, 16, 2)):
+        d = run_library(R, torch, *args, split=s, waves=w, depth=dp)
+        assert np.array_equal(a[1], d[1]), (s, w, dp)
         np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
 
 

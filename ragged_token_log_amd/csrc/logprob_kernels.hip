@@ -13,23 +13,21 @@
 //
 //  * Each row (or row segment) is one workgroup of 4, 8 or 16 waves.  Waves
 //    take interleaved chunks of 64 lanes x kU float4, read with nontemporal
-//    loads.  Per chunk a lane
-//    reduces its 16 values to a chunk max, updates a running (m, s) with
-//    s = sum e^(x-m) (exp2 with log2(e) applied after an exact subtraction),
-//    and compares one order key -- built from the chunk max and the lane's
-//    first token id -- against the wave's threshold T.
+//    buffer loads, two chunks in flight per wave.  Per chunk a lane reduces
+//    its 16 values to a chunk max and updates a running (m, s) with
+//    s = sum e^(x-m) (exp2 with log2(e) applied after an exact subtraction).
 //  * Ranking uses a 64-bit order key: the fp32 bits mapped to an unsigned
 //    order (with -0.0 folded onto +0.0) in the high word, the complemented
 //    token id in the low word.  A larger key is a better (value, id) pair, so
 //    ties go to the lowest id and every merge uses one total order.
-//  * Each wave keeps its exact top-7 keys so far spread over lanes 0..6, and
-//    T = the 7th of them, raised further to any T another wave of the
-//    workgroup has published in LDS (a key that 7 real elements beat can
-//    never enter).  A chunk that beats T has its keys merged into the list:
-//    one by one (a lane-parallel shift) when they are few, else by one
-//    wave-wide selection over the chunk and the list.
-//  * The waves' (m, s) pairs and top-7 lists merge through LDS; the
-//    epilogue writes lp = x - (m + ln s) for the 7 slots and the chosen token.
+//  * The workgroup keeps one shared list of the 7 best keys entered so far in
+//    LDS, filled by cascades of atomic max operations, and every wave filters
+//    its chunks against one bound T: a seed taken from all waves' first
+//    chunks (one barrier), raised to the list's 7th key as it fills.  A chunk
+//    whose lane maxima stay below T costs one compare; the few columns that
+//    beat it enter their keys one at a time.
+//  * The waves' (m, s) pairs merge through LDS; the last wave to finish
+//    writes lp = x - (m + ln s) for the 7 listed keys and the chosen token.
 //  * With too few rows to fill 256 CUs, a row is split into segments, one
 //    workgroup each, which write (m, s, 7 keys) records; a second kernel (one
 //    wave per row) merges a row's records in segment order and writes it.
@@ -120,19 +118,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
                max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-    v += dpp_u32<kDppXor1>(v);
-    v += dpp_u32<kDppXor2>(v);
-    v += dpp_u32<kDppHalfMirror>(v);
-    v += dpp_u32<kDppMirror>(v);
-    return (readlane_u32(v, 0) + readlane_u32(v, 16)) + (readlane_u32(v, 32) + readlane_u32(v, 48));
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Orders this wave's LDS accesses around an LDS counter: the workgroup-scope
@@ -140,6 +125,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // for the wave's in-flight global loads.
 __device__ __forceinline__ void lds_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
 __device__ __forceinline__ void lds_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
+
+// A relaxed read of an LDS word that other waves update atomically.  It stays
+// an LDS access (a volatile read through a generic pointer would become a flat
+// access, whose wait also drains the wave's in-flight global loads).
+__device__ __forceinline__ uint64_t lds_load_relaxed(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // Lane 0 adds 1 to an LDS counter; every lane gets the previous value.
 __device__ __forceinline__ uint32_t lds_arrive(uint32_t *counter, int lane) {
@@ -149,12 +141,27 @@ __device__ __forceinline__ uint32_t lds_arrive(uint32_t *counter, int lane) {
 }
 
 // Logits are read exactly once: nontemporal 16-byte loads (the `nt` form of
-// global_load_dwordx4) stream them without displacing reusable cache lines;
+// buffer_load_dwordx4) stream them without displacing reusable cache lines;
 // on gfx950 they sustain ~13% more HBM bandwidth than plain loads here.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 stream_load(const float4 *p) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kAuxNontemporal = 2;         // cache-policy bit of the buffer load: nt
+
+struct StreamRange {
+    __amdgpu_buffer_rsrc_t rsrc;
+};
+
+// A raw buffer over `bytes` bytes starting at p (16-byte aligned); the range
+// fits 31 bits because a segment holds at most 2^29 elements.
+__device__ __forceinline__ StreamRange make_stream_range(const float *p, uint32_t bytes) {
+    return StreamRange{__builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), 0, int(bytes), kBufferWord3)};
+}
+
+// 16 bytes at byte offset off; zeros, with no memory access, past the range.
+__device__ __forceinline__ f32x4 stream_load(const StreamRange &r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r.rsrc, off, 0, kAuxNontemporal));
 }
 
 // (m, s) with s = sum e^(x - m): merge (m2, s2) into (m, s).  A max of -inf
@@ -217,34 +224,18 @@ __device__ __forceinline__ uint64_t wave_select7(uint64_t (&e)[kPer], int lane, 
 }
 
 // ------------------------------------------------------------------ candidates
-
-constexpr int kInsertMax = 24;       // above this many candidates in a chunk, merge in bulk
-constexpr int kDppShr1 = 0x111;      // row_shr:1: lane i reads lane i-1 of its row of 16
-
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_u64_or0(uint64_t v) {
-    return (uint64_t(dpp_u32<kCtrl>(uint32_t(v >> 32))) << 32) | dpp_u32<kCtrl>(uint32_t(v));
-}
-
-// A wave's exact top-7 keys so far, spread over lanes: lane r < 7 holds the
-// r-th best (0 = empty), other lanes hold 0.  T (wave-uniform) is the 7th
-// key, or a larger bound that another wave of the workgroup published.
-struct WaveTop {
-    uint64_t L;
-    uint64_t T;
-};
-
-// Inserts a wave-uniform key that is not in the list yet, all slots at once:
-// slots holding smaller keys shift down by one lane (row_shr:1) and the first
-// of them takes k.
-__device__ __forceinline__ void top_insert(WaveTop &w, uint64_t k, int lane) {
-    const uint64_t prev = dpp_u64_or0<kDppShr1>(w.L);   // slot above (lane 0: none)
-    const bool below = k > w.L;
-    const bool take_k = lane == 0 || prev > k;
-    const uint64_t nl = below ? (take_k ? k : prev) : w.L;
-    w.L = lane < kSlots ? nl : 0ull;
-    w.T = umax64(w.T, readlane_u64(w.L, kSlots - 1));
-}
+//
+// A workgroup keeps one list of the 7 best keys entered so far, in LDS slots
+// (descending; 0 = empty).  A key enters by a cascade of atomic max
+// operations down the slots: at each slot the atomic leaves the larger of
+// (slot, key) there and hands the smaller on to the next slot.  Every key
+// visits the slots in order and a slot keeps the largest key that ever
+// reached it, so whatever the interleaving of the waves' cascades, slot i ends
+// with the (i+1)-th best of all keys entered, and at every moment the slots
+// are in descending order.  A key handed on at or below a bound T that 7
+// other real keys exceed can be dropped.  All waves filter against one bound,
+// T = max(seed, slot 6): the seed comes from the first chunks' lane maxima,
+// slot 6 is the 7th best key entered so far.
 
 // The smallest value a key above T can have; a cheap superset test for
 // candidates (below the key of -inf, nothing is excluded).
@@ -252,46 +243,49 @@ __device__ __forceinline__ float threshold_value(uint64_t T) {
     return uint32_t(T >> 32) >= 0x007FFFFFu ? key_value(T) : -INFINITY;
 }
 
-// Exact merge of candidate keys (those above T) into the list by one
-// wave-wide selection over the candidates and the list together.  A key
-// already in the list may also be among the candidates: the selection removes
-// every copy of the key it picks, so duplicates count once.
-template <int kN>
-__device__ __forceinline__ void bulk_merge(WaveTop &w, uint64_t (&f)[kN + 1], int lane) {
-#pragma unroll
-    for (int j = 0; j < kN; ++j) f[j] = f[j] > w.T ? f[j] : 0ull;
-    f[kN] = w.L;
-    uint32_t found;
-    w.L = wave_select7<kN + 1>(f, lane, &found);
-    w.T = umax64(w.T, readlane_u64(w.L, kSlots - 1));
-}
-
-// Inserts the keys of one column (one key per lane) that are above T.
-// Returns false, inserting nothing, when that would exceed the budget.
-__device__ __forceinline__ bool insert_column(WaveTop &w, uint64_t k, uint32_t &budget, int lane) {
-    uint64_t mask = __ballot(k > w.T);
-    if (mask == 0) return true;
-    const uint32_t n = uint32_t(__popcll(mask));
-    if (n > budget) return false;
-    budget -= n;
-    while (mask != 0) {
-        const int l = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        top_insert(w, readlane_u64(k, l), lane);
+// Enters the lanes' keys that are above T (a lane passes 0 to enter none)
+// and returns a bound at least T.  Keys go one at a time, as wave-uniform
+// values, each with one atomic per slot it moves through.  Slots only ever
+// grow, so a key below what a slot held at a snapshot would pass that slot
+// unchanged: a key starts at the first slot the snapshot had below it,
+// mostly the last one.  After a key settles in the last slot, that slot
+// holds at least the larger of its old value and the key, which bounds the
+// later keys.
+__device__ __forceinline__ uint64_t enter_keys(uint64_t *slots, uint64_t k, uint64_t T, int lane) {
+    uint64_t live = __ballot(k > T);
+    if (live == 0) return T;
+    const uint64_t held = lds_load_relaxed(slots + (lane < kSlots ? lane : kSlots - 1));
+    const bool slot_lane = lane < kSlots;
+    while (live != 0) {
+        const int l = __builtin_ctzll(live);
+        live &= live - 1;
+        uint64_t kk = readlane_u64(k, l);
+        if (kk <= T) continue;
+        uint32_t i = uint32_t(__popcll(__ballot(slot_lane && held > kk)));
+        for (; i < uint32_t(kSlots); ++i) {
+            uint64_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_max(slots + i, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = readlane_u64(old, 0);
+            if (i == uint32_t(kSlots - 1)) T = umax64(T, umax64(old, kk));
+            if (old < kk) {
+                kk = old;             // the slot took the key; the old one moves on
+                if (kk <= T) break;
+            }
+        }
     }
-    return true;
+    return T;
 }
 
-__device__ __forceinline__ float f4_get(const float4 &v, int q) {
+__device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// Raises T from the lanes' running maxima: if 7 lanes have each seen an
-// element of value >= t (counting lanes that tie), no element below t can be
-// in the top 7, so T may rise to just under the smallest key of value t.
-// Every lane's running max must be a real element of this wave's range.
-__device__ __forceinline__ void tighten_from_lane_max(WaveTop &w, float lane_max) {
-    float v = lane_max;
+// A bound from one real element per lane (or -inf for none): if 7 lanes hold
+// values >= t (counting lanes that tie), no element below t can be in the
+// top 7, so the bound may be just under the smallest key of value t.  A -inf
+// t excludes nothing.
+__device__ __forceinline__ uint64_t bound_from_lane_values(float v) {
     float t = -INFINITY;
     uint32_t cnt = 0;
 #pragma unroll 1
@@ -302,86 +296,9 @@ __device__ __forceinline__ void tighten_from_lane_max(WaveTop &w, float lane_max
         if (cnt >= uint32_t(kSlots)) break;
         v = (v == mx) ? -INFINITY : v;
     }
-    if (cnt >= uint32_t(kSlots)) {
-        const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
-        if (k > 0) w.T = umax64(w.T, k - 1);
-    }
-}
-
-// Seeds T from the first-chunk maxima of all waves of the workgroup
-// (vals: kN values per lane, -inf where a wave had no chunk): the 7th largest,
-// counting ties, is reached by 7 distinct real elements unless it is -inf,
-// and a -inf bound excludes nothing.  Every wave computes the same T.
-template <int kN>
-__device__ __forceinline__ void seed_from_maxima(WaveTop &w, float (&v)[kN]) {
-    float t = -INFINITY;
-    uint32_t cnt = 0;
-#pragma unroll 1
-    for (int r = 0; r < kSlots; ++r) {
-        float lm = v[0];
-#pragma unroll
-        for (int i = 1; i < kN; ++i) lm = fmaxf(lm, v[i]);
-        const float mx = wave_max_f32(lm);
-        uint32_t c = 0;
-#pragma unroll
-        for (int i = 0; i < kN; ++i) c += v[i] == mx ? 1u : 0u;
-        cnt += wave_sum_u32(c);
-        t = mx;
-        if (cnt >= uint32_t(kSlots)) break;
-#pragma unroll
-        for (int i = 0; i < kN; ++i) v[i] = v[i] == mx ? -INFINITY : v[i];
-    }
-    if (cnt >= uint32_t(kSlots)) {
-        const uint64_t k = order_key(t, kPadId);
-        if (k > 0) w.T = umax64(w.T, k - 1);
-    }
-}
-
-// Merges a chunk's keys above T into the list.  A wave whose T is still 0
-// first seeds it from its own lanes' maxima.  A float compare against T's value skips
-// the columns with no candidate; the others are inserted while few
-// candidates arrive, else (heavy ties) the chunk is merged in bulk, one
-// float4 column group at a time.  Keys are rebuilt in the bulk path from
-// register copies the compiler cannot see through, so the common path never
-// keeps a chunk's keys alive.
-template <int kU_>
-__device__ __forceinline__ void chunk_merge(WaveTop &w, const float4 (&x)[kU_], uint32_t first_id,
-                                            float lane_max, int lane) {
-    if (w.T == 0) tighten_from_lane_max(w, lane_max);
-    uint32_t budget = uint32_t(kInsertMax);
-    const float tv = threshold_value(w.T);
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < 4 * kU_; ++j) {
-        const int u = j >> 2, q = j & 3;
-        const float v = f4_get(x[u], q);
-        if (__ballot(v >= tv) == 0) continue;
-        const uint64_t k = order_key(v, first_id + 4u * uint32_t(u * kWave) + q);
-        if (!insert_column(w, k, budget, lane)) {
-            ok = false;
-            break;
-        }
-    }
-    if (ok) return;
-#pragma unroll
-    for (int u = 0; u < kU_; ++u) {
-        float y[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(y[q]));
-        const uint32_t id = first_id + 4u * uint32_t(u * kWave);
-        uint64_t f[5];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) f[q] = order_key(y[q], id + uint32_t(q));
-        bulk_merge<4>(w, f, lane);
-    }
-}
-
-// One key per lane (head / tail elements).
-__device__ __forceinline__ void single_merge(WaveTop &w, uint64_t k, int lane) {
-    uint32_t budget = uint32_t(kInsertMax);
-    if (insert_column(w, k, budget, lane)) return;
-    uint64_t f[2] = {k, 0ull};
-    bulk_merge<1>(w, f, lane);
+    if (cnt < uint32_t(kSlots)) return 0ull;
+    const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
+    return k > 0 ? k - 1 : 0ull;
 }
 
 // ------------------------------------------------------------------ row kernel
@@ -400,16 +317,24 @@ struct RowArgs {
 
 __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint64_t o, int lane,
                                           uint64_t key, uint32_t top_n, float lse,
-                                          const float *row, uint32_t chosen) {
+                                          float x_chosen, uint32_t chosen) {
     // lanes 0..6: ranked slots; lane 7: the chosen token
     if (lane < kSlots) {
         const bool valid = uint32_t(lane) < top_n && key != 0;
         out_lp[o * kCols + lane] = valid ? key_value(key) - lse : -INFINITY;
         out_id[o * kCols + lane] = valid ? key_id(key) : kPadId;
     } else if (lane == kSlots) {
-        out_lp[o * kCols + lane] = row[chosen] - lse;
+        out_lp[o * kCols + lane] = x_chosen - lse;
         out_id[o * kCols + lane] = chosen;
     }
+}
+
+// The whole descriptor of a workgroup's row in one 16-byte scalar load (not
+// one dependent load per field as they are first used).
+__device__ __forceinline__ RowDesc load_desc_uniform(const RowDesc *desc, uint32_t o) {
+    uint4 v = *reinterpret_cast<const uint4 *>(desc + o);
+    asm volatile("" : "+s"(v.x), "+s"(v.y), "+s"(v.z));
+    return RowDesc{v.x, v.y, v.z, v.w};
 }
 
 __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, uint64_t o, int lane) {
@@ -422,18 +347,17 @@ __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, u
 template <int kWaves, int kDepth>
 __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
-    __shared__ uint64_t s_keys[kWaves * kSlots];
+    __shared__ uint64_t s_top[kSlots];
     __shared__ float s_lmax[kWaves * kWave];
-    __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
-    __shared__ uint32_t s_seeded, s_done;
+    __shared__ uint32_t s_done;
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: loop control stays scalar
     const uint32_t o = blockIdx.x / a.split;
     const uint32_t seg = blockIdx.x - o * a.split;
-    const RowDesc d = a.desc[o];
+    const RowDesc d = load_desc_uniform(a.desc, o);
 
     if (d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
         if (a.split == 1 && wave == 0) write_padding(a.out_lp, a.out_id, o, lane);
@@ -446,8 +370,15 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t v0 = seg_start < V ? uint32_t(seg_start) : V;
     const uint32_t v1 = (uint64_t(v0) + a.seg_len < V) ? v0 + a.seg_len : V;
 
-    WaveTop w{0ull, 0ull};
-    float m = -INFINITY, s = 0.0f;
+    float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^(x - m)
+    float x_chosen;
+    // wave-uniform filter state: seed bound, T = max(seed, slot 6), T's value
+    uint64_t seed = 0, T = 0;
+    float tv = -INFINITY;
+    auto refresh = [&]() __attribute__((always_inline)) {
+        T = umax64(seed, uniform64(lds_load_relaxed(&s_top[kSlots - 1])));
+        tv = threshold_value(T);
+    };
 
     // aligned body: float4 loads from a 16-byte aligned element a0
     uint32_t a0 = v0;
@@ -458,16 +389,31 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     }
     const uint32_t nf4 = (v1 - a0) >> 2;
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
-    const float4 *body = reinterpret_cast<const float4 *>(row + a0);
 
-    auto load_chunk = [&](float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
-        const float4 *p = body + uint64_t(ch) * kChunkF4 + lane;
+    // The body's full chunks are read through a buffer resource whose range
+    // ends after the last of them: a load of a chunk past the end returns
+    // zeros without touching memory.  So every refill is unconditional, no
+    // buffer value ever merges two paths, and the compiler keeps each buffer
+    // in place instead of copying buffers at the loop's back edge (a copy
+    // would first wait for every load in flight).
+    const StreamRange body = make_stream_range(row + a0, nchunks * uint32_t(kChunkF4 * 16));
+    auto load_chunk = [&](f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+        const uint32_t off = ch * uint32_t(kChunkF4 * 16) + uint32_t(lane) * 16u;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) x[u] = stream_load(p + u * kWave);
+        for (int u = 0; u < kU; ++u) x[u] = stream_load(body, off + uint32_t(u * kWave * 16));
+    };
+    // Scheduling barriers keep the loads where they are: after the last use
+    // of the buffer's old values (so the new ones can take the same
+    // registers) and ahead of the wait for the next buffer (so that the other
+    // loads stay in flight meanwhile).
+    auto refill = [&](f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk(x, ch);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // LSE update for one chunk; returns the lane's chunk max
-    auto lse_chunk = [&](const float4 (&x)[kU]) __attribute__((always_inline)) {
+    auto lse_chunk = [&](const f32x4 (&x)[kU]) __attribute__((always_inline)) {
         float cm = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
 #pragma unroll
         for (int u = 1; u < kU; ++u)
@@ -488,63 +434,96 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         return cm;
     };
 
-    // top-k part for one chunk whose lane maxima are cm
-    auto topk_chunk = [&](const float4 (&x)[kU], uint32_t ch, float cm) __attribute__((always_inline)) {
-        // any element of this lane's chunk has a key <= order_key(cm, first_id)
+    // Top-k part for one chunk whose lane maxima are cm, against the bound
+    // as of this chunk.  A float compare of the lane maxima with T's value
+    // passes almost every chunk by; then the order key of (lane max, the
+    // lane's first id), which no key of the lane's chunk exceeds; then one
+    // float compare per column, and the columns with candidates cascade.
+    auto topk_chunk = [&](const f32x4 (&x)[kU], uint32_t ch, float cm) __attribute__((always_inline)) {
+        if (__ballot(cm >= tv) == 0) return;
         const uint32_t first_id = a0 + 4u * (ch * uint32_t(kChunkF4) + uint32_t(lane));
-        const uint64_t kc = order_key(cm, first_id);
-        if (__ballot(kc > w.T) == 0) return;              // common case
-        const uint64_t t_before = w.T;
-        w.T = umax64(w.T, uniform64(*(volatile uint64_t *)&s_T));
-        if (__ballot(kc > w.T) == 0) return;
-        chunk_merge<kU>(w, x, first_id, m, lane);
-        if (w.T != t_before && lane == 0) atomicMax((unsigned long long *)&s_T, w.T);
+        if (__ballot(order_key(cm, first_id) > T) == 0) return;
+        // columns (u, q) holding a candidate, then one column at a time
+        // through a single copy of the entry code (uniform register indexing)
+        static_assert(kU == 4, "16 columns per chunk");
+        uint32_t cols = 0;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const float gm = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
+            if (__ballot(gm >= tv) == 0) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                cols |= (__ballot(f4_get(x[u], q) >= tv) != 0 ? 1u : 0u) << (4 * u + q);
+        }
+        const f32x16 xv = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                                  __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                                  0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        while (cols != 0) {
+            const uint32_t j = uint32_t(__builtin_ctz(cols));
+            cols &= cols - 1;
+            const uint32_t id = first_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u);
+            T = enter_keys(s_top, order_key(xv[j], id), T, lane);
+        }
+        tv = threshold_value(T);
     };
 
-    auto process_chunk = [&](const float4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+    // The bound is re-read from LDS for every chunk, the read issued before
+    // the chunk's arithmetic so that its latency hides there.
+    auto process_chunk = [&](const f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
+        const uint64_t s6 = lds_load_relaxed(&s_top[kSlots - 1]);
         const float cm = lse_chunk(x);
+        T = umax64(seed, uniform64(s6));
+        tv = threshold_value(T);
         topk_chunk(x, ch, cm);
     };
 
     // kDepth chunks in flight per wave (register buffers used in rotation).
-    // Each wave publishes its first chunk's lane maxima; the last wave to do
-    // so seeds one threshold for the whole workgroup from all of them, while
-    // the others carry on (no wave waits for another).
+    // After the first chunk every wave publishes its lanes' chunk maxima; past
+    // one barrier each wave takes, per lane position, the max over the waves
+    // and seeds the threshold from the 7th largest of those 64 values, so all
+    // waves start from the same bound for the whole workgroup's first chunks.
     {
-        float4 xb[kDepth][kU];
+        f32x4 xb[kDepth][kU];
         uint32_t ch = uint32_t(wave);
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
-            if (ch + uint32_t(d * kWaves) < nchunks) load_chunk(xb[d], ch + uint32_t(d * kWaves));
-        if (tid == 0) {
-            s_T = 0;
-            s_seeded = 0;
-            s_done = 0;
-        }
-        __syncthreads();
+            refill(xb[d], ch + uint32_t(d * kWaves));
+        // the chosen token's logit, fetched now so that its latency hides under
+        // the stream instead of trailing the final merge (a per-lane index keeps
+        // it a vector load that nothing waits on before its use)
+        x_chosen = row[(a.split == 1 && lane == kSlots) ? d.chosen : 0u];
+        if (tid < kSlots) s_top[tid] = 0;
+        if (tid == 0) s_done = 0;
         float cm0 = -INFINITY;
         if (ch < nchunks) cm0 = lse_chunk(xb[0]);
         s_lmax[wave * kWave + lane] = cm0;
-        lds_release();
-        if (lds_arrive(&s_seeded, lane) == uint32_t(kWaves - 1)) {
-            lds_acquire();
-            float v[kWaves];
+        __syncthreads();
+        {
+            float cmx = s_lmax[lane];
 #pragma unroll
-            for (int i = 0; i < kWaves; ++i) v[i] = s_lmax[i * kWave + lane];
-            seed_from_maxima<kWaves>(w, v);
-            if (lane == 0) atomicMax((unsigned long long *)&s_T, w.T);
+            for (int i = 1; i < kWaves; ++i) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
+            seed = bound_from_lane_values(cmx);
+            T = seed;
+            tv = threshold_value(T);
         }
         if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
         constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
-        if (ch + kAhead < nchunks) load_chunk(xb[0], ch + kAhead);
+        refill(xb[0], ch + kAhead);
         ch += kWaves;
-        // buffer d % kDepth holds chunk ch on the d-th step of each round
-        while (ch < nchunks) {
+        // The remaining chunks of this wave go in whole rounds of kDepth steps
+        // (buffer d % kDepth holds chunk ch on the d-th step of a round); in
+        // the last round, steps past the end skip their chunk and their
+        // refill reads nothing.  The loop has one exit, at its bottom, and no
+        // buffer is read after it: an exit from the middle, or a use after
+        // the loop, would add paths on which buffers are copied between
+        // registers or every wait for loads in flight must be stricter.
+        const uint32_t mine = nchunks > uint32_t(wave) ? (nchunks - uint32_t(wave) + kWaves - 1) / kWaves : 0u;
+        const uint32_t rounds = mine > 1 ? (mine - 1 + kDepth - 1) / uint32_t(kDepth) : 0u;
+        for (uint32_t r = 0; r < rounds; ++r) {
 #pragma unroll
             for (int d = 1; d <= kDepth; ++d) {
-                if (ch >= nchunks) break;
-                process_chunk(xb[d % kDepth], ch);
-                if (ch + kAhead < nchunks) load_chunk(xb[d % kDepth], ch + kAhead);
+                if (ch < nchunks) process_chunk(xb[d % kDepth], ch);
+                refill(xb[d % kDepth], ch + kAhead);
                 ch += kWaves;
             }
         }
@@ -553,7 +532,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // head (before a0) and tail (after the last full chunk): one element per
     // thread per pass
     {
-        w.T = umax64(w.T, uniform64(*(volatile uint64_t *)&s_T));
+        refresh();
         const uint32_t nh = a0 - v0;
         const uint32_t tail0 = a0 + nchunks * uint32_t(kChunkF4) * 4u;
         const uint32_t nrest = nh + (v1 - tail0);
@@ -567,14 +546,13 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
             const float ms = (mn == -INFINITY) ? 0.0f : mn;
             s = s * fast_exp2((m - ms) * kLog2e) + fast_exp2((x - ms) * kLog2e);
             m = mn;
-            single_merge(w, valid ? order_key(x, e) : 0ull, lane);
+            T = enter_keys(s_top, valid ? order_key(x, e) : 0ull, T, lane);
         }
     }
 
-    // per wave: (m, s) across lanes and the wave's 7 keys into LDS; the last
-    // wave of the workgroup to get here merges them
+    // per wave: (m, s) across lanes into LDS; the last wave of the workgroup
+    // to get here merges them and writes the row (or the segment's record)
     wave_lse(m, s);
-    if (lane < kSlots) s_keys[wave * kSlots + lane] = w.L;
     if (lane == 0) {
         s_m[wave] = m;
         s_s[wave] = s;
@@ -583,16 +561,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
     lds_acquire();
 
-    // workgroup merge: the kWaves * 7 keys spread over the lanes
-    constexpr int kPer = (kWaves * kSlots + kWave - 1) / kWave;
-    uint64_t e[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int idx = lane + kWave * i;
-        e[i] = idx < kWaves * kSlots ? s_keys[idx < kWaves * kSlots ? idx : 0] : 0ull;
-    }
-    uint32_t found;
-    const uint64_t mine = wave_select7<kPer>(e, lane, &found);
+    const uint64_t mine = lane < kSlots ? lds_load_relaxed(&s_top[lane < kSlots ? lane : 0]) : 0ull;
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {
         M = s_m[lane];
@@ -601,7 +570,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     wave_lse(M, S);
 
     if (a.split == 1) {
-        write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, M + logf(S), row, d.chosen);
+        write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, M + logf(S), x_chosen, d.chosen);
     } else {
         PartialRec *rec = a.partials + uint64_t(o) * a.split + seg;
         if (lane == 0) {
@@ -636,6 +605,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         write_padding(a.out_lp, a.out_id, o, lane);
         return;
     }
+    const float *row = a.src + uint64_t(d.src_row) * a.vocab;
+    const float x_chosen = lane == kSlots ? row[d.chosen] : 0.0f;
     const PartialRec *recs = a.partials + uint64_t(o) * a.split;
     float m = -INFINITY, s = 0.0f;
     if (uint32_t(lane) < a.split) {
@@ -653,8 +624,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     uint32_t found;
     const uint64_t top = wave_select7<kPer>(e, lane, &found);
-    const float *row = a.src + uint64_t(d.src_row) * a.vocab;
-    write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), row, d.chosen);
+    write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), x_chosen, d.chosen);
 }
 
 // ------------------------------------------------------------------ streaming-read probe
@@ -769,8 +739,7 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ra.src = src;
     ra.vocab = plan->vocab;
     ra.split = plan->split;
-    ra.seg_len = static_cast<uint32_t>(
-        lp::align_up((uint64_t(plan->vocab) + plan->split - 1) / plan->split, 4));
+    ra.seg_len = static_cast<uint32_t>(lp::segment_length(plan->vocab, plan->split));
     ra.out_rows = static_cast<uint32_t>(plan->out_rows);
     ra.desc = desc;
     ra.out_lp = out_logprobs;

@@ -15,6 +15,17 @@ constexpr uint32_t kCols = 1u << kLevels;     // 8 output columns
 constexpr uint32_t kTopSlots = kCols - 1;     // 7 ranked slots + 1 chosen slot
 constexpr uint32_t kPadId = 0xFFFFFFFFu;
 constexpr uint32_t kMaxSplit = 64;
+// Longest vocabulary segment one workgroup streams: its byte range must fit
+// the 31-bit range of the buffer resource the row kernel reads it through.
+constexpr uint32_t kMaxSegment = 1u << 29;
+
+// Elements per segment when a row of `vocab` is cut into `split` segments
+// (a multiple of 4, so every segment but the first starts 16-byte aligned
+// whenever the row does).
+inline uint64_t segment_length(uint32_t vocab, uint32_t split) {
+    const uint64_t s = (uint64_t(vocab) + split - 1) / split;
+    return (s + 3) & ~uint64_t(3);
+}
 
 // One output row as the device sees it (16 bytes, one dwordx4 load).
 struct RowDesc {

@@ -39,7 +39,10 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
     constexpr uint64_t kSomeRows = 384;
     constexpr uint64_t kCUs = 256;
     constexpr uint32_t kMinSegment = 32768;
-    *split = 1;
+    // fewest segments that keep each within kMaxSegment (1 for any real vocabulary)
+    uint32_t min_split = 1;
+    while (segment_length(vocab, min_split) > kMaxSegment) ++min_split;
+    *split = min_split;
     if (read_rows >= kManyRows || read_rows == 0) {
         *waves = 4;
         return;
@@ -55,6 +58,7 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
     if (by_vocab < 1) by_vocab = 1;
     if (s > by_vocab) s = by_vocab;
     if (s > kMaxSplit) s = kMaxSplit;
+    if (s < min_split) s = min_split;
     *split = static_cast<uint32_t>(s);
 }
 
@@ -187,6 +191,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
 lp_status lp_plan_set_split(lp_plan *plan, uint32_t split) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (split < 1 || split > lp::kMaxSplit) return LP_ERR_UNSUPPORTED;
+    if (lp::segment_length(plan->vocab, split) > lp::kMaxSegment) return LP_ERR_UNSUPPORTED;
     plan->split = split;
     lp::size_workspace(*plan);
     return LP_OK;

@@ -107,6 +107,24 @@ def test_split_and_workspace():
     assert big.split == 1
 
 
+def test_segments_stay_within_the_streamed_range():
+    # one workgroup streams at most 2^29 elements of a row: a wider row is
+    # always cut into segments, and a split leaving longer segments is refused
+    many = 3000
+    wide = R.Plan(np.arange(many + 1, dtype=np.uint32), np.zeros(many, bool), np.full(many, 1),
+                  (1 << 31) + 1, False)
+    assert wide.split == 5
+    assert wide.workspace_bytes == ((many * 16 + 255) // 256) * 256 + many * 5 * 64
+    with pytest.raises(R.LogprobError) as e:
+        wide.set_split(4)
+    assert e.value.name == "LP_ERR_UNSUPPORTED"
+    edge = R.Plan(np.arange(many + 1, dtype=np.uint32), np.zeros(many, bool), np.full(many, 1),
+                  1 << 31, False)
+    assert edge.split == 4
+    edge.set_split(64)
+    assert edge.split == 64
+
+
 def _expect(name, fn):
     with pytest.raises(R.LogprobError) as e:
         fn()

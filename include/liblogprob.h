@@ -73,8 +73,13 @@ typedef struct lp_plan_info {
                                  > 1 = one workgroup per segment plus a merge kernel */
     uint32_t has_logits;      /* 1 if full logits are given */
     uint32_t waves;           /* waves per workgroup (4, 8 or 16) */
-    uint32_t depth;           /* 16-byte-load chunks in flight per wave (2 or 4) */
+    uint32_t depth;           /* 16-byte-load chunks in flight per wave (1 or 2) */
     uint64_t workspace_bytes; /* device scratch lp_compute_ragged needs */
+    uint32_t direct_rows;     /* 1 if output row o reads logits row o for every o (every
+                                 request echoes with full logits, or none has full logits,
+                                 and every top_n > 0): the kernel then addresses rows
+                                 without waiting for their descriptors */
+    uint32_t reserved;        /* 0 */
 } lp_plan_info;
 
 /*
@@ -120,7 +125,7 @@ lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
  * Results do not depend on it beyond fp32 rounding of the log-probabilities. */
 lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
 
-/* Overrides the chunks in flight per wave (2 or 4); LP_ERR_UNSUPPORTED
+/* Overrides the chunks in flight per wave (1 or 2); LP_ERR_UNSUPPORTED
  * otherwise.  Results are identical for either value. */
 lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
 

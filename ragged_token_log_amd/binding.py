@@ -54,6 +54,7 @@ class PlanInfo(ctypes.Structure):
         ("split", ctypes.c_uint32), ("has_logits", ctypes.c_uint32),
         ("waves", ctypes.c_uint32), ("depth", ctypes.c_uint32),
         ("workspace_bytes", ctypes.c_uint64),
+        ("direct_rows", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
     ]
 
 

@@ -225,56 +225,27 @@ __device__ __forceinline__ uint64_t wave_select7(uint64_t (&e)[kPer], int lane, 
 
 // ------------------------------------------------------------------ candidates
 //
-// A workgroup keeps one list of the 7 best keys entered so far, in LDS slots
-// (descending; 0 = empty).  A key enters by a cascade of atomic max
-// operations down the slots: at each slot the atomic leaves the larger of
-// (slot, key) there and hands the smaller on to the next slot.  Every key
-// visits the slots in order and a slot keeps the largest key that ever
-// reached it, so whatever the interleaving of the waves' cascades, slot i ends
-// with the (i+1)-th best of all keys entered, and at every moment the slots
-// are in descending order.  A key handed on at or below a bound T that 7
-// other real keys exceed can be dropped.  All waves filter against one bound,
-// T = max(seed, slot 6): the seed comes from the first chunks' lane maxima,
-// slot 6 is the 7th best key entered so far.
+// Each wave keeps the 7 best keys it has seen, sorted, one per lane in lanes
+// 0..6 (0 = empty).  A wave filters its elements against a bound T: a key at
+// or below T cannot be in the row's top 7, because 7 real keys above it are
+// known.  T is the larger of the wave's own 7th key and a workgroup-wide bound
+// in LDS, which every wave raises (atomic max) whenever its own bound rises:
+// any wave's 7th key bounds the whole row, since the 7 keys above it are real
+// elements of the row.  A seed starts T off from the first chunks' lane maxima.
 
-// The smallest value a key above T can have; a cheap superset test for
-// candidates (below the key of -inf, nothing is excluded).
+// The smallest value a key above T can have (below the key of -inf, nothing
+// is excluded): a float compare with it is a superset test for candidates,
+// ties to be settled by the key compare.
 __device__ __forceinline__ float threshold_value(uint64_t T) {
     return uint32_t(T >> 32) >= 0x007FFFFFu ? key_value(T) : -INFINITY;
 }
 
-// Enters the lanes' keys that are above T (a lane passes 0 to enter none)
-// and returns a bound at least T.  Keys go one at a time, as wave-uniform
-// values, each with one atomic per slot it moves through.  Slots only ever
-// grow, so a key below what a slot held at a snapshot would pass that slot
-// unchanged: a key starts at the first slot the snapshot had below it,
-// mostly the last one.  After a key settles in the last slot, that slot
-// holds at least the larger of its old value and the key, which bounds the
-// later keys.
-__device__ __forceinline__ uint64_t enter_keys(uint64_t *slots, uint64_t k, uint64_t T, int lane) {
-    uint64_t live = __ballot(k > T);
-    if (live == 0) return T;
-    const uint64_t held = lds_load_relaxed(slots + (lane < kSlots ? lane : kSlots - 1));
-    const bool slot_lane = lane < kSlots;
-    while (live != 0) {
-        const int l = __builtin_ctzll(live);
-        live &= live - 1;
-        uint64_t kk = readlane_u64(k, l);
-        if (kk <= T) continue;
-        uint32_t i = uint32_t(__popcll(__ballot(slot_lane && held > kk)));
-        for (; i < uint32_t(kSlots); ++i) {
-            uint64_t old = 0;
-            if (lane == 0)
-                old = __hip_atomic_fetch_max(slots + i, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            old = readlane_u64(old, 0);
-            if (i == uint32_t(kSlots - 1)) T = umax64(T, umax64(old, kk));
-            if (old < kk) {
-                kk = old;             // the slot took the key; the old one moves on
-                if (kk <= T) break;
-            }
-        }
-    }
-    return T;
+// The smallest value strictly above T's value.  For a chunk whose ids all
+// exceed T's id, an element beats T exactly when its value is above T's, so
+// the float compare with this is exact there.
+__device__ __forceinline__ float strict_value(uint64_t T) {
+    const uint32_t hi = uint32_t(T >> 32);
+    return hi >= 0x007FFFFFu ? key_value(uint64_t(hi + 1u) << 32) : -INFINITY;
 }
 
 __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
@@ -299,6 +270,18 @@ __device__ __forceinline__ uint64_t bound_from_lane_values(float v) {
     if (cnt < uint32_t(kSlots)) return 0ull;
     const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
     return k > 0 ? k - 1 : 0ull;
+}
+
+// Inserts the wave-uniform key k into the sorted list in lanes 0..6: lane i
+// takes k if k lands at position i, its upper neighbour's key if k lands
+// above it (a one-lane DPP shift), else keeps its own.  Lanes 7..63 stay 0.
+__device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t k, int lane) {
+    constexpr int kDppShr1 = 0x111;  // row_shr:1, lane 0 of a row gets `old`
+    const uint32_t ph = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list >> 32)), kDppShr1, 0xF, 0xF, false));
+    const uint32_t pl = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list)), kDppShr1, 0xF, 0xF, false));
+    const uint64_t above = lane == 0 ? ~0ull : ((uint64_t(ph) << 32) | pl);
+    const uint64_t next = k > list ? (k > above ? above : k) : list;
+    return lane < kSlots ? next : 0ull;
 }
 
 // ------------------------------------------------------------------ row kernel
@@ -329,12 +312,13 @@ __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint6
     }
 }
 
-// The whole descriptor of a workgroup's row in one 16-byte scalar load (not
-// one dependent load per field as they are first used).
+// The whole descriptor of a workgroup's row in one 16-byte load, its fields
+// made wave-uniform.
 __device__ __forceinline__ RowDesc load_desc_uniform(const RowDesc *desc, uint32_t o) {
-    uint4 v = *reinterpret_cast<const uint4 *>(desc + o);
-    asm volatile("" : "+s"(v.x), "+s"(v.y), "+s"(v.z));
-    return RowDesc{v.x, v.y, v.z, v.w};
+    const uint4 v = *reinterpret_cast<const uint4 *>(desc + o);
+    return RowDesc{uint32_t(__builtin_amdgcn_readfirstlane(int(v.x))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.y))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))), 0u};
 }
 
 __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, uint64_t o, int lane) {
@@ -344,11 +328,16 @@ __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, u
     }
 }
 
-template <int kWaves, int kDepth>
+// kDirect: output row o reads logits row o and no row is padding-only, so
+// the row's address does not wait for its descriptor (whose chosen token and
+// top_n are needed only at the end).
+template <int kWaves, int kDepth, bool kDirect>
 __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
-    __shared__ uint64_t s_top[kSlots];
-    __shared__ float s_lmax[kWaves * kWave];
+    static_assert(kThreads >= kChunkF4, "one thread per float4 of the partial chunk");
+    __shared__ float s_lmax[kThreads];
+    __shared__ uint64_t s_keys[kWaves * kSlots];
+    __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
 
@@ -359,44 +348,38 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t seg = blockIdx.x - o * a.split;
     const RowDesc d = load_desc_uniform(a.desc, o);
 
-    if (d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
+    if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
         if (a.split == 1 && wave == 0) write_padding(a.out_lp, a.out_id, o, lane);
         return;
     }
 
     const uint32_t V = a.vocab;
-    const float *row = a.src + uint64_t(d.src_row) * V;
+    const float *row = a.src + uint64_t(kDirect ? o : d.src_row) * V;
     const uint64_t seg_start = uint64_t(seg) * a.seg_len;
     const uint32_t v0 = seg_start < V ? uint32_t(seg_start) : V;
     const uint32_t v1 = (uint64_t(v0) + a.seg_len < V) ? v0 + a.seg_len : V;
 
-    float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^(x - m)
-    float x_chosen;
-    // wave-uniform filter state: seed bound, T = max(seed, slot 6), T's value
-    uint64_t seed = 0, T = 0;
-    float tv = -INFINITY;
-    auto refresh = [&]() __attribute__((always_inline)) {
-        T = umax64(seed, uniform64(lds_load_relaxed(&s_top[kSlots - 1])));
-        tv = threshold_value(T);
-    };
-
-    // aligned body: float4 loads from a 16-byte aligned element a0
-    uint32_t a0 = v0;
-    {
-        const uint32_t mis = uint32_t((reinterpret_cast<uintptr_t>(row + v0) >> 2) & 3u);
-        a0 = v0 + ((4u - mis) & 3u);
-        if (a0 > v1) a0 = v1;
-    }
+    // [v0, a0): < 4 elements before the first 16-byte boundary; [a0, a0 + 4 nf4):
+    // float4s, nchunks full chunks of 1024 elements then a partial chunk;
+    // then < 4 trailing elements
+    uint32_t nh = (4u - uint32_t((reinterpret_cast<uintptr_t>(row + v0) >> 2) & 3u)) & 3u;
+    if (nh > v1 - v0) nh = v1 - v0;
+    const uint32_t a0 = v0 + nh;
     const uint32_t nf4 = (v1 - a0) >> 2;
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
+    const uint32_t ntr = (v1 - a0) & 3u;
 
-    // The body's full chunks are read through a buffer resource whose range
-    // ends after the last of them: a load of a chunk past the end returns
-    // zeros without touching memory.  So every refill is unconditional, no
-    // buffer value ever merges two paths, and the compiler keeps each buffer
-    // in place instead of copying buffers at the loop's back edge (a copy
-    // would first wait for every load in flight).
-    const StreamRange body = make_stream_range(row + a0, nchunks * uint32_t(kChunkF4 * 16));
+    float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^(x - m)
+    uint64_t list = 0;              // lane i < 7: the wave's (i+1)-th best key so far
+    uint64_t T = 0;                 // wave-uniform bound (see above)
+
+    // All float4s of the segment are read through one buffer resource whose
+    // range ends at the last of them: a load past the end returns zeros
+    // without touching memory.  So refills are unconditional, no buffer value
+    // ever merges two paths, and the compiler keeps each buffer in place
+    // instead of copying buffers at the loop's back edge (a copy would first
+    // wait for every load in flight).
+    const StreamRange body = make_stream_range(row + a0, nf4 * 16u);
     auto load_chunk = [&](f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
         const uint32_t off = ch * uint32_t(kChunkF4 * 16) + uint32_t(lane) * 16u;
 #pragma unroll
@@ -426,25 +409,42 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
             acc[u] = fast_exp2((x[u].x - ms) * kLog2e) + fast_exp2((x[u].y - ms) * kLog2e) +
                      (fast_exp2((x[u].z - ms) * kLog2e) + fast_exp2((x[u].w - ms) * kLog2e));
         }
-        float csum = acc[0];
-#pragma unroll
-        for (int u = 1; u < kU; ++u) csum += acc[u];
+        const float csum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         s = s * fast_exp2((m - ms) * kLog2e) + csum;
         m = mn;
         return cm;
     };
 
-    // Top-k part for one chunk whose lane maxima are cm, against the bound
-    // as of this chunk.  A float compare of the lane maxima with T's value
-    // passes almost every chunk by; then the order key of (lane max, the
-    // lane's first id), which no key of the lane's chunk exceeds; then one
-    // float compare per column, and the columns with candidates cascade.
+    // One column: a value and an id per lane, lanes passing tv_l tested
+    // further (a lane that must not take part passes tv_l = +inf).  Keys above
+    // T go into the list one at a time in lane order; T rises as it fills.
+    auto column = [&](float v, uint32_t id, float tv_l) __attribute__((always_inline)) {
+        const bool pass = v >= tv_l;
+        if (__ballot(pass) == 0) return;
+        const uint64_t key = order_key(v, id);
+        uint64_t mask = __ballot(pass && key > T);
+        while (mask != 0) {
+            const int l = __builtin_ctzll(mask);
+            list = list_insert(list, readlane_u64(key, l), lane);
+            T = umax64(T, readlane_u64(list, kSlots - 1));
+            mask = __ballot(pass && key > T) & ~((2ull << l) - 1ull);
+        }
+    };
+
+    // The filter value for chunk ch against the bound as it stands.
+    auto chunk_tv = [&](uint32_t ch) __attribute__((always_inline)) {
+        const uint32_t first = a0 + ch * uint32_t(kChunkF4 * 4);
+        return key_id(T) < first ? strict_value(T) : threshold_value(T);
+    };
+
+    // Top-k part for one chunk whose lane maxima are cm: a ballot of the lane
+    // maxima against tv passes most chunks by; else one ballot per float4
+    // group and per column finds the columns holding candidates, which then
+    // go through a single copy of the column code (uniform register indexing).
     auto topk_chunk = [&](const f32x4 (&x)[kU], uint32_t ch, float cm) __attribute__((always_inline)) {
+        const float tv = chunk_tv(ch);
         if (__ballot(cm >= tv) == 0) return;
-        const uint32_t first_id = a0 + 4u * (ch * uint32_t(kChunkF4) + uint32_t(lane));
-        if (__ballot(order_key(cm, first_id) > T) == 0) return;
-        // columns (u, q) holding a candidate, then one column at a time
-        // through a single copy of the entry code (uniform register indexing)
+        const uint64_t T0 = T;
         static_assert(kU == 4, "16 columns per chunk");
         uint32_t cols = 0;
 #pragma unroll
@@ -458,54 +458,53 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         const f32x16 xv = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        const uint32_t lane_id = a0 + ch * uint32_t(kChunkF4 * 4) + 4u * uint32_t(lane);
         while (cols != 0) {
             const uint32_t j = uint32_t(__builtin_ctz(cols));
             cols &= cols - 1;
-            const uint32_t id = first_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u);
-            T = enter_keys(s_top, order_key(xv[j], id), T, lane);
+            column(xv[j], lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u), tv);
         }
-        tv = threshold_value(T);
+        if (T != T0 && lane == 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
-    // The bound is re-read from LDS for every chunk, the read issued before
-    // the chunk's arithmetic so that its latency hides there.
-    auto process_chunk = [&](const f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
-        const uint64_t s6 = lds_load_relaxed(&s_top[kSlots - 1]);
-        const float cm = lse_chunk(x);
-        T = umax64(seed, uniform64(s6));
-        tv = threshold_value(T);
-        topk_chunk(x, ch, cm);
-    };
-
-    // kDepth chunks in flight per wave (register buffers used in rotation).
-    // After the first chunk every wave publishes its lanes' chunk maxima; past
-    // one barrier each wave takes, per lane position, the max over the waves
-    // and seeds the threshold from the 7th largest of those 64 values, so all
-    // waves start from the same bound for the whole workgroup's first chunks.
-    {
-        f32x4 xb[kDepth][kU];
-        uint32_t ch = uint32_t(wave);
+    f32x4 xb[kDepth][kU];
+    uint32_t ch = uint32_t(wave);
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-            refill(xb[d], ch + uint32_t(d * kWaves));
-        // the chosen token's logit, fetched now so that its latency hides under
-        // the stream instead of trailing the final merge (a per-lane index keeps
-        // it a vector load that nothing waits on before its use)
-        x_chosen = row[(a.split == 1 && lane == kSlots) ? d.chosen : 0u];
-        if (tid < kSlots) s_top[tid] = 0;
-        if (tid == 0) s_done = 0;
+    for (int dd = 0; dd < kDepth; ++dd) refill(xb[dd], ch + uint32_t(dd * kWaves));
+    // The partial chunk (one float4 per thread), the head and trailing
+    // elements (one per thread) and the chosen token's logit are loaded now,
+    // so that their latency hides under the stream.
+    const uint32_t rest4 = nchunks * uint32_t(kChunkF4) + uint32_t(tid);
+    const bool rest4_ok = rest4 < nf4;
+    const f32x4 xr4 = stream_load(body, rest4 * 16u);
+    const bool e1_ok = uint32_t(tid) < nh + ntr;
+    const uint32_t e1 = uint32_t(tid) < nh ? v0 + uint32_t(tid) : a0 + 4u * nf4 + (uint32_t(tid) - nh);
+    const float xr1 = row[e1_ok ? e1 : 0u];
+    const float x_chosen = row[(a.split == 1 && lane == kSlots) ? d.chosen : 0u];
+    // LDS set-up (before any data can have arrived, so the barrier costs only
+    // the spread of the waves' start)
+    s_lmax[tid] = -INFINITY;
+    if (tid == 0) {
+        s_T = 0;
+        s_done = 0;
+    }
+    __syncthreads();
+
+    {
+        // First chunk: the wave publishes its lanes' chunk maxima and seeds T
+        // from, per lane position, the max over the maxima the waves have
+        // published so far (its own at least); ones not yet written read
+        // -inf.  These are distinct elements of the row, so the 7th largest
+        // of the 64 values bounds it.
         float cm0 = -INFINITY;
         if (ch < nchunks) cm0 = lse_chunk(xb[0]);
         s_lmax[wave * kWave + lane] = cm0;
-        __syncthreads();
-        {
-            float cmx = s_lmax[lane];
+        float cmx = cm0;
 #pragma unroll
-            for (int i = 1; i < kWaves; ++i) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
-            seed = bound_from_lane_values(cmx);
-            T = seed;
-            tv = threshold_value(T);
-        }
+        for (int i = 0; i < kWaves; ++i)
+            if (i != wave) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
+        T = bound_from_lane_values(cmx);
+        if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
         constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
         refill(xb[0], ch + kAhead);
@@ -516,42 +515,54 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         // refill reads nothing.  The loop has one exit, at its bottom, and no
         // buffer is read after it: an exit from the middle, or a use after
         // the loop, would add paths on which buffers are copied between
-        // registers or every wait for loads in flight must be stricter.
+        // registers or every wait for loads in flight must be stricter.  The
+        // shared bound is read before each chunk's arithmetic, so that its
+        // latency hides there.
         const uint32_t mine = nchunks > uint32_t(wave) ? (nchunks - uint32_t(wave) + kWaves - 1) / kWaves : 0u;
         const uint32_t rounds = mine > 1 ? (mine - 1 + kDepth - 1) / uint32_t(kDepth) : 0u;
         for (uint32_t r = 0; r < rounds; ++r) {
 #pragma unroll
-            for (int d = 1; d <= kDepth; ++d) {
-                if (ch < nchunks) process_chunk(xb[d % kDepth], ch);
-                refill(xb[d % kDepth], ch + kAhead);
+            for (int dd = 1; dd <= kDepth; ++dd) {
+                if (ch < nchunks) {
+                    const uint64_t shared = lds_load_relaxed(&s_T);
+                    const float cm = lse_chunk(xb[dd % kDepth]);
+                    T = umax64(T, uniform64(shared));
+                    topk_chunk(xb[dd % kDepth], ch, cm);
+                }
+                refill(xb[dd % kDepth], ch + kAhead);
                 ch += kWaves;
             }
         }
     }
 
-    // head (before a0) and tail (after the last full chunk): one element per
-    // thread per pass
+    // the partial chunk and the single elements, from the registers they
+    // were loaded into at the start
     {
-        refresh();
-        const uint32_t nh = a0 - v0;
-        const uint32_t tail0 = a0 + nchunks * uint32_t(kChunkF4) * 4u;
-        const uint32_t nrest = nh + (v1 - tail0);
-        for (uint32_t base = 0; base < nrest; base += kThreads) {
-            const uint32_t r = base + uint32_t(tid);
-            const bool valid = r < nrest;
-            const uint32_t e = (r < nh) ? v0 + r : tail0 + (r - nh);
-            float x = -INFINITY;
-            if (valid) x = row[e];
-            const float mn = fmaxf(m, x);
-            const float ms = (mn == -INFINITY) ? 0.0f : mn;
-            s = s * fast_exp2((m - ms) * kLog2e) + fast_exp2((x - ms) * kLog2e);
-            m = mn;
-            T = enter_keys(s_top, valid ? order_key(x, e) : 0ull, T, lane);
+        const f32x4 x4 = rest4_ok ? xr4 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        const float x1 = e1_ok ? xr1 : -INFINITY;
+        const float cm = fmaxf(fmaxf(fmaxf(x4.x, x4.y), fmaxf(x4.z, x4.w)), x1);
+        const float mn = fmaxf(m, cm);
+        const float ms = (mn == -INFINITY) ? 0.0f : mn;
+        const float add = (fast_exp2((x4.x - ms) * kLog2e) + fast_exp2((x4.y - ms) * kLog2e)) +
+                          (fast_exp2((x4.z - ms) * kLog2e) + fast_exp2((x4.w - ms) * kLog2e)) +
+                          fast_exp2((x1 - ms) * kLog2e);
+        s = s * fast_exp2((m - ms) * kLog2e) + add;
+        m = mn;
+        T = umax64(T, uniform64(lds_load_relaxed(&s_T)));
+        const float tv = threshold_value(T);
+        if (__ballot(cm >= tv) != 0) {
+            const uint32_t id4 = a0 + 4u * rest4;
+            const float tv4 = rest4_ok ? tv : INFINITY;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) column(f4_get(x4, q), id4 + uint32_t(q), tv4);
+            column(x1, e1, e1_ok ? tv : INFINITY);
         }
     }
 
-    // per wave: (m, s) across lanes into LDS; the last wave of the workgroup
-    // to get here merges them and writes the row (or the segment's record)
+    // per wave: its list and (m, s) across lanes into LDS; the last wave of
+    // the workgroup to get here merges them and writes the row (or the
+    // segment's record)
+    if (lane < kSlots) s_keys[wave * kSlots + lane] = list;
     wave_lse(m, s);
     if (lane == 0) {
         s_m[wave] = m;
@@ -561,7 +572,15 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
     lds_acquire();
 
-    const uint64_t mine = lane < kSlots ? lds_load_relaxed(&s_top[lane < kSlots ? lane : 0]) : 0ull;
+    constexpr int kPer = (kWaves * kSlots + kWave - 1) / kWave;
+    uint64_t e[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t idx = uint32_t(lane + kWave * i);
+        e[i] = idx < uint32_t(kWaves * kSlots) ? s_keys[idx] : 0ull;
+    }
+    uint32_t found;
+    const uint64_t top = wave_select7<kPer>(e, lane, &found);
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {
         M = s_m[lane];
@@ -570,14 +589,14 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     wave_lse(M, S);
 
     if (a.split == 1) {
-        write_row(a.out_lp, a.out_id, o, lane, mine, d.top_n, M + logf(S), x_chosen, d.chosen);
+        write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, M + logf(S), x_chosen, d.chosen);
     } else {
         PartialRec *rec = a.partials + uint64_t(o) * a.split + seg;
         if (lane == 0) {
             rec->m = M;
             rec->s = S;
         }
-        if (lane < kSlots) rec->keys[lane] = mine;
+        if (lane < kSlots) rec->keys[lane] = top;
     }
 }
 
@@ -677,6 +696,26 @@ void release_staging(lp_plan &p) {
     p.staging_pending = false;
 }
 
+template <int kWaves, int kDepth>
+static void launch_shape(bool direct, dim3 grid, hipStream_t s, const dev::RowArgs &ra) {
+    if (direct) hipLaunchKernelGGL((dev::row_kernel<kWaves, kDepth, true>), grid, dim3(kWaves * 64), 0, s, ra);
+    else hipLaunchKernelGGL((dev::row_kernel<kWaves, kDepth, false>), grid, dim3(kWaves * 64), 0, s, ra);
+}
+
+static void launch_row_kernel(uint32_t waves, bool deep, bool direct, dim3 grid, hipStream_t s,
+                              const dev::RowArgs &ra) {
+    if (waves == 16) {
+        if (deep) launch_shape<16, 2>(direct, grid, s, ra);
+        else launch_shape<16, 1>(direct, grid, s, ra);
+    } else if (waves == 8) {
+        if (deep) launch_shape<8, 2>(direct, grid, s, ra);
+        else launch_shape<8, 1>(direct, grid, s, ra);
+    } else {
+        if (deep) launch_shape<4, 2>(direct, grid, s, ra);
+        else launch_shape<4, 1>(direct, grid, s, ra);
+    }
+}
+
 static lp_status check_workspace(const lp_plan *plan, const void *ws, uint64_t ws_bytes) {
     if (ws == nullptr || ws_bytes < plan->workspace_bytes) return LP_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return LP_ERR_WORKSPACE;
@@ -747,17 +786,7 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ra.partials = partials;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<uint32_t>(blocks));
-    const bool deep = plan->depth == 4;
-    if (waves == 16) {
-        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<16, 4>), grid, dim3(16 * 64), 0, s, ra);
-        else hipLaunchKernelGGL((lp::dev::row_kernel<16, 2>), grid, dim3(16 * 64), 0, s, ra);
-    } else if (waves == 8) {
-        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<8, 4>), grid, dim3(8 * 64), 0, s, ra);
-        else hipLaunchKernelGGL((lp::dev::row_kernel<8, 2>), grid, dim3(8 * 64), 0, s, ra);
-    } else {
-        if (deep) hipLaunchKernelGGL((lp::dev::row_kernel<4, 4>), grid, dim3(4 * 64), 0, s, ra);
-        else hipLaunchKernelGGL((lp::dev::row_kernel<4, 2>), grid, dim3(4 * 64), 0, s, ra);
-    }
+    lp::launch_row_kernel(plan->waves, plan->depth == 2, plan->direct_rows != 0, grid, s, ra);
     LP_HIP_TRY(hipGetLastError());
     if (plan->split > 1) {
         lp::dev::MergeArgs ma;

@@ -15,9 +15,10 @@ constexpr uint32_t kCols = 1u << kLevels;     // 8 output columns
 constexpr uint32_t kTopSlots = kCols - 1;     // 7 ranked slots + 1 chosen slot
 constexpr uint32_t kPadId = 0xFFFFFFFFu;
 constexpr uint32_t kMaxSplit = 64;
-// Longest vocabulary segment one workgroup streams: its byte range must fit
-// the 31-bit range of the buffer resource the row kernel reads it through.
-constexpr uint32_t kMaxSegment = 1u << 29;
+// Longest vocabulary segment one workgroup streams: its byte range (at most
+// 1 GiB) must fit the 32-bit range and offsets of the buffer resource the row
+// kernel reads it through.
+constexpr uint32_t kMaxSegment = 1u << 28;
 
 // Elements per segment when a row of `vocab` is cut into `split` segments
 // (a multiple of 4, so every segment but the first starts 16-byte aligned
@@ -64,7 +65,8 @@ struct lp_plan {
     uint64_t read_rows = 0;
     uint32_t split = 1;
     uint32_t waves = 4;              // waves per workgroup: 4, 8 or 16
-    uint32_t depth = 2;              // chunks in flight per wave: 2 or 4
+    uint32_t depth = 2;              // chunks in flight per wave: 1 or 2
+    uint32_t direct_rows = 0;        // 1: output row o reads logits row o (all top_n > 0)
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 64 when split > 1
     uint64_t workspace_bytes = 0;

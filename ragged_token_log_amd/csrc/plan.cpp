@@ -27,14 +27,17 @@ void size_workspace(lp_plan &p) {
     p.workspace_bytes = p.desc_bytes + p.partial_bytes;
 }
 
-// Kernel shape: waves per workgroup and vocabulary segments per row.  Rows
-// are independent, so a launch with many rows runs one workgroup of 4 waves
-// per row.  Fewer rows get more waves per row, so each row is streamed by
-// more loads in flight; too few rows to occupy 256 CUs even then are split
+// Kernel shape: waves per workgroup, chunks in flight per wave and
+// vocabulary segments per row.  Rows are independent, so a launch with many
+// rows runs one workgroup of 4 waves per row, two chunks in flight per wave.
+// A few hundred rows (two or three workgroups per CU) run 8 waves with one
+// chunk in flight each: their whole batch is in flight at once, and fewer
+// bytes queued per wave shorten the last rows' wait.  Fewer rows than CUs
+// get more waves per row; too few to occupy 256 CUs even then are split
 // into segments (one workgroup each, at least kMinSegment elements), whose
 // partial results a second kernel merges.
 static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
-                           uint32_t *split) {
+                           uint32_t *depth, uint32_t *split) {
     constexpr uint64_t kManyRows = 1024;
     constexpr uint64_t kSomeRows = 384;
     constexpr uint64_t kCUs = 256;
@@ -43,16 +46,21 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
     uint32_t min_split = 1;
     while (segment_length(vocab, min_split) > kMaxSegment) ++min_split;
     *split = min_split;
+    *depth = 2;
     if (read_rows >= kManyRows || read_rows == 0) {
         *waves = 4;
         return;
     }
     if (read_rows >= kSomeRows) {
         *waves = 8;
+        *depth = 1;
+        return;
+    }
+    if (read_rows >= kCUs) {
+        *waves = 8;
         return;
     }
     *waves = 16;
-    if (read_rows >= kCUs) return;
     uint64_t s = (kCUs + read_rows - 1) / read_rows;
     uint64_t by_vocab = vocab / kMinSegment;
     if (by_vocab < 1) by_vocab = 1;
@@ -157,11 +165,18 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         }
         p->out_rows = acc;
         p->read_rows = read;
+        // Output row o reads logits row o when every request is read (top_n >
+        // 0) and either none has full logits (request n reads next-token row
+        // n) or every request echoes (its output rows are its token rows).
+        bool direct = read == acc;
+        if (has_logits)
+            for (uint32_t n = 0; n < batch && direct; ++n) direct = p->echo[n] != 0;
+        p->direct_rows = direct ? 1u : 0u;
     } catch (...) {
         delete p;
         return LP_ERR_NOMEM;
     }
-    lp::choose_variant(p->read_rows, vocab, &p->waves, &p->split);
+    lp::choose_variant(p->read_rows, vocab, &p->waves, &p->depth, &p->split);
     lp::size_workspace(*p);
 
     if (output_row_offsets != nullptr)
@@ -185,6 +200,8 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
     info->depth = plan->depth;
     info->has_logits = plan->has_logits;
     info->workspace_bytes = plan->workspace_bytes;
+    info->direct_rows = plan->direct_rows;
+    info->reserved = 0;
     return LP_OK;
 }
 
@@ -206,7 +223,7 @@ lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves) {
 
 lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
-    if (depth != 2 && depth != 4) return LP_ERR_UNSUPPORTED;
+    if (depth != 1 && depth != 2) return LP_ERR_UNSUPPORTED;
     plan->depth = depth;
     return LP_OK;
 }

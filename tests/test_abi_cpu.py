@@ -67,6 +67,33 @@ def test_plan_matches_oracle(seed):
     assert info["columns"] == 8 and info["levels"] == 3
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_direct_rows_flag(seed):
+    """The plan marks a batch direct exactly when output row o reads logits
+    row o for every o and no request has top_n == 0 (then the kernel takes
+    the row from its own index instead of the descriptor)."""
+    rng = np.random.default_rng(100 + seed)
+    has_logits = seed % 4 != 0
+    batch = int(rng.integers(1, 10))
+    off, echo, top_n, tokens, sampled = _random_batch(rng, batch, 40, has_logits,
+                                                      p_echo=(1.0, 0.5, 0.0)[seed % 3])
+    if seed % 2:
+        top_n = np.maximum(top_n, 1)
+    plan = R.Plan(off, echo, top_n, 40, has_logits)
+    tasks = LO.row_tasks(off, echo, top_n, tokens, sampled, has_logits)
+    want = all(t.src_row == o and t.top_n > 0 for o, t in enumerate(tasks))
+    assert plan.info()["direct_rows"] == int(want)
+
+
+def test_direct_rows_on_named_workloads():
+    expect = {"no_echo_next_token": 1, "ragged_echo_mix": 0, "decode_peaked": 1,
+              "prefill_echo_large": 1, "tie_edge_stress": 1}
+    for name, make in gen.WORKLOADS.items():
+        c = make()
+        plan = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, c.has_logits)
+        assert plan.info()["direct_rows"] == expect[name], name
+
+
 def test_plan_on_named_workloads():
     for name, make in gen.WORKLOADS.items():
         c = make()
@@ -95,10 +122,10 @@ def test_split_and_workspace():
     assert plan.info()["waves"] == 8
     plan.set_waves(16)
     assert plan.info()["waves"] == 16
-    plan.set_depth(4)
-    assert plan.info()["depth"] == 4
+    plan.set_depth(1)
+    assert plan.info()["depth"] == 1
     with pytest.raises(R.LogprobError):
-        plan.set_depth(3)
+        plan.set_depth(4)
     with pytest.raises(R.LogprobError) as e:
         plan.set_waves(6)
     assert e.value.name == "LP_ERR_UNSUPPORTED"
@@ -108,19 +135,19 @@ def test_split_and_workspace():
 
 
 def test_segments_stay_within_the_streamed_range():
-    # one workgroup streams at most 2^29 elements of a row: a wider row is
+    # one workgroup streams at most 2^28 elements of a row: a wider row is
     # always cut into segments, and a split leaving longer segments is refused
     many = 3000
     wide = R.Plan(np.arange(many + 1, dtype=np.uint32), np.zeros(many, bool), np.full(many, 1),
                   (1 << 31) + 1, False)
-    assert wide.split == 5
-    assert wide.workspace_bytes == ((many * 16 + 255) // 256) * 256 + many * 5 * 64
+    assert wide.split == 9
+    assert wide.workspace_bytes == ((many * 16 + 255) // 256) * 256 + many * 9 * 64
     with pytest.raises(R.LogprobError) as e:
-        wide.set_split(4)
+        wide.set_split(8)
     assert e.value.name == "LP_ERR_UNSUPPORTED"
     edge = R.Plan(np.arange(many + 1, dtype=np.uint32), np.zeros(many, bool), np.full(many, 1),
                   1 << 31, False)
-    assert edge.split == 4
+    assert edge.split == 8
     edge.set_split(64)
     assert edge.split == 64
 

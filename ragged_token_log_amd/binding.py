@@ -30,8 +30,9 @@ EXPORTED = (
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
 
-LEVELS = 3
-COLUMNS = 8
+LEVELS = 3          # default heap depth: 8 columns, top_n <= 7
+MAX_LEVELS = 6      # 64 columns
+COLUMNS = 8         # columns at the default levels
 MAX_TOP_N = 7
 PAD_ID = 0xFFFFFFFF
 
@@ -152,10 +153,12 @@ class Plan:
                                   ctypes.byref(rows), ctypes.byref(ws)), "lp_plan_ragged")
         self.batch = batch
         self.vocab = int(vocab)
+        self.levels = int(levels)
         self.has_logits = bool(has_logits)
         self.out_off = out_off
         self.out_rows = int(rows.value)
         self.input_row_offsets = off
+        self.columns = int(self.info()["columns"])
 
     # ---------------------------------------------------------------- facts
     def info(self) -> dict:
@@ -275,8 +278,8 @@ def _check_logits(t, rows, vocab, name, torch):
 
 
 def alloc_outputs(plan: Plan, device, torch):
-    lp = torch.empty((plan.out_rows, COLUMNS), dtype=torch.float32, device=device)
-    ids = torch.empty((plan.out_rows, COLUMNS), dtype=torch.uint32, device=device)
+    lp = torch.empty((plan.out_rows, plan.columns), dtype=torch.float32, device=device)
+    ids = torch.empty((plan.out_rows, plan.columns), dtype=torch.uint32, device=device)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
     return lp, ids, ws
 
@@ -284,7 +287,8 @@ def alloc_outputs(plan: Plan, device, torch):
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens,
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
-                                     depth: int | None = None, stream=None):
+                                     depth: int | None = None, stream=None,
+                                     levels: int = LEVELS):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -294,7 +298,11 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     ``input_row_offsets``, ``tokens``, ``sampled_tokens``, ``batch_top_n`` and
     ``batch_echo`` are host sequences.
 
-    Returns ``(logprobs (R, 8) float32, token_ids (R, 8) uint32,
+    ``levels`` is the heap depth of the MAX page's graph (section
+    "log_probabilities_ragged_graph"): C = 2**levels output columns (one at
+    levels 0), top_n <= C - 1.
+
+    Returns ``(logprobs (R, C) float32, token_ids (R, C) uint32,
     output_row_offsets (batch+1,) uint32 numpy)``, the tensors on the GPU.
     """
     import torch
@@ -310,7 +318,7 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
         if logits.device != next_token_logits.device:
             raise LogprobError(3, "logits and next_token_logits on different devices")
     plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
-                None if logits is None else int(logits.shape[0]))
+                None if logits is None else int(logits.shape[0]), levels=levels)
     try:
         if split is not None:
             plan.set_split(split)

@@ -46,7 +46,6 @@ namespace dev {
 constexpr int kWave = 64;
 constexpr int kU = 4;                // float4 loads per lane per chunk
 constexpr int kChunkF4 = kWave * kU; // float4 per wave-chunk (1024 elements)
-constexpr int kSlots = int(kTopSlots);
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ order keys
@@ -107,6 +106,15 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     v = fmaxf(v, dpp_f32<kDppMirror>(v));
     return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
                  fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+__device__ __forceinline__ float wave_min_f32(float v) {
+    v = fminf(v, dpp_f32<kDppXor1>(v));
+    v = fminf(v, dpp_f32<kDppXor2>(v));
+    v = fminf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fminf(v, dpp_f32<kDppMirror>(v));
+    return fminf(fminf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fminf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -196,16 +204,17 @@ __device__ __forceinline__ void wave_lse(float &m, float &s) {
     s = S;
 }
 
-// Best 7 keys of up to kPer*64 keys held kPer per lane (0 = empty).  Returns,
-// in lane r < 7, the r-th best key (0 if fewer exist); *count gets how many
-// were found.  Each round finds the largest high word across the wave, then
-// the largest low word among keys with that high word (keys are unique).
-template <int kPer>
-__device__ __forceinline__ uint64_t wave_select7(uint64_t (&e)[kPer], int lane, uint32_t *count) {
+// Best kK keys of up to kPer*64 keys held kPer per lane (0 = empty).
+// Returns, in lane r < kK, the r-th best key (0 if fewer exist); *count gets
+// how many were found.  Each round finds the largest high word across the
+// wave, then the largest low word among keys with that high word (keys are
+// unique).
+template <int kK, int kPer>
+__device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, uint32_t *count) {
     uint64_t mine = 0;
     uint32_t found = 0;
 #pragma unroll 1
-    for (int r = 0; r < kSlots; ++r) {
+    for (int r = 0; r < kK; ++r) {
         uint64_t b = e[0];
 #pragma unroll
         for (int i = 1; i < kPer; ++i) b = umax64(b, e[i]);
@@ -252,36 +261,61 @@ __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// A bound from one real element per lane (or -inf for none): if 7 lanes hold
-// values >= t (counting lanes that tie), no element below t can be in the
-// top 7, so the bound may be just under the smallest key of value t.  A -inf
-// t excludes nothing.
+// A bound from one real element per lane (or -inf for none): if kK lanes
+// hold values >= t (counting lanes that tie), no element below t can be in
+// the top kK, so the bound may be just under the smallest key of value t.
+// t is the kK-th largest of the 64 lane values, found by rounds of wave max
+// (or, for kK > 32, as the (65 - kK)-th smallest by rounds of wave min).  A
+// -inf t excludes nothing.
+template <int kK>
 __device__ __forceinline__ uint64_t bound_from_lane_values(float v) {
     float t = -INFINITY;
     uint32_t cnt = 0;
+    if constexpr (kK <= 32) {
 #pragma unroll 1
-    for (int r = 0; r < kSlots; ++r) {
-        const float mx = wave_max_f32(v);
-        cnt += uint32_t(__popcll(__ballot(v == mx)));
-        t = mx;
-        if (cnt >= uint32_t(kSlots)) break;
-        v = (v == mx) ? -INFINITY : v;
+        for (int r = 0; r < kK; ++r) {
+            const float mx = wave_max_f32(v);
+            cnt += uint32_t(__popcll(__ballot(v == mx)));
+            t = mx;
+            if (cnt >= uint32_t(kK)) break;
+            v = (v == mx) ? -INFINITY : v;
+        }
+        if (cnt < uint32_t(kK)) return 0ull;
+    } else {
+        constexpr uint32_t kNeed = uint32_t(kWave + 1 - kK);
+#pragma unroll 1
+        for (uint32_t r = 0; r < kNeed; ++r) {
+            const float mn = wave_min_f32(v);
+            cnt += uint32_t(__popcll(__ballot(v == mn)));
+            t = mn;
+            if (cnt >= kNeed) break;
+            v = (v == mn) ? INFINITY : v;
+        }
     }
-    if (cnt < uint32_t(kSlots)) return 0ull;
     const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
     return k > 0 ? k - 1 : 0ull;
 }
 
-// Inserts the wave-uniform key k into the sorted list in lanes 0..6: lane i
-// takes k if k lands at position i, its upper neighbour's key if k lands
-// above it (a one-lane DPP shift), else keeps its own.  Lanes 7..63 stay 0.
+// Inserts the wave-uniform key k into the sorted list in lanes 0..kK-1: lane
+// i takes k if k lands at position i, its upper neighbour's key if k lands
+// above it (a one-lane shift), else keeps its own.  Other lanes stay 0.
+template <int kK>
 __device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t k, int lane) {
-    constexpr int kDppShr1 = 0x111;  // row_shr:1, lane 0 of a row gets `old`
-    const uint32_t ph = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list >> 32)), kDppShr1, 0xF, 0xF, false));
-    const uint32_t pl = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list)), kDppShr1, 0xF, 0xF, false));
+    uint32_t ph, pl;
+    if constexpr (kK <= 16) {
+        // the list lies within the first row of 16 lanes: DPP row_shr:1
+        constexpr int kDppShr1 = 0x111;
+        ph = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list >> 32)), kDppShr1, 0xF, 0xF, false));
+        pl = uint32_t(__builtin_amdgcn_update_dpp(-1, int(uint32_t(list)), kDppShr1, 0xF, 0xF, false));
+    } else {
+        // across rows: a permute from lane - 1
+        const int src = (lane > 0 ? lane - 1 : 0) * 4;
+        ph = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(uint32_t(list >> 32))));
+        pl = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(uint32_t(list))));
+    }
     const uint64_t above = lane == 0 ? ~0ull : ((uint64_t(ph) << 32) | pl);
     const uint64_t next = k > list ? (k > above ? above : k) : list;
-    return lane < kSlots ? next : 0ull;
+    return lane < kK ? next : 0ull;
 }
 
 // ------------------------------------------------------------------ row kernel
@@ -295,20 +329,23 @@ struct RowArgs {
     const RowDesc *desc;
     float *out_lp;             // split == 1: (R, 8)
     uint32_t *out_id;          // split == 1: (R, 8)
-    PartialRec *partials;      // split > 1: (R, split)
+    uint64_t *partials;        // split > 1: (R, split) records of slots + 1 words
 };
 
+// One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK
+// the chosen token.
+template <int kK>
 __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint64_t o, int lane,
                                           uint64_t key, uint32_t top_n, float lse,
                                           float x_chosen, uint32_t chosen) {
-    // lanes 0..6: ranked slots; lane 7: the chosen token
-    if (lane < kSlots) {
+    constexpr uint64_t kC = uint64_t(kK) + 1;
+    if (lane < kK) {
         const bool valid = uint32_t(lane) < top_n && key != 0;
-        out_lp[o * kCols + lane] = valid ? key_value(key) - lse : -INFINITY;
-        out_id[o * kCols + lane] = valid ? key_id(key) : kPadId;
-    } else if (lane == kSlots) {
-        out_lp[o * kCols + lane] = x_chosen - lse;
-        out_id[o * kCols + lane] = chosen;
+        out_lp[o * kC + lane] = valid ? key_value(key) - lse : -INFINITY;
+        out_id[o * kC + lane] = valid ? key_id(key) : kPadId;
+    } else if (lane == kK) {
+        out_lp[o * kC + lane] = x_chosen - lse;
+        out_id[o * kC + lane] = chosen;
     }
 }
 
@@ -321,22 +358,26 @@ __device__ __forceinline__ RowDesc load_desc_uniform(const RowDesc *desc, uint32
                    uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))), 0u};
 }
 
+template <int kK>
 __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, uint64_t o, int lane) {
-    if (lane < int(kCols)) {
-        out_lp[o * kCols + lane] = -INFINITY;
-        out_id[o * kCols + lane] = kPadId;
+    constexpr uint64_t kC = uint64_t(kK) + 1;
+    if (lane <= kK) {
+        out_lp[o * kC + lane] = -INFINITY;
+        out_id[o * kC + lane] = kPadId;
     }
 }
 
 // kDirect: output row o reads logits row o and no row is padding-only, so
 // the row's address does not wait for its descriptor (whose chosen token and
 // top_n are needed only at the end).
-template <int kWaves, int kDepth, bool kDirect>
+// kK: ranked slots per row (2^levels - 1).
+template <int kK, int kWaves, int kDepth, bool kDirect>
 __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
     static_assert(kThreads >= kChunkF4, "one thread per float4 of the partial chunk");
+    static_assert(kK >= 1 && kK < kWave, "one lane per column");
     __shared__ float s_lmax[kThreads];
-    __shared__ uint64_t s_keys[kWaves * kSlots];
+    __shared__ uint64_t s_keys[kWaves * kK];
     __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
@@ -349,7 +390,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const RowDesc d = load_desc_uniform(a.desc, o);
 
     if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
-        if (a.split == 1 && wave == 0) write_padding(a.out_lp, a.out_id, o, lane);
+        if (a.split == 1 && wave == 0) write_padding<kK>(a.out_lp, a.out_id, o, lane);
         return;
     }
 
@@ -370,7 +411,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t ntr = (v1 - a0) & 3u;
 
     float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^(x - m)
-    uint64_t list = 0;              // lane i < 7: the wave's (i+1)-th best key so far
+    uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
 
     // All float4s of the segment are read through one buffer resource whose
@@ -425,8 +466,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         uint64_t mask = __ballot(pass && key > T);
         while (mask != 0) {
             const int l = __builtin_ctzll(mask);
-            list = list_insert(list, readlane_u64(key, l), lane);
-            T = umax64(T, readlane_u64(list, kSlots - 1));
+            list = list_insert<kK>(list, readlane_u64(key, l), lane);
+            T = umax64(T, readlane_u64(list, kK - 1));
             mask = __ballot(pass && key > T) & ~((2ull << l) - 1ull);
         }
     };
@@ -480,7 +521,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const bool e1_ok = uint32_t(tid) < nh + ntr;
     const uint32_t e1 = uint32_t(tid) < nh ? v0 + uint32_t(tid) : a0 + 4u * nf4 + (uint32_t(tid) - nh);
     const float xr1 = row[e1_ok ? e1 : 0u];
-    const float x_chosen = row[(a.split == 1 && lane == kSlots) ? d.chosen : 0u];
+    const float x_chosen = row[(a.split == 1 && lane == kK) ? d.chosen : 0u];
     // LDS set-up (before any data can have arrived, so the barrier costs only
     // the spread of the waves' start)
     s_lmax[tid] = -INFINITY;
@@ -494,8 +535,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         // First chunk: the wave publishes its lanes' chunk maxima and seeds T
         // from, per lane position, the max over the maxima the waves have
         // published so far (its own at least); ones not yet written read
-        // -inf.  These are distinct elements of the row, so the 7th largest
-        // of the 64 values bounds it.
+        // -inf.  These are distinct elements of the row, so the kK-th
+        // largest of the 64 values bounds it.
         float cm0 = -INFINITY;
         if (ch < nchunks) cm0 = lse_chunk(xb[0]);
         s_lmax[wave * kWave + lane] = cm0;
@@ -503,7 +544,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < kWaves; ++i)
             if (i != wave) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
-        T = bound_from_lane_values(cmx);
+        T = bound_from_lane_values<kK>(cmx);
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
         constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
@@ -562,7 +603,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // per wave: its list and (m, s) across lanes into LDS; the last wave of
     // the workgroup to get here merges them and writes the row (or the
     // segment's record)
-    if (lane < kSlots) s_keys[wave * kSlots + lane] = list;
+    if (lane < kK) s_keys[wave * kK + lane] = list;
     wave_lse(m, s);
     if (lane == 0) {
         s_m[wave] = m;
@@ -572,15 +613,15 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
     lds_acquire();
 
-    constexpr int kPer = (kWaves * kSlots + kWave - 1) / kWave;
+    constexpr int kPer = (kWaves * kK + kWave - 1) / kWave;
     uint64_t e[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < uint32_t(kWaves * kSlots) ? s_keys[idx] : 0ull;
+        e[i] = idx < uint32_t(kWaves * kK) ? s_keys[idx] : 0ull;
     }
     uint32_t found;
-    const uint64_t top = wave_select7<kPer>(e, lane, &found);
+    const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {
         M = s_m[lane];
@@ -589,14 +630,14 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     wave_lse(M, S);
 
     if (a.split == 1) {
-        write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, M + logf(S), x_chosen, d.chosen);
+        write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M + logf(S), x_chosen, d.chosen);
     } else {
-        PartialRec *rec = a.partials + uint64_t(o) * a.split + seg;
+        uint64_t *rec = a.partials + (uint64_t(o) * a.split + seg) * uint64_t(kK + 1);
         if (lane == 0) {
-            rec->m = M;
-            rec->s = S;
+            reinterpret_cast<float *>(rec)[0] = M;
+            reinterpret_cast<float *>(rec)[1] = S;
         }
-        if (lane < kSlots) rec->keys[lane] = top;
+        if (lane < kK) rec[1 + lane] = top;
     }
 }
 
@@ -608,42 +649,55 @@ struct MergeArgs {
     uint32_t split;
     uint32_t out_rows;
     const RowDesc *desc;
-    const PartialRec *partials;
+    const uint64_t *partials;
     float *out_lp;
     uint32_t *out_id;
 };
 
 // Split variant, second launch: one wave per output row combines the row's
-// segment records in segment order, then writes the row.
+// segment records in segment order, then writes the row.  split * kK <=
+// kMaxMergeKeys, so kPer keys per lane hold them.
+template <int kK>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    constexpr int kPer = int((kMaxMergeKeys + kWave - 1) / kWave) < (int(kMaxSplit) * kK + kWave - 1) / kWave
+                             ? int((kMaxMergeKeys + kWave - 1) / kWave)
+                             : (int(kMaxSplit) * kK + kWave - 1) / kWave;
     const int lane = int(threadIdx.x) & (kWave - 1);
     const uint32_t o = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (o >= a.out_rows) return;
     const RowDesc d = a.desc[o];
     if (d.top_n == 0) {
-        write_padding(a.out_lp, a.out_id, o, lane);
+        write_padding<kK>(a.out_lp, a.out_id, o, lane);
         return;
     }
     const float *row = a.src + uint64_t(d.src_row) * a.vocab;
-    const float x_chosen = lane == kSlots ? row[d.chosen] : 0.0f;
-    const PartialRec *recs = a.partials + uint64_t(o) * a.split;
+    const float x_chosen = lane == kK ? row[d.chosen] : 0.0f;
+    const uint64_t *recs = a.partials + uint64_t(o) * a.split * uint64_t(kK + 1);
     float m = -INFINITY, s = 0.0f;
     if (uint32_t(lane) < a.split) {
-        m = recs[lane].m;
-        s = recs[lane].s;
+        const float *ms = reinterpret_cast<const float *>(recs + uint64_t(lane) * (kK + 1));
+        m = ms[0];
+        s = ms[1];
     }
     wave_lse(m, s);
-    constexpr int kPer = (int(kMaxSplit) * kSlots + kWave - 1) / kWave;
-    const uint32_t nkeys = a.split * uint32_t(kSlots);
+    const uint32_t nkeys = a.split * uint32_t(kK);
     uint64_t e[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < nkeys ? recs[idx / kSlots].keys[idx % kSlots] : 0ull;
+        e[i] = idx < nkeys ? recs[(idx / kK) * (kK + 1) + 1 + idx % kK] : 0ull;
     }
     uint32_t found;
-    const uint64_t top = wave_select7<kPer>(e, lane, &found);
-    write_row(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), x_chosen, d.chosen);
+    const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
+    write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), x_chosen, d.chosen);
+}
+
+// Plans that read no row (every top_n is 0): all R * columns entries padding.
+__global__ __launch_bounds__(256) void pad_kernel(float *out_lp, uint32_t *out_id, uint64_t n) {
+    for (uint64_t i = uint64_t(blockIdx.x) * 256u + threadIdx.x; i < n; i += uint64_t(gridDim.x) * 256u) {
+        out_lp[i] = -INFINITY;
+        out_id[i] = kPadId;
+    }
 }
 
 // ------------------------------------------------------------------ streaming-read probe
@@ -696,23 +750,44 @@ void release_staging(lp_plan &p) {
     p.staging_pending = false;
 }
 
-template <int kWaves, int kDepth>
+template <int kK, int kWaves, int kDepth>
 static void launch_shape(bool direct, dim3 grid, hipStream_t s, const dev::RowArgs &ra) {
-    if (direct) hipLaunchKernelGGL((dev::row_kernel<kWaves, kDepth, true>), grid, dim3(kWaves * 64), 0, s, ra);
-    else hipLaunchKernelGGL((dev::row_kernel<kWaves, kDepth, false>), grid, dim3(kWaves * 64), 0, s, ra);
+    if (direct) hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, true>), grid, dim3(kWaves * 64), 0, s, ra);
+    else hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, false>), grid, dim3(kWaves * 64), 0, s, ra);
 }
 
-static void launch_row_kernel(uint32_t waves, bool deep, bool direct, dim3 grid, hipStream_t s,
-                              const dev::RowArgs &ra) {
-    if (waves == 16) {
-        if (deep) launch_shape<16, 2>(direct, grid, s, ra);
-        else launch_shape<16, 1>(direct, grid, s, ra);
-    } else if (waves == 8) {
-        if (deep) launch_shape<8, 2>(direct, grid, s, ra);
-        else launch_shape<8, 1>(direct, grid, s, ra);
+template <int kK>
+static void launch_rows(const lp_plan &p, dim3 grid, hipStream_t s, const dev::RowArgs &ra,
+                        const dev::MergeArgs &ma) {
+    const bool deep = p.depth == 2, direct = p.direct_rows != 0;
+    if (p.waves == 16) {
+        if (deep) launch_shape<kK, 16, 2>(direct, grid, s, ra);
+        else launch_shape<kK, 16, 1>(direct, grid, s, ra);
+    } else if (p.waves == 8) {
+        if (deep) launch_shape<kK, 8, 2>(direct, grid, s, ra);
+        else launch_shape<kK, 8, 1>(direct, grid, s, ra);
     } else {
-        if (deep) launch_shape<4, 2>(direct, grid, s, ra);
-        else launch_shape<4, 1>(direct, grid, s, ra);
+        if (deep) launch_shape<kK, 4, 2>(direct, grid, s, ra);
+        else launch_shape<kK, 4, 1>(direct, grid, s, ra);
+    }
+    if (p.split > 1) {
+        const uint32_t mblocks = static_cast<uint32_t>((p.out_rows + 3) / 4);
+        hipLaunchKernelGGL(dev::merge_kernel<kK>, dim3(mblocks), dim3(256), 0, s, ma);
+    }
+}
+
+// The row kernel (and the merge kernel for split plans) for the plan's slot
+// count; false if the plan has none the library is built for.
+static bool launch_for_slots(const lp_plan &p, dim3 grid, hipStream_t s, const dev::RowArgs &ra,
+                             const dev::MergeArgs &ma) {
+    switch (p.slots) {
+        case 1: launch_rows<1>(p, grid, s, ra, ma); return true;
+        case 3: launch_rows<3>(p, grid, s, ra, ma); return true;
+        case 7: launch_rows<7>(p, grid, s, ra, ma); return true;
+        case 15: launch_rows<15>(p, grid, s, ra, ma); return true;
+        case 31: launch_rows<31>(p, grid, s, ra, ma); return true;
+        case 63: launch_rows<63>(p, grid, s, ra, ma); return true;
+        default: return false;
     }
 }
 
@@ -771,9 +846,19 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     const uint64_t blocks = plan->out_rows * plan->split;
     if (blocks * waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
 
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->read_rows == 0) {   // every row padding-only; no logits read
+        const uint64_t n = plan->out_rows * plan->columns;
+        uint64_t g = (n + 255) / 256;
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL(lp::dev::pad_kernel, dim3(static_cast<uint32_t>(g)), dim3(256), 0, s,
+                           out_logprobs, out_token_ids, n);
+        LP_HIP_TRY(hipGetLastError());
+        return LP_OK;
+    }
     char *ws = static_cast<char *>(workspace);
     auto *desc = reinterpret_cast<const lp::RowDesc *>(ws);
-    auto *partials = reinterpret_cast<lp::PartialRec *>(ws + plan->desc_bytes);
+    auto *partials = reinterpret_cast<uint64_t *>(ws + plan->desc_bytes);
     lp::dev::RowArgs ra;
     ra.src = src;
     ra.vocab = plan->vocab;
@@ -784,24 +869,18 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ra.out_lp = out_logprobs;
     ra.out_id = out_token_ids;
     ra.partials = partials;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    lp::dev::MergeArgs ma;
+    ma.src = src;
+    ma.vocab = plan->vocab;
+    ma.split = plan->split;
+    ma.out_rows = static_cast<uint32_t>(plan->out_rows);
+    ma.desc = desc;
+    ma.partials = partials;
+    ma.out_lp = out_logprobs;
+    ma.out_id = out_token_ids;
     const dim3 grid(static_cast<uint32_t>(blocks));
-    lp::launch_row_kernel(plan->waves, plan->depth == 2, plan->direct_rows != 0, grid, s, ra);
+    if (!lp::launch_for_slots(*plan, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
     LP_HIP_TRY(hipGetLastError());
-    if (plan->split > 1) {
-        lp::dev::MergeArgs ma;
-        ma.src = src;
-        ma.vocab = plan->vocab;
-        ma.split = plan->split;
-        ma.out_rows = static_cast<uint32_t>(plan->out_rows);
-        ma.desc = desc;
-        ma.partials = partials;
-        ma.out_lp = out_logprobs;
-        ma.out_id = out_token_ids;
-        const uint32_t mblocks = static_cast<uint32_t>((plan->out_rows + 3) / 4);
-        hipLaunchKernelGGL(lp::dev::merge_kernel, dim3(mblocks), dim3(256), 0, s, ma);
-        LP_HIP_TRY(hipGetLastError());
-    }
     return LP_OK;
 }
 

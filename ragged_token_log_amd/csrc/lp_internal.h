@@ -10,11 +10,22 @@
 
 namespace lp {
 
-constexpr uint32_t kLevels = 3;
-constexpr uint32_t kCols = 1u << kLevels;     // 8 output columns
-constexpr uint32_t kTopSlots = kCols - 1;     // 7 ranked slots + 1 chosen slot
+// Output columns per row: 2^levels (one when levels is 0), the last one for
+// the chosen token, the others ranked slots; at most 64, one lane each.
+constexpr uint32_t kMaxLevels = 6;
 constexpr uint32_t kPadId = 0xFFFFFFFFu;
 constexpr uint32_t kMaxSplit = 64;
+// Keys the merge kernel's one wave holds for a row (16 per lane): the split
+// is capped so that split * slots stays within it.
+constexpr uint32_t kMaxMergeKeys = 1024;
+
+inline uint32_t columns_for_levels(uint32_t levels) { return levels > 0 ? 1u << levels : 1u; }
+
+inline uint32_t max_split_for_slots(uint32_t slots) {
+    if (slots == 0) return kMaxSplit;
+    const uint32_t s = kMaxMergeKeys / slots;
+    return s < kMaxSplit ? s : kMaxSplit;
+}
 // Longest vocabulary segment one workgroup streams: its byte range (at most
 // 1 GiB) must fit the 32-bit range and offsets of the buffer resource the row
 // kernel reads it through.
@@ -37,15 +48,11 @@ struct RowDesc {
 };
 static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
 
-// Partial result of one (row, vocabulary segment) in the split variant:
-// the segment's running max and scaled sum, and its 7 best order keys.
+// Partial result of one (row, vocabulary segment) in the split variant, in
+// 8-byte words: word 0 holds the segment's running max and scaled sum (two
+// floats), words 1..slots its best order keys, descending.
 // Workspace layout: [R descriptors, padded to 256 B][R x split records].
-struct PartialRec {
-    float m;
-    float s;
-    uint64_t keys[kTopSlots];
-};
-static_assert(sizeof(PartialRec) == 64, "PartialRec is 64 bytes");
+inline uint64_t partial_record_bytes(uint32_t slots) { return 8ull * (uint64_t(slots) + 1); }
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -55,6 +62,8 @@ struct lp_plan {
     uint32_t batch = 0;
     uint32_t vocab = 0;
     uint32_t levels = 0;
+    uint32_t columns = 0;            // 2^levels (1 at levels 0)
+    uint32_t slots = 0;              // columns - 1 ranked slots
     uint32_t has_logits = 0;
     uint64_t logits_rows = 0;
     std::vector<uint32_t> in_off;    // B+1
@@ -68,7 +77,7 @@ struct lp_plan {
     uint32_t depth = 2;              // chunks in flight per wave: 1 or 2
     uint32_t direct_rows = 0;        // 1: output row o reads logits row o (all top_n > 0)
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
-    uint64_t partial_bytes = 0;      // R * split * 64 when split > 1
+    uint64_t partial_bytes = 0;      // R * split * 8 (slots + 1) when split > 1
     uint64_t workspace_bytes = 0;
     // pinned staging for the descriptor upload (allocated on first stage)
     void *staging = nullptr;

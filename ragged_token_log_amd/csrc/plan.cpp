@@ -23,7 +23,7 @@ namespace lp {
 
 void size_workspace(lp_plan &p) {
     p.desc_bytes = align_up(p.out_rows * sizeof(RowDesc), 256);
-    p.partial_bytes = p.split > 1 ? p.out_rows * p.split * sizeof(PartialRec) : 0;
+    p.partial_bytes = p.split > 1 ? p.out_rows * p.split * partial_record_bytes(p.slots) : 0;
     p.workspace_bytes = p.desc_bytes + p.partial_bytes;
 }
 
@@ -36,7 +36,7 @@ void size_workspace(lp_plan &p) {
 // get more waves per row; too few to occupy 256 CUs even then are split
 // into segments (one workgroup each, at least kMinSegment elements), whose
 // partial results a second kernel merges.
-static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
+static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t *waves,
                            uint32_t *depth, uint32_t *split) {
     constexpr uint64_t kManyRows = 1024;
     constexpr uint64_t kSomeRows = 384;
@@ -65,7 +65,7 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t *waves,
     uint64_t by_vocab = vocab / kMinSegment;
     if (by_vocab < 1) by_vocab = 1;
     if (s > by_vocab) s = by_vocab;
-    if (s > kMaxSplit) s = kMaxSplit;
+    if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
     if (s < min_split) s = min_split;
     *split = static_cast<uint32_t>(s);
 }
@@ -115,7 +115,9 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
     *plan_out = nullptr;
     if (input_row_offsets == nullptr) return LP_ERR_NULL_ARG;
     if (batch > 0 && (batch_echo == nullptr || batch_top_n == nullptr)) return LP_ERR_NULL_ARG;
-    if (levels != lp::kLevels) return LP_ERR_UNSUPPORTED;
+    if (levels > lp::kMaxLevels) return LP_ERR_UNSUPPORTED;
+    const uint32_t columns = lp::columns_for_levels(levels);
+    const int32_t max_top_n = int32_t(columns) - 1;
     if (vocab < 1) return LP_ERR_SHAPE;
 
     // offsets: start at 0, every request non-empty
@@ -130,7 +132,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
     }
     for (uint32_t n = 0; n < batch; ++n) {
         if (batch_top_n[n] < 0) return LP_ERR_TOP_N_NEGATIVE;
-        if (batch_top_n[n] > int32_t(lp::kTopSlots)) return LP_ERR_TOP_N_TOO_LARGE;
+        if (batch_top_n[n] > max_top_n) return LP_ERR_TOP_N_TOO_LARGE;
     }
     for (uint32_t n = 0; n < batch; ++n)
         if (batch_echo[n] && !has_logits) return LP_ERR_ECHO_NEEDS_LOGITS;
@@ -141,6 +143,8 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         p->batch = batch;
         p->vocab = vocab;
         p->levels = levels;
+        p->columns = columns;
+        p->slots = columns - 1;
         p->has_logits = has_logits ? 1 : 0;
         p->logits_rows = logits_rows;
         p->in_off.assign(input_row_offsets, input_row_offsets + batch + 1);
@@ -176,7 +180,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         delete p;
         return LP_ERR_NOMEM;
     }
-    lp::choose_variant(p->read_rows, vocab, &p->waves, &p->depth, &p->split);
+    lp::choose_variant(p->read_rows, vocab, p->slots, &p->waves, &p->depth, &p->split);
     lp::size_workspace(*p);
 
     if (output_row_offsets != nullptr)
@@ -192,7 +196,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
     info->batch = plan->batch;
     info->vocab = plan->vocab;
     info->levels = plan->levels;
-    info->columns = lp::kCols;
+    info->columns = plan->columns;
     info->out_rows = plan->out_rows;
     info->read_rows = plan->read_rows;
     info->split = plan->split;
@@ -207,7 +211,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
 
 lp_status lp_plan_set_split(lp_plan *plan, uint32_t split) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
-    if (split < 1 || split > lp::kMaxSplit) return LP_ERR_UNSUPPORTED;
+    if (split < 1 || split > lp::max_split_for_slots(plan->slots)) return LP_ERR_UNSUPPORTED;
     if (lp::segment_length(plan->vocab, split) > lp::kMaxSegment) return LP_ERR_UNSUPPORTED;
     plan->split = split;
     lp::size_workspace(*plan);

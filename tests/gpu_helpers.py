@@ -28,9 +28,10 @@ class DeviceRows:
 
 
 def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None,
-                waves=None, depth=None):
+                waves=None, depth=None, levels=3):
     lp, ids, out_off = R.compute_log_probabilities_ragged(
-        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves, depth=depth)
+        offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves, depth=depth,
+        levels=levels)
     torch.cuda.synchronize()
     return lp.cpu().numpy(), ids.cpu().numpy(), out_off
 
@@ -67,9 +68,9 @@ def assert_parity(lp, ids, out_off, ref, where, rows=None):
     assert_lp_close(lp[sel], ref_lp[sel], where)
 
 
-def oracle(offsets, logits, ntl, tokens, sampled, top_n, echo, rows=None):
+def oracle(offsets, logits, ntl, tokens, sampled, top_n, echo, rows=None, levels=3):
     return LO.compute_log_probabilities_ragged(offsets, logits, ntl, tokens, sampled,
-                                               list(top_n), list(echo), rows=rows)
+                                               list(top_n), list(echo), rows=rows, levels=levels)
 
 
 def check_all_rows_properties(torch, src, desc, lp_dev, ids_dev, vocab, chunk=256):

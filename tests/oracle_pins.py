@@ -291,3 +291,66 @@ def pin_errors():
     args["batch_top_n"] = [15, 1]
     lp, ids, _ = LO.compute_log_probabilities_ragged(levels=4, **args)
     assert lp.shape == (3, 16)
+
+
+# ------------------------------------------------------------------ levels
+
+def pin_levels_columns():
+    """[MAX] §log_probabilities_ragged_graph: out_per_token is 2**levels, or 1
+    when levels is 0; one column is the chosen token's, so top_n may reach
+    columns - 1 ([MAX] §图支持的最大 top-n: levels 3 serves up to 7)."""
+    for levels, cols in ((0, 1), (1, 2), (2, 4), (3, 8), (4, 16), (5, 32), (6, 64)):
+        assert LO.columns_for_levels(levels) == cols, levels
+        assert LO.max_top_n(levels) == cols - 1, levels
+
+
+def pin_levels_bruteforce(rows, levels_list=(1, 2, 4, 5, 6)):
+    """Every heap depth: the ranked columns are brute-force repeated argmax
+    ids, padded past min(top_n, V), and the last column is the chosen token;
+    a top_n beyond columns - 1 is rejected."""
+    P = LO.PAD_ID
+    for levels in levels_list:
+        cols = 2 ** levels
+        for x in rows:
+            x = np.asarray(x, dtype=np.float32)
+            V = x.shape[0]
+            for top_n in sorted({0, 1, cols // 2, cols - 1}):
+                chosen = V // 2
+                lp, ids, off = LO.compute_log_probabilities_ragged(
+                    np.array([0, 1], np.uint32), None, x[None, :], np.zeros(1, np.uint32),
+                    np.array([chosen], np.uint32), [top_n], [False], levels=levels)
+                assert lp.shape == (1, cols) and ids.shape == (1, cols)
+                if top_n == 0:
+                    assert ids[0].tolist() == [P] * cols
+                    continue
+                want = brute_top_ids([float(v) for v in x], min(top_n, V))
+                got = ids[0, :len(want)].tolist()
+                assert got == want, (levels, top_n, got, want)
+                assert ids[0, len(want):cols - 1].tolist() == [P] * (cols - 1 - len(want))
+                assert ids[0, cols - 1] == chosen
+            try:
+                LO.compute_log_probabilities_ragged(
+                    np.array([0, 1], np.uint32), None, x[None, :], np.zeros(1, np.uint32),
+                    np.array([0], np.uint32), [cols], [False], levels=levels)
+            except LO.OracleError as e:
+                assert e.code == "LP_ERR_TOP_N_TOO_LARGE"
+            else:
+                raise AssertionError(f"levels {levels}: top_n {cols} accepted")
+
+
+def pin_levels_zero():
+    """levels 0 keeps a single column and admits only top_n == 0, whose rows
+    are padding (reading R6)."""
+    x = np.array([[0.5, 1.5, -1.0]], np.float32)
+    lp, ids, _ = LO.compute_log_probabilities_ragged(
+        np.array([0, 1], np.uint32), None, x, np.zeros(1, np.uint32), np.array([1], np.uint32),
+        [0], [False], levels=0)
+    assert ids.shape == (1, 1) and ids[0, 0] == LO.PAD_ID and np.isneginf(lp[0, 0])
+    try:
+        LO.compute_log_probabilities_ragged(
+            np.array([0, 1], np.uint32), None, x, np.zeros(1, np.uint32),
+            np.array([1], np.uint32), [1], [False], levels=0)
+    except LO.OracleError as e:
+        assert e.code == "LP_ERR_TOP_N_TOO_LARGE"
+    else:
+        raise AssertionError("levels 0 accepted top_n 1")

@@ -94,6 +94,28 @@ def test_direct_rows_on_named_workloads():
         assert plan.info()["direct_rows"] == expect[name], name
 
 
+@pytest.mark.parametrize("levels", range(0, 8))
+def test_levels_columns_and_caps(levels):
+    """[MAX] log_probabilities_ragged_graph: 2**levels columns (1 at levels
+    0), top_n up to columns - 1; the library serves levels 0..6."""
+    off = np.array([0, 2, 3], np.uint32)
+    if levels > 6:
+        _expect("LP_ERR_UNSUPPORTED", lambda: R.Plan(off, [1, 0], [0, 0], 100, True, levels=levels))
+        return
+    cols = LO.columns_for_levels(levels)
+    cap = LO.max_top_n(levels)
+    plan = R.Plan(off, [1, 0], [cap, 0], 100, True, levels=levels)
+    assert plan.columns == cols and plan.info()["columns"] == cols
+    _expect("LP_ERR_TOP_N_TOO_LARGE", lambda: R.Plan(off, [1, 0], [cap + 1, 0], 100, True,
+                                                     levels=levels))
+    # the split cap keeps a row's records within the merge wave's 1024 keys
+    wide = R.Plan(np.array([0, 1], np.uint32), [0], [cap], 1 << 20, False, levels=levels)
+    limit = 64 if cap == 0 else min(64, 1024 // cap)
+    wide.set_split(limit)
+    _expect("LP_ERR_UNSUPPORTED", lambda: wide.set_split(limit + 1))
+    assert wide.workspace_bytes == 256 + limit * 8 * (cap + 1)
+
+
 def test_plan_on_named_workloads():
     for name, make in gen.WORKLOADS.items():
         c = make()
@@ -168,7 +190,7 @@ def test_error_codes_match_oracle_readings():
     _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [1, 0], [1, 1], 5, True, logits_rows=4))
     _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [0, 0], [1, 1], 5, False, logits_rows=3))
     _expect("LP_ERR_SHAPE", lambda: R.Plan(off, [1, 0], [1, 1], 0, True))
-    _expect("LP_ERR_UNSUPPORTED", lambda: R.Plan(off, [1, 0], [1, 1], 5, True, levels=4))
+    _expect("LP_ERR_UNSUPPORTED", lambda: R.Plan(off, [1, 0], [1, 1], 5, True, levels=7))
     plan = R.Plan(off, [1, 0], [1, 7], 5, True)
     _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([1, 2, 5], [4, 0]))
     _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([1, 2, 3], [4, 5]))

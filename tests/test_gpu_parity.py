@@ -145,6 +145,55 @@ def test_decode_peaked(R, split, waves, depth):
     assert np.array_equal(got[1][:, 7], c.sampled)
 
 
+def _levels_batch(seed, vocab, levels, rows_per_req=(1, 4, 1, 6, 2, 3)):
+    rng = np.random.default_rng(seed)
+    lengths = np.array(rows_per_req)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    cap = LO.max_top_n(levels)
+    echo = np.array([1, 1, 0, 1, 0, 1], bool)[: len(lengths)]
+    top_n = rng.integers(0, cap + 1, len(lengths)) if cap > 0 else np.zeros(len(lengths), int)
+    if cap > 0:
+        top_n[0] = cap
+        top_n[-1] = 0
+    logits = _special_rows(rng, int(off[-1]), vocab)
+    ntl = logits[off[1:].astype(np.int64) - 1]
+    tokens = rng.integers(0, vocab, int(off[-1])).astype(np.uint32)
+    sampled = rng.integers(0, vocab, len(lengths)).astype(np.uint32)
+    return off, logits, ntl, tokens, sampled, top_n, echo
+
+
+@pytest.mark.parametrize("levels", [0, 1, 2, 4, 5, 6])
+@pytest.mark.parametrize("vocab", [3, 77, 1027, 40001])
+@pytest.mark.parametrize("split,waves,depth", [(None, None, None), (1, 4, 1), (3, 8, 2), (1, 16, 2),
+                                               (16, 4, 2)])
+def test_levels(R, levels, vocab, split, waves, depth):
+    """[MAX] log_probabilities_ragged_graph: 2**levels columns, top_n up to
+    2**levels - 1, every heap depth the library serves."""
+    log(f"levels={levels} vocab={vocab} split={split} waves={waves} depth={depth}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(levels * 100 + vocab, vocab, levels)
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+    got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split,
+                      waves, depth, levels=levels)
+    assert got[0].shape[1] == LO.columns_for_levels(levels)
+    assert_parity(*got, ref, f"levels={levels} vocab={vocab} split={split}")
+
+
+@pytest.mark.parametrize("levels", [1, 5, 6])
+def test_levels_direct_rows(R, levels):
+    """Next-token rows (the direct-row kernels) at other heap depths, with the
+    split path at its largest split for the depth."""
+    c = gen.decode_peaked(seed=30 + levels, batch=24, vocab=70001)
+    ntl = gen.host_logits(c)
+    cap = LO.max_top_n(levels)
+    top_n = np.full(c.batch, cap)
+    ref = oracle(c.offsets, None, ntl, c.tokens, c.sampled, top_n, c.echo, levels=levels)
+    for split in (None, 1, min(64, 1024 // cap)):
+        log(f"direct rows levels={levels} split={split}")
+        got = run_library(R, torch, c.offsets, None, _dev(ntl), c.tokens, c.sampled, top_n, c.echo,
+                          split, levels=levels)
+        assert_parity(*got, ref, f"direct levels={levels} split={split}")
+
+
 def _full_size(R, c, n_sample, seed):
     dev = torch.device("cuda")
     logits = gen.device_logits(c, dev, torch)

@@ -99,7 +99,18 @@ def _row_ignores_top_n(row, chosen, top_n, cols):
     return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols)
 
 
+def _cap_equals_columns(levels):
+    # plausible slip: forgetting the column reserved for the chosen token
+    return 2 ** levels if levels > 0 else 1
+
+
+def _columns_two_to_levels_plus_one(levels):
+    return 2 ** (levels + 1) if levels > 0 else 1
+
+
 MUTANTS = {
+    "cap_equals_columns": ("max_top_n", _cap_equals_columns),
+    "columns_off_by_level": ("columns_for_levels", _columns_two_to_levels_plus_one),
     "ties_high_id_first": ("rank_descending", _rank_ties_high_id_first),
     "negzero_ranks_low": ("rank_descending", _rank_negzero_below_poszero),
     "lse_no_shift": ("log_softmax_f64", _lsm_no_shift),
@@ -127,6 +138,9 @@ def _run_all_pins():
     P.pin_ranking_special_cases()
     P.pin_batch_hand_example()
     P.pin_errors()
+    P.pin_levels_columns()
+    P.pin_levels_bruteforce([rng.standard_normal(40).astype(np.float32)], levels_list=(1, 4))
+    P.pin_levels_zero()
 
 
 def test_pins_pass_on_true_oracle():

@@ -62,3 +62,18 @@ def test_batch_hand_example():
 
 def test_errors():
     P.pin_errors()
+
+
+def test_levels_columns():
+    P.pin_levels_columns()
+
+
+def test_levels_bruteforce():
+    rng = np.random.default_rng(13)
+    rows = [rng.integers(-3, 4, size=n).astype(np.float32) / 2 for n in (1, 3, 20, 70, 130)]
+    rows += [rng.standard_normal(n).astype(np.float32) for n in (2, 63, 64, 65, 200)]
+    P.pin_levels_bruteforce(rows)
+
+
+def test_levels_zero():
+    P.pin_levels_zero()

@@ -37,11 +37,13 @@ DEFAULT_STEPS = {"no_echo_next_token": 200, "ragged_echo_mix": 200, "decode_peak
 
 def algorithmic_bytes(plan_info, vocab):
     """Bytes a perfect implementation moves per launch: each read row once
-    (4 V), 64 B of output and a 16 B descriptor per output row."""
-    return int(plan_info["read_rows"]) * 4 * vocab + int(plan_info["out_rows"]) * (64 + 16)
+    (4 V), C columns of fp32 + uint32 output (64 B at C = 8) and a 16 B
+    descriptor per output row."""
+    cols = int(plan_info["columns"])
+    return int(plan_info["read_rows"]) * 4 * vocab + int(plan_info["out_rows"]) * (8 * cols + 16)
 
 
-def cpu_baseline(case, logits_dev, ntl_dev, budget_s=10.0, max_rows=2000):
+def cpu_baseline(case, logits_dev, ntl_dev, cols=8, budget_s=10.0, max_rows=2000):
     """The oracle as it stands, on a bounded sample of the same workload: the
     first read rows in output order (at most max_rows), in repeated passes
     until about budget_s of oracle time has been spent."""
@@ -62,7 +64,7 @@ def cpu_baseline(case, logits_dev, ntl_dev, budget_s=10.0, max_rows=2000):
         for o in live:
             t = tasks[o]
             t0 = time.perf_counter()
-            LO.compute_row(rows[t.src_row], t.chosen, t.top_n, 8)
+            LO.compute_row(rows[t.src_row], t.chosen, t.top_n, cols)
             t_total += time.perf_counter() - t0
             done += 1
             if t_total >= budget_s and passes > 1:
@@ -81,6 +83,10 @@ def main():
     ap.add_argument("--workload", default="ragged_echo_mix")
     ap.add_argument("--split", type=int, default=None, help="force the plan's split")
     ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8)")
+    ap.add_argument("--levels", type=int, default=3,
+                    help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
+    ap.add_argument("--top-n", type=int, default=None,
+                    help="replace every nonzero top_n of the workload with this value")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -112,6 +118,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = gen.WORKLOADS[args.workload]()
+    if args.top_n is not None:
+        case.top_n = np.where(np.asarray(case.top_n) > 0, args.top_n, 0)
     steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
     stream = torch.cuda.current_stream(dev)
 
@@ -123,7 +131,8 @@ def main():
     copies = [base] + [base.clone() for _ in range(n_copies - 1)]
     torch.cuda.synchronize()
 
-    plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits)
+    plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits,
+                  levels=args.levels)
     if args.split:
         plan.set_split(args.split)
     if args.waves:
@@ -186,6 +195,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded draws with the workload's shapes and distributions)",
         "config": {"workload": case.name, "batch": case.batch, "vocab": case.vocab,
+                   "levels": args.levels, "max_top_n": int(np.max(case.top_n)),
                    "out_rows": int(info["out_rows"]), "read_rows": read_rows,
                    "split": int(info["split"]), "waves": int(info["waves"]),
                    "logits_copies_cycled": n_copies},
@@ -205,7 +215,8 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(e2e_steps):
-            p2 = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits)
+            p2 = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits,
+                        levels=args.levels)
             if args.split:
                 p2.set_split(args.split)
             if args.waves:
@@ -218,6 +229,24 @@ def main():
         e2e_ms = (time.perf_counter() - t0) * 1e3 / e2e_steps
         result["e2e_host_inputs"] = {"ms_per_step": e2e_ms, "rows_per_s": read_rows / (e2e_ms * 1e-3),
                                      "note": "plan + descriptor upload from host + launch per step"}
+
+    # host result assembly (lp_assemble_ragged) on this step's outputs, after
+    # their copy back: the per-request dicts of the page's compute_top
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
+    t1 = time.perf_counter()
+    reps = 0
+    while True:
+        plan.assemble(lp_h, ids_h)
+        reps += 1
+        if time.perf_counter() - t1 > 0.2:
+            break
+    asm_ms = (time.perf_counter() - t1) * 1e3 / reps
+    result["host_assembly"] = {"ms": asm_ms, "rows_per_s": int(info["out_rows"]) / (asm_ms * 1e-3),
+                               "copy_back_ms": (t1 - t0) * 1e3,
+                               "note": "lp_assemble_ragged on the host, one thread; copy back "
+                                       "of the (R, C) outputs timed separately"}
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
@@ -234,7 +263,7 @@ def main():
         result["roofline"]["traffic"] = traffic
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, base, ntl)
+        result["cpu_baseline"] = cpu_baseline(case, base, ntl, cols=int(info["columns"]))
 
     print(json.dumps(result), flush=True)
 

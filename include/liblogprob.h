@@ -178,6 +178,31 @@ lp_status lp_compute_ragged(lp_plan *plan, const float *logits,
                             uint32_t *out_token_ids, void *workspace,
                             uint64_t workspace_bytes, void *stream);
 
+/*
+ * lp_assemble_ragged -- host-side result assembly of rows copied back from
+ * the device ([MAX] §compute_top 的结果组装; no HIP call).
+ *
+ * For each output row o (C = columns of the plan), the entries of that
+ * row's top-log-probability dict, in insertion order:
+ *   1. the ranked columns 0..C-2 whose token id is < V (padding dropped),
+ *      sorted by log-probability, descending (stable: equal values keep
+ *      their column order), truncated to the request's top_n;
+ *   2. the chosen token of the last column: appended when absent, else its
+ *      value overwrites the existing entry in place.
+ * Rows of requests with top_n == 0 get no entries (the request's result is
+ * None on the page).  The request's token log-probabilities are the last
+ * column of its rows.
+ *
+ *   lp, ids       host, (R, C) fp32 / uint32 as written by lp_launch_ragged
+ *   out_tokens    host out, (R, C) uint32: row o's entries at [o*C, o*C + n_o)
+ *   out_logprobs  host out, (R, C) fp32, matching out_tokens
+ *   out_counts    host out, R uint32: n_o (at most min(top_n, C-1) + 1)
+ * Entries past n_o are left as they were.  LP_ERR_NULL_ARG if a pointer is
+ * NULL while R > 0.
+ */
+lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_t *ids,
+                             uint32_t *out_tokens, float *out_logprobs, uint32_t *out_counts);
+
 /* Frees the plan.  Waits for a pending descriptor copy from its staging
  * buffer first.  NULL is a no-op. */
 void lp_plan_destroy(lp_plan *plan);

@@ -266,3 +266,40 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
         row = src[t.src_row] if t.top_n > 0 else None
         out_lp[o], out_ids[o] = compute_row(row, t.chosen, t.top_n, cols)
     return out_lp, out_ids, out_off
+
+
+# ------------------------------------------------------------------ host assembly
+
+def compute_top(lp_row, id_row, top_n: int, vocab: int) -> dict:
+    """One output row's top dict.  [MAX] §compute_top 的结果组装: drop the
+    padding columns (token id >= vocab), sort the (token, logprob) pairs by
+    logprob descending, keep top_n, then write the sampled token's entry
+    from the row's last column into the dict, overwriting a duplicate key."""
+    if top_n < 0:
+        raise OracleError("LP_ERR_TOP_N_NEGATIVE", f"top_n={top_n}")
+    cols = len(id_row)
+    if top_n > cols - 1:
+        raise OracleError("LP_ERR_TOP_N_TOO_LARGE", f"top_n={top_n} > {cols - 1}")
+    pairs = [(int(t), float(v)) for t, v in zip(id_row[: cols - 1], lp_row[: cols - 1])
+             if int(t) < vocab]
+    pairs = sorted(pairs, key=lambda p: p[1], reverse=True)[:top_n]
+    out = dict(pairs)
+    out[int(id_row[cols - 1])] = float(lp_row[cols - 1])
+    return out
+
+
+def assemble(out_lp, out_ids, out_off, batch_top_n, vocab: int):
+    """Per request: None when top_n == 0, else (token log-probabilities = the
+    last column of each of its rows, top dicts per row).  [MAX]
+    §compute_top 的结果组装 (the final paragraph: a LogProbabilities per
+    batch item, None for top_n == 0)."""
+    res = []
+    for n, top_n in enumerate(batch_top_n):
+        if int(top_n) == 0:
+            res.append(None)
+            continue
+        rows = range(int(out_off[n]), int(out_off[n + 1]))
+        cols = out_ids.shape[1]
+        res.append(([float(out_lp[o, cols - 1]) for o in rows],
+                    [compute_top(out_lp[o], out_ids[o], int(top_n), vocab) for o in rows]))
+    return res

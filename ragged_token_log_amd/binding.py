@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -25,7 +26,7 @@ STATUS_NAMES = {
 # every symbol include/liblogprob.h declares
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
-    "lp_plan_set_depth", "lp_plan_descriptors",
+    "lp_plan_set_depth", "lp_plan_descriptors", "lp_assemble_ragged",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
@@ -81,6 +82,8 @@ def load():
     lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_set_depth.argtypes = [vp, u32]
     lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
+    lib.lp_assemble_ragged.argtypes = [vp, P(ctypes.c_float), P(u32), P(u32), P(ctypes.c_float),
+                                       P(u32)]
     lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
     lib.lp_compute_ragged.argtypes = [vp, vp, vp, P(u32), P(u32), vp, vp, vp, u64, vp]
@@ -91,7 +94,8 @@ def load():
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
-                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_descriptors", "lp_stage_ragged", "lp_launch_ragged",
+                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_descriptors", "lp_assemble_ragged",
+                 "lp_stage_ragged", "lp_launch_ragged",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -193,6 +197,23 @@ class Plan:
                                              _ptr(out, ctypes.c_uint32)), "lp_plan_descriptors")
         return out
 
+    def assemble(self, lp, ids):
+        """lp_assemble_ragged on host (R, C) outputs: per output row the
+        (token, logprob) entries of its top dict in insertion order, as
+        ``(tokens (R, C) uint32, logprobs (R, C) float32, counts (R,) uint32)``."""
+        C = self.columns
+        lp = np.ascontiguousarray(lp, dtype=np.float32)
+        ids = np.ascontiguousarray(ids, dtype=np.uint32)
+        if lp.shape != (self.out_rows, C) or ids.shape != (self.out_rows, C):
+            raise LogprobError(3, "assemble: outputs must be (out_rows, columns)")
+        toks = np.zeros((self.out_rows, C), dtype=np.uint32)
+        vals = np.zeros((self.out_rows, C), dtype=np.float32)
+        counts = np.zeros(self.out_rows, dtype=np.uint32)
+        _check(self._lib.lp_assemble_ragged(self._h, _ptr(lp, ctypes.c_float), _ptr(ids, ctypes.c_uint32),
+                                            _ptr(toks, ctypes.c_uint32), _ptr(vals, ctypes.c_float),
+                                            _ptr(counts, ctypes.c_uint32)), "lp_assemble_ragged")
+        return toks, vals, counts
+
     # ---------------------------------------------------------------- device work
     def stage(self, tokens, sampled_tokens, workspace, stream=None):
         tok = _u32(tokens) if tokens is not None else None
@@ -284,6 +305,17 @@ def alloc_outputs(plan: Plan, device, torch):
     return lp, ids, ws
 
 
+@dataclass
+class LogProbabilities:
+    """One request's result, with the fields of the MAX page's
+    ``LogProbabilities`` (section "数据结构：可序列化的 LogProbabilities"):
+    per output row, the chosen token's log-probability and the dict of top
+    token ids to log-probabilities."""
+
+    token_log_probabilities: list
+    top_log_probabilities: list
+
+
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens,
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
@@ -320,18 +352,60 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
                 None if logits is None else int(logits.shape[0]), levels=levels)
     try:
-        if split is not None:
-            plan.set_split(split)
-        if waves is not None:
-            plan.set_waves(waves)
-        if depth is not None:
-            plan.set_depth(depth)
-        device = next_token_logits.device
-        if stream is None:
-            stream = torch.cuda.current_stream(device)
-        lp, ids, ws = alloc_outputs(plan, device, torch)
-        plan.compute(logits, next_token_logits, tokens, sampled_tokens, lp, ids, ws, stream)
+        lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
+                       depth, stream, torch)
         out_off = plan.out_off.copy()
     finally:
         plan.close()   # waits only for the descriptor upload, not the kernels
     return lp, ids, out_off
+
+
+def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, depth, stream,
+         torch):
+    if split is not None:
+        plan.set_split(split)
+    if waves is not None:
+        plan.set_waves(waves)
+    if depth is not None:
+        plan.set_depth(depth)
+    device = next_token_logits.device
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    lp, ids, ws = alloc_outputs(plan, device, torch)
+    plan.compute(logits, next_token_logits, tokens, sampled_tokens, lp, ids, ws, stream)
+    return lp, ids
+
+
+def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens, sampled_tokens,
+                             batch_top_n, batch_echo, *, levels: int = LEVELS, stream=None):
+    """The whole call of the MAX page's ``compute_log_probabilities_ragged``:
+    the device computation, the copy back, and the host assembly
+    (lp_assemble_ragged).  Returns one entry per request: None when its
+    top_n is 0, else a LogProbabilities whose lists hold one item per output
+    row of the request."""
+    import torch
+
+    lp, ids, out_off = compute_log_probabilities_ragged(
+        input_row_offsets, logits, next_token_logits, tokens, sampled_tokens, batch_top_n,
+        batch_echo, stream=stream, levels=levels)
+    vocab = int(next_token_logits.shape[1])
+    plan = Plan(np.asarray(input_row_offsets), batch_echo, batch_top_n, vocab, logits is not None,
+                None if logits is None else int(logits.shape[0]), levels=levels)
+    try:
+        torch.cuda.synchronize(lp.device)
+        lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
+        toks, vals, counts = plan.assemble(lp_h, ids_h)
+    finally:
+        plan.close()
+    C = lp_h.shape[1]
+    out = []
+    for n, top_n in enumerate(np.asarray(batch_top_n)):
+        if int(top_n) == 0:
+            out.append(None)
+            continue
+        rows = range(int(out_off[n]), int(out_off[n + 1]))
+        out.append(LogProbabilities(
+            token_log_probabilities=[float(lp_h[o, C - 1]) for o in rows],
+            top_log_probabilities=[{int(toks[o, k]): float(vals[o, k]) for k in range(int(counts[o]))}
+                                   for o in rows]))
+    return out

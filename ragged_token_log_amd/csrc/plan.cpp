@@ -239,6 +239,66 @@ lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
                                  reinterpret_cast<lp::RowDesc *>(desc_out));
 }
 
+lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_t *ids,
+                             uint32_t *out_tokens, float *out_logprobs, uint32_t *out_counts) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (plan->out_rows == 0) return LP_OK;
+    if (lp == nullptr || ids == nullptr || out_tokens == nullptr || out_logprobs == nullptr ||
+        out_counts == nullptr)
+        return LP_ERR_NULL_ARG;
+    const uint64_t C = plan->columns;
+    struct Entry {
+        uint32_t token;
+        float value;
+    };
+    std::vector<Entry> e;
+    e.reserve(C);
+    for (uint32_t n = 0; n < plan->batch; ++n) {
+        const int32_t top_n = plan->top_n[n];
+        for (uint64_t o = plan->out_off[n]; o < plan->out_off[n + 1]; ++o) {
+            if (top_n == 0) {
+                out_counts[o] = 0;
+                continue;
+            }
+            const float *lrow = lp + o * C;
+            const uint32_t *irow = ids + o * C;
+            e.clear();
+            for (uint64_t j = 0; j + 1 < C; ++j)
+                if (irow[j] < plan->vocab) e.push_back(Entry{irow[j], lrow[j]});
+            // stable insertion sort, descending; a NaN never compares greater,
+            // so NaN entries (an all -inf row) keep their order
+            for (size_t i = 1; i < e.size(); ++i) {
+                const Entry cur = e[i];
+                size_t k = i;
+                while (k > 0 && cur.value > e[k - 1].value) {
+                    e[k] = e[k - 1];
+                    --k;
+                }
+                e[k] = cur;
+            }
+            if (e.size() > size_t(top_n)) e.resize(size_t(top_n));
+            // insertion into a dict keyed by token: a repeated key keeps its
+            // first position and takes the later value; the chosen token
+            // (last column) goes in last the same way
+            e.push_back(Entry{irow[C - 1], lrow[C - 1]});
+            size_t kept = 0;
+            for (size_t i = 0; i < e.size(); ++i) {
+                size_t k = 0;
+                while (k < kept && e[k].token != e[i].token) ++k;
+                if (k < kept) e[k].value = e[i].value;
+                else e[kept++] = e[i];
+            }
+            e.resize(kept);
+            for (size_t k = 0; k < e.size(); ++k) {
+                out_tokens[o * C + k] = e[k].token;
+                out_logprobs[o * C + k] = e[k].value;
+            }
+            out_counts[o] = static_cast<uint32_t>(e.size());
+        }
+    }
+    return LP_OK;
+}
+
 void lp_plan_destroy(lp_plan *plan) {
     if (plan == nullptr) return;
     lp::release_staging(*plan);

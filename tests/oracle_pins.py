@@ -354,3 +354,67 @@ def pin_levels_zero():
         assert e.code == "LP_ERR_TOP_N_TOO_LARGE"
     else:
         raise AssertionError("levels 0 accepted top_n 1")
+
+
+# ------------------------------------------------------------------ host assembly
+
+def pin_assembly_hand_examples():
+    """[MAX] §compute_top 的结果组装, worked by hand: padding dropped, pairs
+    sorted by logprob descending, top_n kept, the last column forced in
+    (appended, or overwriting a present key in place)."""
+    P = LO.PAD_ID
+    lp = np.array([-1.2, -0.5, -2.0, -np.inf, -np.inf, -np.inf, -np.inf, -3.0], np.float32)
+    ids = np.array([2, 5, 7, P, P, P, P, 9], np.uint32)
+    d = LO.compute_top(lp, ids, 2, 10)
+    assert list(d.items()) == [(5, -0.5), (2, np.float32(-1.2)), (9, -3.0)], d
+    # the sampled token already among the top: its entry takes the last column's value
+    ids2 = ids.copy()
+    ids2[7] = 2
+    d = LO.compute_top(lp, ids2, 3, 10)
+    assert list(d.items()) == [(5, -0.5), (2, -3.0), (7, -2.0)], d
+    # a sampled token outside the kept top_n is appended after them
+    d = LO.compute_top(lp, np.array([2, 5, 7, P, P, P, P, 7], np.uint32), 1, 10)
+    assert list(d.items()) == [(5, -0.5), (7, -3.0)], d
+    # ids >= vocab are padding even when not the pad id
+    d = LO.compute_top(lp, np.array([2, 10, 7, P, P, P, P, 9], np.uint32), 7, 10)
+    assert list(d.keys()) == [2, 7, 9], d
+    # a top_n = 0 request is None; token log-probabilities are the last column
+    out_lp = np.stack([lp, lp, lp])
+    out_ids = np.stack([ids, ids, ids])
+    res = LO.assemble(out_lp, out_ids, np.array([0, 2, 3], np.uint32), [2, 0], 10)
+    assert res[1] is None
+    tlp, tops = res[0]
+    assert tlp == [-3.0, -3.0] and len(tops) == 2
+    for bad, code in ((-1, "LP_ERR_TOP_N_NEGATIVE"), (8, "LP_ERR_TOP_N_TOO_LARGE")):
+        try:
+            LO.compute_top(lp, ids, bad, 10)
+        except LO.OracleError as e:
+            assert e.code == code
+        else:
+            raise AssertionError(f"top_n {bad} accepted")
+
+
+def pin_assembly_worked_example():
+    """The SGLang page's printed response (section "logprob 的数值形态"):
+    with each position's printed pair in its top columns and the printed
+    token as the chosen one, the assembled result is the printed
+    token_logprobs list and top_logprobs dicts (token names mapped to ids)."""
+    with open(os.path.join(GOLDEN, "sglang_worked_example.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    names = sorted({t for pos in g["top_logprobs"] for t, _ in pos} | set(g["tokens"]))
+    tid = {t: i for i, t in enumerate(names)}
+    P = LO.PAD_ID
+    rows_lp, rows_id = [], []
+    for pos, tok in enumerate(g["tokens"]):
+        (t1, a), (t2, b) = g["top_logprobs"][pos]
+        rows_lp.append([a, b] + [-np.inf] * 5 + [g["token_logprobs"][pos]])
+        rows_id.append([tid[t1], tid[t2]] + [P] * 5 + [tid[tok]])
+    out_lp = np.array(rows_lp, np.float32)
+    out_ids = np.array(rows_id, np.uint32)
+    res = LO.assemble(out_lp, out_ids, np.array([0, 3], np.uint32), [2], len(names))
+    tlp, tops = res[0]
+    assert np.allclose(tlp, g["token_logprobs"], atol=1e-6)
+    for pos in range(3):
+        want = {tid[t]: v for t, v in g["top_logprobs"][pos]}
+        assert list(tops[pos].keys()) == list(want.keys()), (pos, tops[pos], want)
+        assert all(abs(tops[pos][k] - want[k]) < 1e-6 for k in want)

@@ -220,3 +220,35 @@ def test_no_echo_request_with_full_logits_needs_no_tokens():
     plan = R.Plan([0, 4, 6], [0, 0], [3, 3], 9, True)
     d = plan.descriptors(None, [1, 2])
     assert d[:, :2].tolist() == [[3, 1], [5, 2]]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_assembly_matches_oracle(seed):
+    """lp_assemble_ragged (host code, no GPU) against the oracle's
+    compute_top on random device-shaped outputs: shuffled columns, padding,
+    ties, sampled tokens inside and outside the top columns."""
+    rng = np.random.default_rng(200 + seed)
+    levels = int(rng.integers(1, 7))
+    cols = 2 ** levels
+    batch = int(rng.integers(1, 8))
+    vocab = int(rng.integers(cols, 4 * cols + 2))
+    off, echo, top_n, tokens, sampled = _random_batch(rng, batch, vocab, True)
+    top_n = rng.integers(0, cols, size=batch)
+    plan = R.Plan(off, echo, top_n, vocab, True, levels=levels)
+    R_rows = plan.out_rows
+    ids = rng.integers(0, vocab + 3, size=(R_rows, cols)).astype(np.uint32)
+    ids[rng.random((R_rows, cols)) < 0.2] = binding.PAD_ID
+    ids[:, -1] = rng.integers(0, vocab, size=R_rows)
+    take = rng.random(R_rows) < 0.5            # sampled token among the columns
+    ids[take, -1] = ids[take, 0] % vocab
+    lp = (rng.integers(-6, 1, size=(R_rows, cols)) / 2).astype(np.float32)
+    toks, vals, counts = plan.assemble(lp, ids)
+    want = LO.assemble(lp, ids, plan.out_off, top_n, vocab)
+    for n in range(batch):
+        rows = range(int(plan.out_off[n]), int(plan.out_off[n + 1]))
+        if want[n] is None:
+            assert all(counts[o] == 0 for o in rows)
+            continue
+        for k, o in enumerate(rows):
+            got = list(zip(toks[o, :counts[o]].tolist(), vals[o, :counts[o]].tolist()))
+            assert got == list(want[n][1][k].items()), (n, o, got, want[n][1][k])

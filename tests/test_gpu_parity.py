@@ -194,6 +194,35 @@ def test_levels_direct_rows(R, levels):
         assert_parity(*got, ref, f"direct levels={levels} split={split}")
 
 
+def _same_value(a, b):
+    return (np.isnan(a) and np.isnan(b)) or a == b or abs(a - b) <= 1e-5
+
+
+@pytest.mark.parametrize("levels", [1, 3, 5])
+@pytest.mark.parametrize("vocab", [5, 1027, 32000])
+def test_log_probabilities_objects(R, levels, vocab):
+    """The whole call: device path, copy back and host assembly
+    (lp_assemble_ragged) against the oracle's rows and its compute_top."""
+    log(f"log_probabilities_ragged levels={levels} vocab={vocab}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(7 * levels + vocab, vocab, levels)
+    got = R.log_probabilities_ragged(off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
+                                     levels=levels)
+    ref_lp, ref_ids, ref_off = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+    want = LO.assemble(ref_lp, ref_ids, ref_off, top_n, vocab)
+    assert len(got) == len(want)
+    for n, (g, w) in enumerate(zip(got, want)):
+        if w is None:
+            assert g is None, n
+            continue
+        assert isinstance(g, R.LogProbabilities)
+        w_tlp, w_tops = w
+        assert len(g.token_log_probabilities) == len(w_tlp)
+        assert all(_same_value(a, b) for a, b in zip(g.token_log_probabilities, w_tlp)), n
+        for gd, wd in zip(g.top_log_probabilities, w_tops):
+            assert list(gd.keys()) == list(wd.keys()), (n, gd, wd)
+            assert all(_same_value(gd[k], wd[k]) for k in wd), (n, gd, wd)
+
+
 def _full_size(R, c, n_sample, seed):
     dev = torch.device("cuda")
     logits = gen.device_logits(c, dev, torch)

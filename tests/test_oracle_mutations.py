@@ -99,6 +99,25 @@ def _row_ignores_top_n(row, chosen, top_n, cols):
     return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols)
 
 
+def _top_no_overwrite(lp_row, id_row, top_n, vocab):
+    # plausible slip: the sampled token only added when absent (no overwrite)
+    cols = len(id_row)
+    pairs = [(int(t), float(v)) for t, v in zip(id_row[: cols - 1], lp_row[: cols - 1])
+             if int(t) < vocab]
+    out = dict(sorted(pairs, key=lambda p: p[1], reverse=True)[:top_n])
+    out.setdefault(int(id_row[cols - 1]), float(lp_row[cols - 1]))
+    return out
+
+
+def _top_truncate_before_sort(lp_row, id_row, top_n, vocab):
+    cols = len(id_row)
+    pairs = [(int(t), float(v)) for t, v in zip(id_row[: cols - 1], lp_row[: cols - 1])
+             if int(t) < vocab][:top_n]
+    out = dict(sorted(pairs, key=lambda p: p[1], reverse=True))
+    out[int(id_row[cols - 1])] = float(lp_row[cols - 1])
+    return out
+
+
 def _cap_equals_columns(levels):
     # plausible slip: forgetting the column reserved for the chosen token
     return 2 ** levels if levels > 0 else 1
@@ -109,6 +128,8 @@ def _columns_two_to_levels_plus_one(levels):
 
 
 MUTANTS = {
+    "top_no_overwrite": ("compute_top", _top_no_overwrite),
+    "top_truncate_before_sort": ("compute_top", _top_truncate_before_sort),
     "cap_equals_columns": ("max_top_n", _cap_equals_columns),
     "columns_off_by_level": ("columns_for_levels", _columns_two_to_levels_plus_one),
     "ties_high_id_first": ("rank_descending", _rank_ties_high_id_first),
@@ -141,6 +162,8 @@ def _run_all_pins():
     P.pin_levels_columns()
     P.pin_levels_bruteforce([rng.standard_normal(40).astype(np.float32)], levels_list=(1, 4))
     P.pin_levels_zero()
+    P.pin_assembly_hand_examples()
+    P.pin_assembly_worked_example()
 
 
 def test_pins_pass_on_true_oracle():

@@ -77,3 +77,11 @@ def test_levels_bruteforce():
 
 def test_levels_zero():
     P.pin_levels_zero()
+
+
+def test_assembly_hand_examples():
+    P.pin_assembly_hand_examples()
+
+
+def test_assembly_worked_example():
+    P.pin_assembly_worked_example()

@@ -87,6 +87,8 @@ def main():
                     help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
     ap.add_argument("--top-n", type=int, default=None,
                     help="replace every nonzero top_n of the workload with this value")
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="log_softmax(logits / T) for every request")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -137,6 +139,8 @@ def main():
         plan.set_split(args.split)
     if args.waves:
         plan.set_waves(args.waves)
+    if args.temperature is not None:
+        plan.set_temperature(args.temperature)
     info = plan.info()
     lp, ids, ws = R.alloc_outputs(plan, dev, torch)
     plan.stage(case.tokens, case.sampled, ws, stream)   # descriptors resident in HBM
@@ -196,6 +200,7 @@ def main():
         "data": "synthetic (seeded draws with the workload's shapes and distributions)",
         "config": {"workload": case.name, "batch": case.batch, "vocab": case.vocab,
                    "levels": args.levels, "max_top_n": int(np.max(case.top_n)),
+                   "temperature": args.temperature if args.temperature is not None else 1.0,
                    "out_rows": int(info["out_rows"]), "read_rows": read_rows,
                    "split": int(info["split"]), "waves": int(info["waves"]),
                    "logits_copies_cycled": n_copies},

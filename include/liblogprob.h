@@ -58,7 +58,9 @@ typedef enum lp_status {
     LP_ERR_UNSUPPORTED = 8,       /* levels != 3, or a split outside 1..64 */
     LP_ERR_WORKSPACE = 9,         /* workspace NULL or smaller than the plan asks */
     LP_ERR_HIP = 10,              /* a HIP runtime call failed; see lp_last_hip_error() */
-    LP_ERR_NOMEM = 11             /* host allocation failed */
+    LP_ERR_NOMEM = 11,            /* host allocation failed */
+    LP_ERR_TEMPERATURE = 12       /* a temperature that is not a positive finite number
+                                     with a finite reciprocal */
 } lp_status;
 
 /* Facts about a plan (all host values). */
@@ -130,10 +132,24 @@ lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
 lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
 
 /*
+ * Per-request temperature (host, B floats; NULL restores 1 for all).  The
+ * log-probabilities of request n become log_softmax(x / T_n) of its rows,
+ * the temperature scaling the FlashInfer page describes (its Temperature
+ * processor divides the logits by a positive temperature) and that [SGL]
+ * §output 从 forward() 到响应对象的完整路径 applies before the softmax whose
+ * result the logprobs reuse.  The ranking stays on the raw logits (for T > 0
+ * it is the same order).  LP_ERR_TEMPERATURE, with the plan unchanged, if
+ * some T_n is not positive and finite or 1/T_n is not finite and nonzero.
+ * Applies to descriptors built after the call.
+ */
+lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature);
+
+/*
  * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of
- * 4 uint32 to desc_out: {logits row read, chosen token, top_n, 0}, in output
+ * 4 uint32 to desc_out: {logits row read, chosen token, top_n, 1/temperature bits}, in output
  * row order.  tokens: host, T uint32 (may be NULL when no request echoes);
- * sampled_tokens: host, B uint32.  LP_ERR_TOKEN_RANGE if an id >= V.
+ * sampled_tokens: host, B uint32.  LP_ERR_TOKEN_RANGE if an id >= V.  The
+ * fourth word holds the fp32 bits of the row's 1 / temperature.
  */
 lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
                               const uint32_t *sampled_tokens, uint32_t *desc_out);

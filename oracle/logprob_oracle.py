@@ -43,6 +43,7 @@ they are compared at 1e-5 absolute.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -191,10 +192,27 @@ def row_tasks(input_row_offsets, batch_echo, batch_top_n, tokens, sampled_tokens
     return tasks
 
 
-def log_softmax_f64(row) -> tuple[np.ndarray, float]:
-    """log p = x - logsumexp(x) in float64.  [SGL] §logprob 的数值形态: a
-    logprob is log of a probability in (0, 1], so it is <= 0."""
-    x = np.asarray(row, dtype=np.float64)
+def check_temperature(t) -> float:
+    """A request's temperature: positive and finite (the FlashInfer page's
+    Temperature processor rejects a non-positive value), with a finite,
+    nonzero reciprocal (reading R19)."""
+    t = float(np.float32(t))
+    if not (t > 0.0 and math.isfinite(t)):
+        raise OracleError("LP_ERR_TEMPERATURE", f"temperature={t}")
+    with np.errstate(over="ignore"):
+        inv = float(np.float32(1.0) / np.float32(t))
+    if not (0.0 < inv < math.inf):
+        raise OracleError("LP_ERR_TEMPERATURE", f"temperature={t}: 1/T not finite")
+    return t
+
+
+def log_softmax_f64(row, temperature: float = 1.0) -> tuple[np.ndarray, float]:
+    """log p = z - logsumexp(z), z = x / temperature, in float64.  [SGL]
+    §logprob 的数值形态: a logprob is log of a probability in (0, 1], so it
+    is <= 0; [SGL] §output 从 forward() 到响应对象的完整路径 and the FlashInfer
+    page's Temperature processor: the softmax is of the logits divided by
+    the temperature."""
+    x = np.asarray(row, dtype=np.float64) / np.float64(temperature)
     m = np.max(x)
     with np.errstate(invalid="ignore"):
         lse = m + np.log(np.sum(np.exp(x - m)))
@@ -210,7 +228,7 @@ def rank_descending(row_f32) -> np.ndarray:
     return np.argsort(-canon.astype(np.float64), kind="stable")
 
 
-def compute_row(row_f32, chosen: int, top_n: int, cols: int):
+def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float = 1.0):
     """One output row: ``cols - 1`` top slots (padded past min(top_n, V)) and
     the chosen token in the last slot.  [MAX] §log_probabilities_ragged_graph
     (lp_logits / lp_tokens) and §compute_top 的结果组装."""
@@ -221,7 +239,7 @@ def compute_row(row_f32, chosen: int, top_n: int, cols: int):
     x = np.asarray(row_f32, dtype=np.float32)
     if np.any(np.isnan(x)) or np.any(np.isposinf(x)):
         raise OracleError("LP_ERR_UNSUPPORTED", "NaN or +inf logits (R10)")
-    lp, _ = log_softmax_f64(x)
+    lp, _ = log_softmax_f64(x, temperature)
     order = rank_descending(x)
     take = order[: min(top_n, x.shape[0], cols - 1)]
     for j, t in enumerate(take):
@@ -234,7 +252,7 @@ def compute_row(row_f32, chosen: int, top_n: int, cols: int):
 
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits,
                                      tokens, sampled_tokens, batch_top_n, batch_echo,
-                                     levels=DEFAULT_LEVELS, rows=None):
+                                     levels=DEFAULT_LEVELS, rows=None, batch_temperature=None):
     """The whole path for one batch.
 
     Arguments follow [MAX] §compute_log_probabilities_ragged：执行计算并组装结果.
@@ -258,13 +276,21 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
                       sampled_tokens, has_logits)
     src = logits if has_logits else next_token_logits
     n_out = len(tasks)
+    batch = len(batch_top_n)
+    if batch_temperature is None:
+        temps = [1.0] * batch
+    else:
+        temps = [check_temperature(t) for t in batch_temperature]
+        if len(temps) != batch:
+            raise OracleError("LP_ERR_SHAPE", "one temperature per request")
+    req = np.repeat(np.arange(batch), np.diff(out_off.astype(np.int64)))
     out_lp = np.full((n_out, cols), -np.inf, dtype=np.float32)
     out_ids = np.full((n_out, cols), PAD_ID, dtype=np.uint32)
     which = range(n_out) if rows is None else rows
     for o in which:
         t = tasks[o]
         row = src[t.src_row] if t.top_n > 0 else None
-        out_lp[o], out_ids[o] = compute_row(row, t.chosen, t.top_n, cols)
+        out_lp[o], out_ids[o] = compute_row(row, t.chosen, t.top_n, cols, temps[req[o]])
     return out_lp, out_ids, out_off
 
 

@@ -20,13 +20,13 @@ STATUS_NAMES = {
     0: "LP_OK", 1: "LP_ERR_NULL_ARG", 2: "LP_ERR_OFFSETS", 3: "LP_ERR_SHAPE",
     4: "LP_ERR_TOP_N_NEGATIVE", 5: "LP_ERR_TOP_N_TOO_LARGE", 6: "LP_ERR_ECHO_NEEDS_LOGITS",
     7: "LP_ERR_TOKEN_RANGE", 8: "LP_ERR_UNSUPPORTED", 9: "LP_ERR_WORKSPACE",
-    10: "LP_ERR_HIP", 11: "LP_ERR_NOMEM",
+    10: "LP_ERR_HIP", 11: "LP_ERR_NOMEM", 12: "LP_ERR_TEMPERATURE",
 }
 
 # every symbol include/liblogprob.h declares
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
-    "lp_plan_set_depth", "lp_plan_descriptors", "lp_assemble_ragged",
+    "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_descriptors", "lp_assemble_ragged",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
@@ -81,6 +81,7 @@ def load():
     lib.lp_plan_set_split.argtypes = [vp, u32]
     lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_set_depth.argtypes = [vp, u32]
+    lib.lp_plan_set_temperature.argtypes = [vp, P(ctypes.c_float)]
     lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
     lib.lp_assemble_ragged.argtypes = [vp, P(ctypes.c_float), P(u32), P(u32), P(ctypes.c_float),
                                        P(u32)]
@@ -94,7 +95,8 @@ def load():
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
-                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_descriptors", "lp_assemble_ragged",
+                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_temperature",
+                 "lp_plan_descriptors", "lp_assemble_ragged",
                  "lp_stage_ragged", "lp_launch_ragged",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
@@ -186,6 +188,21 @@ class Plan:
 
     def set_depth(self, depth: int):
         _check(self._lib.lp_plan_set_depth(self._h, int(depth)), "lp_plan_set_depth")
+
+    def set_temperature(self, temperature):
+        """Per-request temperatures (a scalar for all, a length-batch
+        sequence, or None for 1)."""
+        if temperature is None:
+            _check(self._lib.lp_plan_set_temperature(self._h, None), "lp_plan_set_temperature")
+            return
+        t = np.asarray(temperature, dtype=np.float32)
+        if t.ndim == 0:
+            t = np.full(self.batch, t, dtype=np.float32)
+        t = np.ascontiguousarray(t)
+        if t.shape != (self.batch,):
+            raise LogprobError(3, "temperature must be a scalar or one value per request")
+        _check(self._lib.lp_plan_set_temperature(self._h, _ptr(t, ctypes.c_float)),
+               "lp_plan_set_temperature")
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
         """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
@@ -320,7 +337,7 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
                                      depth: int | None = None, stream=None,
-                                     levels: int = LEVELS):
+                                     levels: int = LEVELS, temperature=None):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -332,7 +349,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
 
     ``levels`` is the heap depth of the MAX page's graph (section
     "log_probabilities_ragged_graph"): C = 2**levels output columns (one at
-    levels 0), top_n <= C - 1.
+    levels 0), top_n <= C - 1.  ``temperature`` (a scalar or one per
+    request) gives log_softmax(logits / temperature); None means 1.
 
     Returns ``(logprobs (R, C) float32, token_ids (R, C) uint32,
     output_row_offsets (batch+1,) uint32 numpy)``, the tensors on the GPU.
@@ -352,6 +370,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
                 None if logits is None else int(logits.shape[0]), levels=levels)
     try:
+        if temperature is not None:
+            plan.set_temperature(temperature)
         lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
                        depth, stream, torch)
         out_off = plan.out_off.copy()
@@ -377,7 +397,8 @@ def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, 
 
 
 def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens, sampled_tokens,
-                             batch_top_n, batch_echo, *, levels: int = LEVELS, stream=None):
+                             batch_top_n, batch_echo, *, levels: int = LEVELS, temperature=None,
+                             stream=None):
     """The whole call of the MAX page's ``compute_log_probabilities_ragged``:
     the device computation, the copy back, and the host assembly
     (lp_assemble_ragged).  Returns one entry per request: None when its
@@ -387,7 +408,7 @@ def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, token
 
     lp, ids, out_off = compute_log_probabilities_ragged(
         input_row_offsets, logits, next_token_logits, tokens, sampled_tokens, batch_top_n,
-        batch_echo, stream=stream, levels=levels)
+        batch_echo, stream=stream, levels=levels, temperature=temperature)
     vocab = int(next_token_logits.shape[1])
     plan = Plan(np.asarray(input_row_offsets), batch_echo, batch_top_n, vocab, logits is not None,
                 None if logits is None else int(logits.shape[0]), levels=levels)

@@ -175,31 +175,32 @@ __device__ __forceinline__ f32x4 stream_load(const StreamRange &r, uint32_t off)
 // (m, s) with s = sum e^(x - m): merge (m2, s2) into (m, s).  A max of -inf
 // (nothing finite seen) contributes nothing and never forms -inf - -inf.
 // Symmetric in its two operands, so both lanes of a butterfly agree bit for bit.
-__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+// c = log2(e) / temperature: every sum is of e^((x - m) / temperature)
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2, float c) {
     const float M = fmaxf(m, m2);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
-    s = s * fast_exp2((m - Ms) * kLog2e) + s2 * fast_exp2((m2 - Ms) * kLog2e);
+    s = s * fast_exp2((m - Ms) * c) + s2 * fast_exp2((m2 - Ms) * c);
     m = M;
 }
 
 template <int kCtrl>
-__device__ __forceinline__ void lse_dpp_step(float &m, float &s) {
+__device__ __forceinline__ void lse_dpp_step(float &m, float &s, float c) {
     const float m2 = dpp_f32<kCtrl>(m);
     const float s2 = dpp_f32<kCtrl>(s);
-    lse_merge(m, s, m2, s2);
+    lse_merge(m, s, m2, s2, c);
 }
 
 // Every lane ends with the wave's (m, s), merged in a fixed order.
-__device__ __forceinline__ void wave_lse(float &m, float &s) {
-    lse_dpp_step<kDppXor1>(m, s);
-    lse_dpp_step<kDppXor2>(m, s);
-    lse_dpp_step<kDppHalfMirror>(m, s);
-    lse_dpp_step<kDppMirror>(m, s);
+__device__ __forceinline__ void wave_lse(float &m, float &s, float c) {
+    lse_dpp_step<kDppXor1>(m, s, c);
+    lse_dpp_step<kDppXor2>(m, s, c);
+    lse_dpp_step<kDppHalfMirror>(m, s, c);
+    lse_dpp_step<kDppMirror>(m, s, c);
     float M = readlane_f32(m, 0), S = readlane_f32(s, 0);
-    lse_merge(M, S, readlane_f32(m, 16), readlane_f32(s, 16));
+    lse_merge(M, S, readlane_f32(m, 16), readlane_f32(s, 16), c);
     float M2 = readlane_f32(m, 32), S2 = readlane_f32(s, 32);
-    lse_merge(M2, S2, readlane_f32(m, 48), readlane_f32(s, 48));
-    lse_merge(M, S, M2, S2);
+    lse_merge(M2, S2, readlane_f32(m, 48), readlane_f32(s, 48), c);
+    lse_merge(M, S, M2, S2, c);
     m = M;
     s = S;
 }
@@ -332,19 +333,27 @@ struct RowArgs {
     uint64_t *partials;        // split > 1: (R, split) records of slots + 1 words
 };
 
+// log p = (x - M) / temperature - ln S for a row whose max is M and whose
+// S = sum of e^((x - M) / temperature): the subtraction comes first, so a
+// large common offset of the row costs no accuracy.
+__device__ __forceinline__ float logprob(float x, float M, float inv_temp, float ln_s) {
+    return (x - M) * inv_temp - ln_s;
+}
+
 // One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK
 // the chosen token.
 template <int kK>
 __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint64_t o, int lane,
-                                          uint64_t key, uint32_t top_n, float lse,
-                                          float x_chosen, uint32_t chosen) {
+                                          uint64_t key, uint32_t top_n, float M, float S,
+                                          float inv_temp, float x_chosen, uint32_t chosen) {
     constexpr uint64_t kC = uint64_t(kK) + 1;
+    const float ln_s = logf(S);
     if (lane < kK) {
         const bool valid = uint32_t(lane) < top_n && key != 0;
-        out_lp[o * kC + lane] = valid ? key_value(key) - lse : -INFINITY;
+        out_lp[o * kC + lane] = valid ? logprob(key_value(key), M, inv_temp, ln_s) : -INFINITY;
         out_id[o * kC + lane] = valid ? key_id(key) : kPadId;
     } else if (lane == kK) {
-        out_lp[o * kC + lane] = x_chosen - lse;
+        out_lp[o * kC + lane] = logprob(x_chosen, M, inv_temp, ln_s);
         out_id[o * kC + lane] = chosen;
     }
 }
@@ -355,7 +364,8 @@ __device__ __forceinline__ RowDesc load_desc_uniform(const RowDesc *desc, uint32
     const uint4 v = *reinterpret_cast<const uint4 *>(desc + o);
     return RowDesc{uint32_t(__builtin_amdgcn_readfirstlane(int(v.x))),
                    uint32_t(__builtin_amdgcn_readfirstlane(int(v.y))),
-                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))), 0u};
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.w)))};
 }
 
 template <int kK>
@@ -410,7 +420,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
     const uint32_t ntr = (v1 - a0) & 3u;
 
-    float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^(x - m)
+    // the row's 1 / temperature; sums are of e^((x - m) / temperature)
+    const float inv_temp = __uint_as_float(d.inv_temp_bits);
+    const float c = kLog2e * inv_temp;
+    float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^((x - m) / temperature)
     uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
 
@@ -447,11 +460,11 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         float acc[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            acc[u] = fast_exp2((x[u].x - ms) * kLog2e) + fast_exp2((x[u].y - ms) * kLog2e) +
-                     (fast_exp2((x[u].z - ms) * kLog2e) + fast_exp2((x[u].w - ms) * kLog2e));
+            acc[u] = fast_exp2((x[u].x - ms) * c) + fast_exp2((x[u].y - ms) * c) +
+                     (fast_exp2((x[u].z - ms) * c) + fast_exp2((x[u].w - ms) * c));
         }
         const float csum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        s = s * fast_exp2((m - ms) * kLog2e) + csum;
+        s = s * fast_exp2((m - ms) * c) + csum;
         m = mn;
         return cm;
     };
@@ -584,10 +597,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         const float cm = fmaxf(fmaxf(fmaxf(x4.x, x4.y), fmaxf(x4.z, x4.w)), x1);
         const float mn = fmaxf(m, cm);
         const float ms = (mn == -INFINITY) ? 0.0f : mn;
-        const float add = (fast_exp2((x4.x - ms) * kLog2e) + fast_exp2((x4.y - ms) * kLog2e)) +
-                          (fast_exp2((x4.z - ms) * kLog2e) + fast_exp2((x4.w - ms) * kLog2e)) +
-                          fast_exp2((x1 - ms) * kLog2e);
-        s = s * fast_exp2((m - ms) * kLog2e) + add;
+        const float add = (fast_exp2((x4.x - ms) * c) + fast_exp2((x4.y - ms) * c)) +
+                          (fast_exp2((x4.z - ms) * c) + fast_exp2((x4.w - ms) * c)) +
+                          fast_exp2((x1 - ms) * c);
+        s = s * fast_exp2((m - ms) * c) + add;
         m = mn;
         T = umax64(T, uniform64(lds_load_relaxed(&s_T)));
         const float tv = threshold_value(T);
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // the workgroup to get here merges them and writes the row (or the
     // segment's record)
     if (lane < kK) s_keys[wave * kK + lane] = list;
-    wave_lse(m, s);
+    wave_lse(m, s, c);
     if (lane == 0) {
         s_m[wave] = m;
         s_s[wave] = s;
@@ -627,10 +640,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         M = s_m[lane];
         S = s_s[lane];
     }
-    wave_lse(M, S);
+    wave_lse(M, S, c);
 
     if (a.split == 1) {
-        write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M + logf(S), x_chosen, d.chosen);
+        write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, inv_temp, x_chosen, d.chosen);
     } else {
         uint64_t *rec = a.partials + (uint64_t(o) * a.split + seg) * uint64_t(kK + 1);
         if (lane == 0) {
@@ -679,7 +692,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         m = ms[0];
         s = ms[1];
     }
-    wave_lse(m, s);
+    const float inv_temp = __uint_as_float(d.inv_temp_bits);
+    wave_lse(m, s, kLog2e * inv_temp);
     const uint32_t nkeys = a.split * uint32_t(kK);
     uint64_t e[kPer];
 #pragma unroll
@@ -689,7 +703,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     uint32_t found;
     const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
-    write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m + logf(s), x_chosen, d.chosen);
+    write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m, s, inv_temp, x_chosen, d.chosen);
 }
 
 // Plans that read no row (every top_n is 0): all R * columns entries padding.

@@ -44,7 +44,7 @@ struct RowDesc {
     uint32_t src_row;   // logits row to read (row of `logits` or of next_token_logits)
     uint32_t chosen;    // token whose log-probability goes in the last column
     uint32_t top_n;     // 0 => padding only, logits not read
-    uint32_t reserved;
+    uint32_t inv_temp_bits;  // fp32 bits of 1 / temperature of the row's request
 };
 static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
 
@@ -70,6 +70,7 @@ struct lp_plan {
     std::vector<uint32_t> out_off;   // B+1
     std::vector<uint8_t> echo;       // B
     std::vector<int32_t> top_n;      // B
+    std::vector<float> inv_temp;     // B: 1 / temperature (1 unless set)
     uint64_t out_rows = 0;
     uint64_t read_rows = 0;
     uint32_t split = 1;

@@ -95,7 +95,9 @@ lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
             d.src_row = static_cast<uint32_t>(src_end - count + k);
             d.chosen = (pos + 1 < len) ? tokens[p.in_off[n] + pos + 1] : sampled[n];
             d.top_n = static_cast<uint32_t>(p.top_n[n]);
-            d.reserved = 0;
+            uint32_t bits;
+            std::memcpy(&bits, &p.inv_temp[n], 4);
+            d.inv_temp_bits = bits;
             out[o] = d;
         }
     }
@@ -150,6 +152,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         p->in_off.assign(input_row_offsets, input_row_offsets + batch + 1);
         p->echo.resize(batch);
         p->top_n.resize(batch);
+        p->inv_temp.assign(batch, 1.0f);
         p->out_off.resize(size_t(batch) + 1);
         uint64_t acc = 0, read = 0;
         p->out_off[0] = 0;
@@ -229,6 +232,22 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (depth != 1 && depth != 2) return LP_ERR_UNSUPPORTED;
     plan->depth = depth;
+    return LP_OK;
+}
+
+lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (batch_temperature == nullptr) {
+        plan->inv_temp.assign(plan->batch, 1.0f);
+        return LP_OK;
+    }
+    for (uint32_t n = 0; n < plan->batch; ++n) {
+        const float t = batch_temperature[n];
+        // positive and finite, with a finite, nonzero reciprocal
+        if (!(t > 0.0f) || !(t < 3.0e38f) || !(1.0f / t > 0.0f) || !(1.0f / t < 3.0e38f))
+            return LP_ERR_TEMPERATURE;
+    }
+    for (uint32_t n = 0; n < plan->batch; ++n) plan->inv_temp[n] = 1.0f / batch_temperature[n];
     return LP_OK;
 }
 
@@ -319,6 +338,7 @@ const char *lp_status_string(lp_status status) {
         case LP_ERR_WORKSPACE: return "LP_ERR_WORKSPACE";
         case LP_ERR_HIP: return "LP_ERR_HIP";
         case LP_ERR_NOMEM: return "LP_ERR_NOMEM";
+        case LP_ERR_TEMPERATURE: return "LP_ERR_TEMPERATURE";
     }
     return "LP_ERR_UNKNOWN";
 }

@@ -418,3 +418,44 @@ def pin_assembly_worked_example():
         want = {tid[t]: v for t, v in g["top_logprobs"][pos]}
         assert list(tops[pos].keys()) == list(want.keys()), (pos, tops[pos], want)
         assert all(abs(tops[pos][k] - want[k]) < 1e-6 for k in want)
+
+
+# ------------------------------------------------------------------ temperature
+
+def pin_temperature():
+    """log_softmax(x / T): closed forms, a 50-digit brute force, the ranking
+    untouched by T, and the rejected temperatures."""
+    # two tokens apart by d: the lower one has -log(1 + e^(d/T)) at temperature T
+    for d, T in ((1.0, 0.5), (3.0, 2.0), (0.25, 0.1), (5.0, 1.0)):
+        x = np.array([0.0, -d], np.float32)
+        lp, _ = LO.log_softmax_f64(x, T)
+        assert abs(lp[1] - (-math.log1p(math.exp(d / T)))) < 1e-12, (d, T, lp)
+        assert abs(lp[0] - (-math.log1p(math.exp(-d / T)))) < 1e-12, (d, T, lp)
+    # uniform rows stay uniform at any temperature
+    for T in (0.3, 4.0):
+        lp, _ = LO.log_softmax_f64(np.full(1000, 2.5, np.float32), T)
+        assert np.allclose(lp, -math.log(1000), atol=1e-12)
+    # brute force at 50 digits on x / T
+    rng = np.random.default_rng(17)
+    for T in (0.2, 0.7, 3.0):
+        xs = (rng.standard_normal(9) * 3).astype(np.float32)
+        want, _ = mp_logprobs([float(v) / T for v in xs])
+        lp, _ = LO.log_softmax_f64(xs, T)
+        assert max(abs(float(a) - float(b)) for a, b in zip(lp, want)) < 1e-12, T
+    # the ids and the row layout do not depend on T; the values are the
+    # float32 rounding of log_softmax(x / T)
+    x = (rng.integers(-4, 5, 200) / 2).astype(np.float32)
+    base_lp, base_id = LO.compute_row(x, 3, 7, 8)
+    for T in (0.05, 0.5, 9.0):
+        lp, ids = LO.compute_row(x, 3, 7, 8, T)
+        assert ids.tolist() == base_id.tolist() == brute_top_ids([float(v) for v in x], 7) + [3]
+        z = x.astype(np.float64) / T
+        ref = z - (z.max() + math.log(np.exp(z - z.max()).sum()))
+        assert np.allclose(lp[:7], ref[ids[:7]].astype(np.float32), atol=1e-6)
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        try:
+            LO.check_temperature(bad)
+        except LO.OracleError as e:
+            assert e.code == "LP_ERR_TEMPERATURE"
+        else:
+            raise AssertionError(f"temperature {bad} accepted")

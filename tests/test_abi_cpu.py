@@ -60,7 +60,8 @@ def test_plan_matches_oracle(seed):
     assert plan.out_rows == int(out_off[-1])
     desc = plan.descriptors(tokens, sampled)
     tasks = LO.row_tasks(off, echo, top_n, tokens, sampled, has_logits)
-    want = np.array([[t.src_row, t.chosen, t.top_n, 0] for t in tasks], dtype=np.uint32)
+    one = int(np.array([1.0], np.float32).view(np.uint32)[0])
+    want = np.array([[t.src_row, t.chosen, t.top_n, one] for t in tasks], dtype=np.uint32)
     assert np.array_equal(desc, want)
     info = plan.info()
     assert info["read_rows"] == sum(int(c) for c, t in zip(counts, top_n) if t > 0)
@@ -252,3 +253,19 @@ def test_assembly_matches_oracle(seed):
         for k, o in enumerate(rows):
             got = list(zip(toks[o, :counts[o]].tolist(), vals[o, :counts[o]].tolist()))
             assert got == list(want[n][1][k].items()), (n, o, got, want[n][1][k])
+
+
+def test_temperature_in_descriptors_and_errors():
+    off = np.array([0, 2, 3], np.uint32)
+    plan = R.Plan(off, [1, 0], [3, 2], 50, True)
+    tokens = np.array([1, 2, 3], np.uint32)
+    sampled = np.array([4, 5], np.uint32)
+    plan.set_temperature([0.5, 2.0])
+    desc = plan.descriptors(tokens, sampled)
+    inv = desc[:, 3].view(np.float32)
+    assert inv.tolist() == [2.0, 2.0, 0.5]           # rows of request 0, then request 1
+    for bad in ([0.0, 1.0], [-1.0, 1.0], [np.inf, 1.0], [np.nan, 1.0], [1e-45, 1.0]):
+        _expect("LP_ERR_TEMPERATURE", lambda b=bad: plan.set_temperature(b))
+    assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [2.0, 2.0, 0.5]
+    plan.set_temperature(None)
+    assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [1.0] * 3

@@ -194,6 +194,58 @@ def test_levels_direct_rows(R, levels):
         assert_parity(*got, ref, f"direct levels={levels} split={split}")
 
 
+def _assert_close_rel(got, want, where):
+    """Logprobs at a temperature T != 1: |lp| reaches |x - max| / T, so the
+    fp32 rounding of the value itself grows with it; the bound is 1e-5 plus
+    4 ulp of the expected value (NaN and infinities exactly)."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(nan, np.isnan(got)), where
+    inf = np.isinf(want)
+    assert np.array_equal(got[inf], want[inf]), where
+    fin = ~nan & ~inf
+    tol = 1e-5 + 4 * np.spacing(np.abs(want[fin]))
+    d = np.abs(got[fin].astype(np.float64) - want[fin])
+    assert np.all(d <= tol), (where, float(d.max()), float(np.abs(want[fin]).max()))
+
+
+@pytest.mark.parametrize("levels", [3, 5])
+@pytest.mark.parametrize("vocab", [1027, 40001])
+@pytest.mark.parametrize("split", [None, 3, 16])
+def test_temperature(R, levels, vocab, split):
+    """log_softmax(x / T) per request (the temperature of the FlashInfer
+    page's Temperature processor), ranking on the raw logits."""
+    log(f"temperature levels={levels} vocab={vocab} split={split}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(3 * vocab + levels, vocab, levels)
+    temps = np.array([0.25, 0.7, 1.0, 1.9, 5.0, 0.4], np.float32)[: len(top_n)]
+    ref = LO.compute_log_probabilities_ragged(off, logits, ntl, tokens, sampled, list(top_n),
+                                              list(echo), levels=levels, batch_temperature=temps)
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split=split, levels=levels,
+        temperature=temps)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_off, ref[2])
+    assert np.array_equal(ids.cpu().numpy(), ref[1]), "ids"
+    _assert_close_rel(lp.cpu().numpy(), ref[0], f"temperature levels={levels} split={split}")
+
+
+def test_temperature_decode_shape(R):
+    """The decode workload (direct rows) at T = 0.6 and T = 1.5."""
+    c = gen.decode_peaked()
+    ntl = gen.host_logits(c)
+    for T in (0.6, 1.5):
+        log(f"decode_peaked temperature={T}")
+        ref = LO.compute_log_probabilities_ragged(c.offsets, None, ntl, c.tokens, c.sampled,
+                                                  list(c.top_n), list(c.echo),
+                                                  batch_temperature=[T] * c.batch)
+        lp, ids, _ = R.compute_log_probabilities_ragged(c.offsets, None, _dev(ntl), c.tokens,
+                                                        c.sampled, c.top_n, c.echo, temperature=T)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ref[1])
+        _assert_close_rel(lp.cpu().numpy(), ref[0], f"decode T={T}")
+
+
 def _same_value(a, b):
     return (np.isnan(a) and np.isnan(b)) or a == b or abs(a - b) <= 1e-5
 

@@ -29,20 +29,20 @@ def _rank_negzero_below_poszero(row_f32):
     return np.argsort(-key, kind="stable")
 
 
-def _lsm_no_shift(row):
-    x = np.asarray(row, dtype=np.float64)
+def _lsm_no_shift(row, temperature=1.0):
+    x = np.asarray(row, dtype=np.float64) / temperature
     with np.errstate(invalid="ignore", over="ignore"):
         lse = np.log(np.sum(np.exp(x)))
         return x - lse, float(lse)
 
 
-def _lsm_wrong_sign(row):
-    lp, lse = _orig["log_softmax_f64"](row)
+def _lsm_wrong_sign(row, temperature=1.0):
+    lp, lse = _orig["log_softmax_f64"](row, temperature)
     return -lp, lse
 
 
-def _lsm_dropped_max(row):
-    x = np.asarray(row, dtype=np.float64)
+def _lsm_dropped_max(row, temperature=1.0):
+    x = np.asarray(row, dtype=np.float64) / temperature
     m = np.max(x)
     with np.errstate(invalid="ignore"):
         lse = np.log(np.sum(np.exp(x - m)))
@@ -80,23 +80,23 @@ def _counts_swapped(off, echo):
     return _orig["output_counts_and_offsets"](off, [not bool(e) for e in echo])
 
 
-def _row_pad_zero(row, chosen, top_n, cols):
-    lp, ids = _orig["compute_row"](row, chosen, top_n, cols)
+def _row_pad_zero(row, chosen, top_n, cols, temperature=1.0):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature)
     ids = ids.copy()
     ids[ids == LO.PAD_ID] = 0
     return lp, ids
 
 
-def _row_last_col_top1(row, chosen, top_n, cols):
-    lp, ids = _orig["compute_row"](row, chosen, top_n, cols)
+def _row_last_col_top1(row, chosen, top_n, cols, temperature=1.0):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature)
     if top_n > 0:
         lp = lp.copy()
         lp[cols - 1] = lp[0]
     return lp, ids
 
 
-def _row_ignores_top_n(row, chosen, top_n, cols):
-    return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols)
+def _row_ignores_top_n(row, chosen, top_n, cols, temperature=1.0):
+    return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols, temperature)
 
 
 def _top_no_overwrite(lp_row, id_row, top_n, vocab):
@@ -118,6 +118,14 @@ def _top_truncate_before_sort(lp_row, id_row, top_n, vocab):
     return out
 
 
+def _lsm_temperature_multiplies(row, temperature=1.0):
+    x = np.asarray(row, dtype=np.float64) * np.float64(temperature)
+    m = np.max(x)
+    with np.errstate(invalid="ignore"):
+        lse = m + np.log(np.sum(np.exp(x - m)))
+        return x - lse, float(lse)
+
+
 def _cap_equals_columns(levels):
     # plausible slip: forgetting the column reserved for the chosen token
     return 2 ** levels if levels > 0 else 1
@@ -128,6 +136,7 @@ def _columns_two_to_levels_plus_one(levels):
 
 
 MUTANTS = {
+    "temperature_multiplies": ("log_softmax_f64", _lsm_temperature_multiplies),
     "top_no_overwrite": ("compute_top", _top_no_overwrite),
     "top_truncate_before_sort": ("compute_top", _top_truncate_before_sort),
     "cap_equals_columns": ("max_top_n", _cap_equals_columns),
@@ -164,6 +173,7 @@ def _run_all_pins():
     P.pin_levels_zero()
     P.pin_assembly_hand_examples()
     P.pin_assembly_worked_example()
+    P.pin_temperature()
 
 
 def test_pins_pass_on_true_oracle():

@@ -85,3 +85,7 @@ def test_assembly_hand_examples():
 
 def test_assembly_worked_example():
     P.pin_assembly_worked_example()
+
+
+def test_temperature():
+    P.pin_temperature()

@@ -81,7 +81,7 @@ typedef struct lp_plan_info {
                                  request echoes with full logits, or none has full logits,
                                  and every top_n > 0): the kernel then addresses rows
                                  without waiting for their descriptors */
-    uint32_t reserved;        /* 0 */
+    uint32_t record_words;    /* 8-byte words of one partial record: 2^levels + 1 */
 } lp_plan_info;
 
 /*
@@ -218,6 +218,45 @@ lp_status lp_compute_ragged(lp_plan *plan, const float *logits,
  */
 lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_t *ids,
                              uint32_t *out_tokens, float *out_logprobs, uint32_t *out_counts);
+
+/*
+ * Vocabulary-sharded logits (a tensor-parallel LM head, where each GPU holds
+ * the logits of one vocabulary range: the "TP worker" of [SGL] §output 从
+ * forward() 到响应对象的完整路径).  Each shard reduces its columns of every
+ * read row to one partial record; after the records of all shards are
+ * gathered, lp_merge_shards writes the rows -- the same results as the
+ * unsharded computation over the whole vocabulary (ids bit for bit).
+ *
+ * A record is record_words (lp_plan_info) 8-byte words: (max, scaled sum)
+ * of the shard's part of the row, its best 2^levels - 1 order keys with
+ * global token ids, and the chosen token's logit with a flag set when the
+ * shard holds the chosen token.  Record words are opaque to the caller.
+ *
+ * lp_shard_records -- records of shard [vocab_begin, vocab_begin +
+ * shard_vocab) of the plan's vocabulary.
+ *   shard_logits / shard_next_token_logits  device, rows of shard_vocab fp32
+ *     (the shard's columns only; row layout and which one is read as in
+ *     lp_launch_ragged)
+ *   records    device out, R * record_words 8-byte words, row-major by output
+ *              row (rows of top_n == 0 requests are not written)
+ *   workspace  as for lp_launch_ragged, after lp_stage_ragged
+ * LP_ERR_SHAPE if the range does not fit in [0, V); one kernel launch.
+ *
+ * lp_merge_shards -- merges, for every output row, num_shards records laid
+ * out shard-major: record (s, o) at word (s * R + o) * record_words of
+ * `records` (device).  The shards must cover [0, V) once each; a row whose
+ * chosen token no shard holds gets a NaN last column.  LP_ERR_UNSUPPORTED if
+ * num_shards is not in 1..64 or num_shards * (2^levels - 1) > 1024.  One
+ * kernel launch; outputs as for lp_launch_ragged.
+ */
+lp_status lp_shard_records(const lp_plan *plan, uint32_t vocab_begin, uint32_t shard_vocab,
+                           const float *shard_logits, const float *shard_next_token_logits,
+                           uint64_t *records, void *workspace, uint64_t workspace_bytes,
+                           void *stream);
+
+lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64_t *records,
+                          float *out_logprobs, uint32_t *out_token_ids, void *workspace,
+                          uint64_t workspace_bytes, void *stream);
 
 /* Frees the plan.  Waits for a pending descriptor copy from its staging
  * buffer first.  NULL is a no-op. */

@@ -27,7 +27,8 @@ STATUS_NAMES = {
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
     "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_descriptors", "lp_assemble_ragged",
-    "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_plan_destroy",
+    "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_shard_records",
+    "lp_merge_shards", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
 
@@ -56,7 +57,7 @@ class PlanInfo(ctypes.Structure):
         ("split", ctypes.c_uint32), ("has_logits", ctypes.c_uint32),
         ("waves", ctypes.c_uint32), ("depth", ctypes.c_uint32),
         ("workspace_bytes", ctypes.c_uint64),
-        ("direct_rows", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("direct_rows", ctypes.c_uint32), ("record_words", ctypes.c_uint32),
     ]
 
 
@@ -88,6 +89,8 @@ def load():
     lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
     lib.lp_compute_ragged.argtypes = [vp, vp, vp, P(u32), P(u32), vp, vp, vp, u64, vp]
+    lib.lp_shard_records.argtypes = [vp, u32, u32, vp, vp, vp, vp, u64, vp]
+    lib.lp_merge_shards.argtypes = [vp, u32, vp, vp, vp, vp, u64, vp]
     lib.lp_plan_destroy.argtypes = [vp]
     lib.lp_plan_destroy.restype = None
     lib.lp_status_string.argtypes = [ctypes.c_int]
@@ -97,7 +100,7 @@ def load():
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
                  "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_temperature",
                  "lp_plan_descriptors", "lp_assemble_ragged",
-                 "lp_stage_ragged", "lp_launch_ragged",
+                 "lp_stage_ragged", "lp_launch_ragged", "lp_shard_records", "lp_merge_shards",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -271,6 +274,28 @@ class Plan:
                                            _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
                                            _dev_ptr(workspace), _nbytes(workspace),
                                            _stream_ptr(stream)), "lp_compute_ragged")
+
+    def shard_records(self, vocab_begin: int, shard_logits, shard_next_token_logits, records,
+                      workspace, stream=None):
+        """lp_shard_records: one record per output row for the vocabulary
+        shard [vocab_begin, vocab_begin + width) whose logits (rows of
+        ``width`` fp32, the shard's columns only) are given; ``records`` is a
+        device tensor of out_rows * record_words 8-byte words."""
+        t = shard_logits if self.has_logits else shard_next_token_logits
+        width = int(t.shape[1])
+        _check(self._lib.lp_shard_records(self._h, int(vocab_begin), width, _dev_ptr(shard_logits),
+                                          _dev_ptr(shard_next_token_logits), _dev_ptr(records),
+                                          _dev_ptr(workspace), _nbytes(workspace),
+                                          _stream_ptr(stream)), "lp_shard_records")
+
+    def merge_shards(self, num_shards: int, records, out_logprobs, out_token_ids, workspace,
+                     stream=None):
+        """lp_merge_shards over records laid out (num_shards, out_rows,
+        record_words) in a device tensor."""
+        _check(self._lib.lp_merge_shards(self._h, int(num_shards), _dev_ptr(records),
+                                         _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
+                                         _dev_ptr(workspace), _nbytes(workspace),
+                                         _stream_ptr(stream)), "lp_merge_shards")
 
     def close(self):
         if self._h is not None and self._h.value:

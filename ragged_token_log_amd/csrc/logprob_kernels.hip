@@ -322,16 +322,25 @@ __device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t k, int l
 // ------------------------------------------------------------------ row kernel
 
 struct RowArgs {
-    const float *src;          // logits the op reads (rows of V floats)
-    uint32_t vocab;
+    const float *src;          // logits the op reads: rows of row_len floats
+    uint32_t row_len;          // V, or the width of a vocabulary shard
+    uint32_t id_base;          // token id of a row's first element (a shard's first id)
     uint32_t split;            // segments per row
     uint32_t seg_len;          // elements per segment (multiple of 4)
     uint32_t out_rows;
+    uint32_t records;          // 0: write the rows; 1: one record per (row, segment)
+    uint64_t rec_row_stride;   // 8-byte words between two rows' records
+    uint64_t rec_seg_stride;   // words between a row's segment records
     const RowDesc *desc;
-    float *out_lp;             // split == 1: (R, 8)
-    uint32_t *out_id;          // split == 1: (R, 8)
-    uint64_t *partials;        // split > 1: (R, split) records of slots + 1 words
+    float *out_lp;             // rows: (R, kK + 1)
+    uint32_t *out_id;          // rows: (R, kK + 1)
+    uint64_t *rec;             // records of kK + 2 words (see below)
 };
+
+// A partial record, in 8-byte words: word 0 holds the segment's max and
+// scaled sum (two floats), words 1..kK its best keys (descending, 0 past the
+// ones it has), word kK + 1 the chosen token's logit (a float) and a flag
+// set when the chosen token lies in the segment.
 
 // log p = (x - M) / temperature - ln S for a row whose max is M and whose
 // S = sum of e^((x - M) / temperature): the subtraction comes first, so a
@@ -399,12 +408,13 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t seg = blockIdx.x - o * a.split;
     const RowDesc d = load_desc_uniform(a.desc, o);
 
-    if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads split rows)
-        if (a.split == 1 && wave == 0) write_padding<kK>(a.out_lp, a.out_id, o, lane);
+    if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads record rows)
+        if (!a.records && wave == 0) write_padding<kK>(a.out_lp, a.out_id, o, lane);
         return;
     }
 
-    const uint32_t V = a.vocab;
+    const uint32_t V = a.row_len;
+    const uint32_t gid = a.id_base;  // global id = gid + position in the row
     const float *row = a.src + uint64_t(kDirect ? o : d.src_row) * V;
     const uint64_t seg_start = uint64_t(seg) * a.seg_len;
     const uint32_t v0 = seg_start < V ? uint32_t(seg_start) : V;
@@ -487,7 +497,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
 
     // The filter value for chunk ch against the bound as it stands.
     auto chunk_tv = [&](uint32_t ch) __attribute__((always_inline)) {
-        const uint32_t first = a0 + ch * uint32_t(kChunkF4 * 4);
+        const uint32_t first = gid + a0 + ch * uint32_t(kChunkF4 * 4);
         return key_id(T) < first ? strict_value(T) : threshold_value(T);
     };
 
@@ -512,7 +522,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         const f32x16 xv = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-        const uint32_t lane_id = a0 + ch * uint32_t(kChunkF4 * 4) + 4u * uint32_t(lane);
+        const uint32_t lane_id = gid + a0 + ch * uint32_t(kChunkF4 * 4) + 4u * uint32_t(lane);
         while (cols != 0) {
             const uint32_t j = uint32_t(__builtin_ctz(cols));
             cols &= cols - 1;
@@ -534,7 +544,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const bool e1_ok = uint32_t(tid) < nh + ntr;
     const uint32_t e1 = uint32_t(tid) < nh ? v0 + uint32_t(tid) : a0 + 4u * nf4 + (uint32_t(tid) - nh);
     const float xr1 = row[e1_ok ? e1 : 0u];
-    const float x_chosen = row[(a.split == 1 && lane == kK) ? d.chosen : 0u];
+    // the chosen token's logit, from the segment that holds it
+    const uint32_t chosen_local = d.chosen - gid;
+    const bool owns_chosen = d.chosen >= gid && chosen_local >= v0 && chosen_local < v1;
+    const float x_chosen = row[(owns_chosen && lane == kK) ? chosen_local : 0u];
     // LDS set-up (before any data can have arrived, so the barrier costs only
     // the spread of the waves' start)
     s_lmax[tid] = -INFINITY;
@@ -605,11 +618,11 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         T = umax64(T, uniform64(lds_load_relaxed(&s_T)));
         const float tv = threshold_value(T);
         if (__ballot(cm >= tv) != 0) {
-            const uint32_t id4 = a0 + 4u * rest4;
+            const uint32_t id4 = gid + a0 + 4u * rest4;
             const float tv4 = rest4_ok ? tv : INFINITY;
 #pragma unroll
             for (int q = 0; q < 4; ++q) column(f4_get(x4, q), id4 + uint32_t(q), tv4);
-            column(x1, e1, e1_ok ? tv : INFINITY);
+            column(x1, gid + e1, e1_ok ? tv : INFINITY);
         }
     }
 
@@ -642,34 +655,39 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     }
     wave_lse(M, S, c);
 
-    if (a.split == 1) {
+    if (!a.records) {
         write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, inv_temp, x_chosen, d.chosen);
     } else {
-        uint64_t *rec = a.partials + (uint64_t(o) * a.split + seg) * uint64_t(kK + 1);
+        uint64_t *rec = a.rec + uint64_t(o) * a.rec_row_stride + uint64_t(seg) * a.rec_seg_stride;
         if (lane == 0) {
             reinterpret_cast<float *>(rec)[0] = M;
             reinterpret_cast<float *>(rec)[1] = S;
         }
         if (lane < kK) rec[1 + lane] = top;
+        if (lane == kK) {
+            reinterpret_cast<float *>(rec + kK + 1)[0] = owns_chosen ? x_chosen : 0.0f;
+            reinterpret_cast<uint32_t *>(rec + kK + 1)[1] = owns_chosen ? 1u : 0u;
+        }
     }
 }
 
 // ------------------------------------------------------------------ merge kernel
 
 struct MergeArgs {
-    const float *src;
-    uint32_t vocab;
-    uint32_t split;
+    uint32_t nseg;             // records per row (segments, or vocabulary shards)
     uint32_t out_rows;
+    uint64_t rec_row_stride;   // 8-byte words between two rows' records
+    uint64_t rec_seg_stride;   // words between a row's records
     const RowDesc *desc;
-    const uint64_t *partials;
+    const uint64_t *rec;
     float *out_lp;
     uint32_t *out_id;
 };
 
-// Split variant, second launch: one wave per output row combines the row's
-// segment records in segment order, then writes the row.  split * kK <=
-// kMaxMergeKeys, so kPer keys per lane hold them.
+// Merges each row's records, one wave per output row: the (max, sum) pairs
+// in record order, the best kK of all their keys, the chosen token's logit
+// from the record that holds it (NaN if none does); then writes the row.
+// nseg * kK <= kMaxMergeKeys, so kPer keys per lane hold them.
 template <int kK>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     constexpr int kPer = int((kMaxMergeKeys + kWave - 1) / kWave) < (int(kMaxSplit) * kK + kWave - 1) / kWave
@@ -683,23 +701,27 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         write_padding<kK>(a.out_lp, a.out_id, o, lane);
         return;
     }
-    const float *row = a.src + uint64_t(d.src_row) * a.vocab;
-    const float x_chosen = lane == kK ? row[d.chosen] : 0.0f;
-    const uint64_t *recs = a.partials + uint64_t(o) * a.split * uint64_t(kK + 1);
-    float m = -INFINITY, s = 0.0f;
-    if (uint32_t(lane) < a.split) {
-        const float *ms = reinterpret_cast<const float *>(recs + uint64_t(lane) * (kK + 1));
+    const uint64_t *recs = a.rec + uint64_t(o) * a.rec_row_stride;
+    float m = -INFINITY, s = 0.0f, xc = 0.0f;
+    bool owner = false;
+    if (uint32_t(lane) < a.nseg) {
+        const uint64_t *r = recs + uint64_t(lane) * a.rec_seg_stride;
+        const float *ms = reinterpret_cast<const float *>(r);
         m = ms[0];
         s = ms[1];
+        xc = reinterpret_cast<const float *>(r + kK + 1)[0];
+        owner = reinterpret_cast<const uint32_t *>(r + kK + 1)[1] != 0;
     }
+    const uint64_t own = __ballot(owner);
+    const float x_chosen = own != 0 ? readlane_f32(xc, __builtin_ctzll(own)) : __uint_as_float(0x7FC00000u);
     const float inv_temp = __uint_as_float(d.inv_temp_bits);
     wave_lse(m, s, kLog2e * inv_temp);
-    const uint32_t nkeys = a.split * uint32_t(kK);
+    const uint32_t nkeys = a.nseg * uint32_t(kK);
     uint64_t e[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < nkeys ? recs[(idx / kK) * (kK + 1) + 1 + idx % kK] : 0ull;
+        e[i] = idx < nkeys ? recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK] : 0ull;
     }
     uint32_t found;
     const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
@@ -770,39 +792,69 @@ static void launch_shape(bool direct, dim3 grid, hipStream_t s, const dev::RowAr
     else hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, false>), grid, dim3(kWaves * 64), 0, s, ra);
 }
 
+// What one call enqueues: the row kernel (rows or records), the merge
+// kernel, or both.
+enum class Launch { kRows, kRecords, kMerge, kRecordsThenMerge };
+
 template <int kK>
-static void launch_rows(const lp_plan &p, dim3 grid, hipStream_t s, const dev::RowArgs &ra,
-                        const dev::MergeArgs &ma) {
-    const bool deep = p.depth == 2, direct = p.direct_rows != 0;
-    if (p.waves == 16) {
-        if (deep) launch_shape<kK, 16, 2>(direct, grid, s, ra);
-        else launch_shape<kK, 16, 1>(direct, grid, s, ra);
-    } else if (p.waves == 8) {
-        if (deep) launch_shape<kK, 8, 2>(direct, grid, s, ra);
-        else launch_shape<kK, 8, 1>(direct, grid, s, ra);
-    } else {
-        if (deep) launch_shape<kK, 4, 2>(direct, grid, s, ra);
-        else launch_shape<kK, 4, 1>(direct, grid, s, ra);
+static void launch_k(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
+                     const dev::RowArgs &ra, const dev::MergeArgs &ma) {
+    if (what != Launch::kMerge) {
+        const bool deep = p.depth == 2, direct = p.direct_rows != 0;
+        if (p.waves == 16) {
+            if (deep) launch_shape<kK, 16, 2>(direct, grid, s, ra);
+            else launch_shape<kK, 16, 1>(direct, grid, s, ra);
+        } else if (p.waves == 8) {
+            if (deep) launch_shape<kK, 8, 2>(direct, grid, s, ra);
+            else launch_shape<kK, 8, 1>(direct, grid, s, ra);
+        } else {
+            if (deep) launch_shape<kK, 4, 2>(direct, grid, s, ra);
+            else launch_shape<kK, 4, 1>(direct, grid, s, ra);
+        }
     }
-    if (p.split > 1) {
+    if (what == Launch::kMerge || what == Launch::kRecordsThenMerge) {
         const uint32_t mblocks = static_cast<uint32_t>((p.out_rows + 3) / 4);
         hipLaunchKernelGGL(dev::merge_kernel<kK>, dim3(mblocks), dim3(256), 0, s, ma);
     }
 }
 
-// The row kernel (and the merge kernel for split plans) for the plan's slot
-// count; false if the plan has none the library is built for.
-static bool launch_for_slots(const lp_plan &p, dim3 grid, hipStream_t s, const dev::RowArgs &ra,
-                             const dev::MergeArgs &ma) {
+// The kernels for the plan's slot count; false if the library is not built
+// for it.
+static bool launch_for_slots(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
+                             const dev::RowArgs &ra, const dev::MergeArgs &ma) {
     switch (p.slots) {
-        case 1: launch_rows<1>(p, grid, s, ra, ma); return true;
-        case 3: launch_rows<3>(p, grid, s, ra, ma); return true;
-        case 7: launch_rows<7>(p, grid, s, ra, ma); return true;
-        case 15: launch_rows<15>(p, grid, s, ra, ma); return true;
-        case 31: launch_rows<31>(p, grid, s, ra, ma); return true;
-        case 63: launch_rows<63>(p, grid, s, ra, ma); return true;
+        case 1: launch_k<1>(p, what, grid, s, ra, ma); return true;
+        case 3: launch_k<3>(p, what, grid, s, ra, ma); return true;
+        case 7: launch_k<7>(p, what, grid, s, ra, ma); return true;
+        case 15: launch_k<15>(p, what, grid, s, ra, ma); return true;
+        case 31: launch_k<31>(p, what, grid, s, ra, ma); return true;
+        case 63: launch_k<63>(p, what, grid, s, ra, ma); return true;
         default: return false;
     }
+}
+
+// Plans that read no row: every entry of the (R, C) outputs is padding.
+static lp_status launch_padding(const lp_plan &p, float *out_lp, uint32_t *out_id, hipStream_t s) {
+    const uint64_t n = p.out_rows * p.columns;
+    uint64_t g = (n + 255) / 256;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(dev::pad_kernel, dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, out_lp,
+                       out_id, n);
+    LP_HIP_TRY(hipGetLastError());
+    return LP_OK;
+}
+
+static dev::RowArgs row_args(const lp_plan &p, const float *src, uint32_t row_len, uint32_t id_base,
+                             uint32_t split, const void *workspace) {
+    dev::RowArgs ra{};
+    ra.src = src;
+    ra.row_len = row_len;
+    ra.id_base = id_base;
+    ra.split = split;
+    ra.seg_len = static_cast<uint32_t>(segment_length(row_len, split));
+    ra.out_rows = static_cast<uint32_t>(p.out_rows);
+    ra.desc = static_cast<const RowDesc *>(workspace);
+    return ra;
 }
 
 static lp_status check_workspace(const lp_plan *plan, const void *ws, uint64_t ws_bytes) {
@@ -861,39 +913,27 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     if (blocks * waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (plan->read_rows == 0) {   // every row padding-only; no logits read
-        const uint64_t n = plan->out_rows * plan->columns;
-        uint64_t g = (n + 255) / 256;
-        if (g > 4096) g = 4096;
-        hipLaunchKernelGGL(lp::dev::pad_kernel, dim3(static_cast<uint32_t>(g)), dim3(256), 0, s,
-                           out_logprobs, out_token_ids, n);
-        LP_HIP_TRY(hipGetLastError());
-        return LP_OK;
-    }
-    char *ws = static_cast<char *>(workspace);
-    auto *desc = reinterpret_cast<const lp::RowDesc *>(ws);
-    auto *partials = reinterpret_cast<uint64_t *>(ws + plan->desc_bytes);
-    lp::dev::RowArgs ra;
-    ra.src = src;
-    ra.vocab = plan->vocab;
-    ra.split = plan->split;
-    ra.seg_len = static_cast<uint32_t>(lp::segment_length(plan->vocab, plan->split));
-    ra.out_rows = static_cast<uint32_t>(plan->out_rows);
-    ra.desc = desc;
+    if (plan->read_rows == 0) return lp::launch_padding(*plan, out_logprobs, out_token_ids, s);
+    const uint64_t words = plan->slots + 2;   // one record
+    lp::dev::RowArgs ra = lp::row_args(*plan, src, plan->vocab, 0, plan->split, workspace);
     ra.out_lp = out_logprobs;
     ra.out_id = out_token_ids;
-    ra.partials = partials;
-    lp::dev::MergeArgs ma;
-    ma.src = src;
-    ma.vocab = plan->vocab;
-    ma.split = plan->split;
+    ra.records = plan->split > 1 ? 1u : 0u;
+    ra.rec_row_stride = plan->split * words;
+    ra.rec_seg_stride = words;
+    ra.rec = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + plan->desc_bytes);
+    lp::dev::MergeArgs ma{};
+    ma.nseg = plan->split;
     ma.out_rows = static_cast<uint32_t>(plan->out_rows);
-    ma.desc = desc;
-    ma.partials = partials;
+    ma.rec_row_stride = ra.rec_row_stride;
+    ma.rec_seg_stride = ra.rec_seg_stride;
+    ma.desc = ra.desc;
+    ma.rec = ra.rec;
     ma.out_lp = out_logprobs;
     ma.out_id = out_token_ids;
     const dim3 grid(static_cast<uint32_t>(blocks));
-    if (!lp::launch_for_slots(*plan, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    const lp::Launch what = plan->split > 1 ? lp::Launch::kRecordsThenMerge : lp::Launch::kRows;
+    if (!lp::launch_for_slots(*plan, what, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }
@@ -906,6 +946,62 @@ lp_status lp_compute_ragged(lp_plan *plan, const float *logits, const float *nex
     if (st != LP_OK) return st;
     return lp_launch_ragged(plan, logits, next_token_logits, out_logprobs, out_token_ids,
                             workspace, workspace_bytes, stream);
+}
+
+lp_status lp_shard_records(const lp_plan *plan, uint32_t vocab_begin, uint32_t shard_vocab,
+                           const float *shard_logits, const float *shard_next_token_logits,
+                           uint64_t *records, void *workspace, uint64_t workspace_bytes,
+                           void *stream) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (shard_vocab < 1 || uint64_t(vocab_begin) + shard_vocab > plan->vocab) return LP_ERR_SHAPE;
+    if (shard_vocab > lp::kMaxSegment) return LP_ERR_UNSUPPORTED;
+    if (plan->out_rows == 0 || plan->read_rows == 0) return LP_OK;
+    const float *src = plan->has_logits ? shard_logits : shard_next_token_logits;
+    if (src == nullptr || records == nullptr) return LP_ERR_NULL_ARG;
+    lp_status st = lp::check_workspace(plan, workspace, workspace_bytes);
+    if (st != LP_OK) return st;
+    if (plan->out_rows * plan->waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    lp::dev::RowArgs ra = lp::row_args(*plan, src, shard_vocab, vocab_begin, 1, workspace);
+    ra.records = 1;
+    ra.rec_row_stride = plan->slots + 2;
+    ra.rec_seg_stride = 0;
+    ra.rec = records;
+    lp::dev::MergeArgs ma{};
+    const dim3 grid(static_cast<uint32_t>(plan->out_rows));
+    if (!lp::launch_for_slots(*plan, lp::Launch::kRecords, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    LP_HIP_TRY(hipGetLastError());
+    return LP_OK;
+}
+
+lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64_t *records,
+                          float *out_logprobs, uint32_t *out_token_ids, void *workspace,
+                          uint64_t workspace_bytes, void *stream) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (num_shards < 1 || num_shards > lp::kMaxSplit ||
+        uint64_t(num_shards) * plan->slots > lp::kMaxMergeKeys)
+        return LP_ERR_UNSUPPORTED;
+    if (plan->out_rows == 0) return LP_OK;
+    if (out_logprobs == nullptr || out_token_ids == nullptr) return LP_ERR_NULL_ARG;
+    lp_status st = lp::check_workspace(plan, workspace, workspace_bytes);
+    if (st != LP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->read_rows == 0) return lp::launch_padding(*plan, out_logprobs, out_token_ids, s);
+    if (records == nullptr) return LP_ERR_NULL_ARG;
+    const uint64_t words = plan->slots + 2;
+    lp::dev::RowArgs ra{};
+    lp::dev::MergeArgs ma{};
+    ma.nseg = num_shards;
+    ma.out_rows = static_cast<uint32_t>(plan->out_rows);
+    ma.rec_row_stride = words;
+    ma.rec_seg_stride = plan->out_rows * words;
+    ma.desc = static_cast<const lp::RowDesc *>(workspace);
+    ma.rec = records;
+    ma.out_lp = out_logprobs;
+    ma.out_id = out_token_ids;
+    if (!lp::launch_for_slots(*plan, lp::Launch::kMerge, dim3(1), s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    LP_HIP_TRY(hipGetLastError());
+    return LP_OK;
 }
 
 lp_status lp_bench_stream_read(const float *x, uint64_t n, float *partial_out, uint32_t *grid_out,

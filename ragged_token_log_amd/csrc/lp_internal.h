@@ -48,11 +48,12 @@ struct RowDesc {
 };
 static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
 
-// Partial result of one (row, vocabulary segment) in the split variant, in
-// 8-byte words: word 0 holds the segment's running max and scaled sum (two
-// floats), words 1..slots its best order keys, descending.
+// Partial result of one (row, vocabulary segment or shard), in 8-byte words:
+// word 0 holds the segment's running max and scaled sum (two floats), words
+// 1..slots its best order keys, descending, word slots + 1 the chosen
+// token's logit and a flag set when the segment holds that token.
 // Workspace layout: [R descriptors, padded to 256 B][R x split records].
-inline uint64_t partial_record_bytes(uint32_t slots) { return 8ull * (uint64_t(slots) + 1); }
+inline uint64_t partial_record_bytes(uint32_t slots) { return 8ull * (uint64_t(slots) + 2); }
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -78,7 +79,7 @@ struct lp_plan {
     uint32_t depth = 2;              // chunks in flight per wave: 1 or 2
     uint32_t direct_rows = 0;        // 1: output row o reads logits row o (all top_n > 0)
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
-    uint64_t partial_bytes = 0;      // R * split * 8 (slots + 1) when split > 1
+    uint64_t partial_bytes = 0;      // R * split * 8 (slots + 2) when split > 1
     uint64_t workspace_bytes = 0;
     // pinned staging for the descriptor upload (allocated on first stage)
     void *staging = nullptr;

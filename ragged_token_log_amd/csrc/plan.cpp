@@ -208,7 +208,7 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info) {
     info->has_logits = plan->has_logits;
     info->workspace_bytes = plan->workspace_bytes;
     info->direct_rows = plan->direct_rows;
-    info->reserved = 0;
+    info->record_words = plan->slots + 2;
     return LP_OK;
 }
 

@@ -114,7 +114,8 @@ def test_levels_columns_and_caps(levels):
     limit = 64 if cap == 0 else min(64, 1024 // cap)
     wide.set_split(limit)
     _expect("LP_ERR_UNSUPPORTED", lambda: wide.set_split(limit + 1))
-    assert wide.workspace_bytes == 256 + limit * 8 * (cap + 1)
+    assert wide.workspace_bytes == 256 + limit * 8 * (cap + 2)
+    assert wide.info()["record_words"] == cap + 2
 
 
 def test_plan_on_named_workloads():
@@ -135,7 +136,8 @@ def test_split_and_workspace():
     s = plan.split
     assert s > 1                      # two rows cannot fill the chip
     ws = plan.workspace_bytes
-    assert ws == 256 + 2 * s * 64
+    assert ws == 256 + 2 * s * 72                  # records of 9 words at levels 3
+    assert plan.info()["record_words"] == 9
     plan.set_split(1)
     assert plan.split == 1 and plan.workspace_bytes == 256
     with pytest.raises(R.LogprobError) as e:
@@ -164,7 +166,7 @@ def test_segments_stay_within_the_streamed_range():
     wide = R.Plan(np.arange(many + 1, dtype=np.uint32), np.zeros(many, bool), np.full(many, 1),
                   (1 << 31) + 1, False)
     assert wide.split == 9
-    assert wide.workspace_bytes == ((many * 16 + 255) // 256) * 256 + many * 9 * 64
+    assert wide.workspace_bytes == ((many * 16 + 255) // 256) * 256 + many * 9 * 72
     with pytest.raises(R.LogprobError) as e:
         wide.set_split(8)
     assert e.value.name == "LP_ERR_UNSUPPORTED"

@@ -246,6 +246,63 @@ def test_temperature_decode_shape(R):
         _assert_close_rel(lp.cpu().numpy(), ref[0], f"decode T={T}")
 
 
+def _shard_bounds(vocab, n_shards, rng):
+    """Uneven vocabulary ranges covering [0, vocab) once each."""
+    cuts = sorted(rng.choice(np.arange(1, vocab), size=n_shards - 1, replace=False).tolist())
+    b = [0] + cuts + [vocab]
+    return list(zip(b[:-1], b[1:]))
+
+
+def _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds):
+    dev = torch.device("cuda")
+    has_logits = logits is not None
+    plan = R.Plan(off, echo, top_n, ntl.shape[1], has_logits, levels=levels)
+    words = plan.info()["record_words"]
+    lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+    stream = torch.cuda.current_stream()
+    plan.stage(tokens, sampled, ws, stream)
+    records = torch.zeros((len(bounds), plan.out_rows, words), dtype=torch.int64, device=dev)
+    for k, (b, e) in enumerate(bounds):
+        sl = _dev(logits[:, b:e]) if has_logits else None
+        sn = _dev(ntl[:, b:e])
+        plan.shard_records(b, sl, sn, records[k], ws, stream)
+    plan.merge_shards(len(bounds), records, lp, ids, ws, stream)
+    torch.cuda.synchronize()
+    out = lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off.copy()
+    plan.close()
+    return out
+
+
+@pytest.mark.parametrize("levels", [1, 3, 5])
+@pytest.mark.parametrize("n_shards", [1, 2, 3, 8])
+def test_vocab_shards(R, levels, n_shards):
+    """Vocabulary-sharded logits: per-shard records (global ids), gathered
+    and merged, give the unsharded results."""
+    vocab = 40001
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(11 * n_shards + levels, vocab,
+                                                                   levels)
+    bounds = _shard_bounds(vocab, n_shards, np.random.default_rng(n_shards))
+    log(f"vocab shards levels={levels} shards={bounds}")
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+    got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds)
+    assert_parity(*got, ref, f"shards levels={levels} n={n_shards}")
+    whole = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
+                        levels=levels)
+    assert np.array_equal(got[1], whole[1])
+
+
+def test_vocab_shards_decode_tp8(R):
+    """The decode workload's next-token rows cut into 8 equal vocabulary
+    shards, the shape of an 8-way tensor-parallel LM head."""
+    c = gen.decode_peaked()
+    ntl = gen.host_logits(c)
+    w = c.vocab // 8
+    bounds = [(k * w, (k + 1) * w if k < 7 else c.vocab) for k in range(8)]
+    ref = oracle(c.offsets, None, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    got = _run_sharded(R, c.offsets, None, ntl, c.tokens, c.sampled, c.top_n, c.echo, 3, bounds)
+    assert_parity(*got, ref, "decode tp8 shards")
+
+
 def _same_value(a, b):
     return (np.isnan(a) and np.isnan(b)) or a == b or abs(a - b) <= 1e-5
 

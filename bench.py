@@ -87,6 +87,9 @@ def main():
                     help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
     ap.add_argument("--top-n", type=int, default=None,
                     help="replace every nonzero top_n of the workload with this value")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="also time the vocabulary-sharded path: this many equal shards, "
+                         "each reduced to records, then merged (all on this GPU)")
     ap.add_argument("--temperature", type=float, default=None,
                     help="log_softmax(logits / T) for every request")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,6 +256,10 @@ def main():
                                "note": "lp_assemble_ragged on the host, one thread; copy back "
                                        "of the (R, C) outputs timed separately"}
 
+    if args.shards:
+        result["shards"] = bench_shards(args, case, plan, info, copies, n_copies, torch, dev,
+                                        stream, ws)
+
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
         a = torch.ones(n, device=dev)
@@ -271,6 +278,51 @@ def main():
         result["cpu_baseline"] = cpu_baseline(case, base, ntl, cols=int(info["columns"]))
 
     print(json.dumps(result), flush=True)
+
+
+def bench_shards(args, case, plan, info, copies, n_copies, torch, dev, stream, ws):
+    """The vocabulary-sharded path on one GPU: each of S equal column ranges
+    of the logits as its own contiguous tensor (what one tensor-parallel rank
+    holds), reduced to records; then the merge.  Times one shard's record
+    kernel (what each rank runs) and the merge, each over the timed steps."""
+    S = args.shards
+    V = case.vocab
+    bounds = [(k * V // S, (k + 1) * V // S) for k in range(S)]
+    src_copies = copies[: max(1, min(n_copies, 4))]
+    shards = [[c[:, b:e].contiguous() for (b, e) in bounds] for c in src_copies]
+    words = int(info["record_words"])
+    rec = torch.empty((S, int(info["out_rows"]), words), dtype=torch.int64, device=dev)
+    lp = torch.empty((int(info["out_rows"]), int(info["columns"])), dtype=torch.float32, device=dev)
+    ids = torch.empty(lp.shape, dtype=torch.uint32, device=dev)
+    torch.cuda.synchronize()
+
+    def records(i, k):
+        t = shards[i % len(shards)][k]
+        plan.shard_records(bounds[k][0], t if case.has_logits else None,
+                           None if case.has_logits else t, rec[k], ws, stream)
+
+    steps = 50
+    for i in range(3):
+        records(i, 0)
+    plan.merge_shards(S, rec, lp, ids, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for i in range(steps):
+        records(i, i % S)
+    ev[1].record(stream)
+    for i in range(steps):
+        plan.merge_shards(S, rec, lp, ids, ws, stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    rec_us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    merge_us = ev[1].elapsed_time(ev[2]) * 1e3 / steps
+    shard_bytes = int(info["read_rows"]) * 4 * (V // S) + int(info["out_rows"]) * (16 + 8 * words)
+    return {"n_shards": S, "record_kernel_us": rec_us, "merge_us": merge_us,
+            "record_kernel_gbs": shard_bytes / (rec_us * 1e-6) / 1e9,
+            "record_bytes_per_row": 8 * words,
+            "note": "one shard's record kernel (what each tensor-parallel rank runs on its "
+                    "columns) and the merge over all shards' records, each averaged over "
+                    f"{steps} back-to-back launches; shard copies rotated"}
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "ragged_token_log_amd", "csrc", "logprob_kernels.hip")

@@ -92,6 +92,8 @@ def main():
                          "each reduced to records, then merged (all on this GPU)")
     ap.add_argument("--temperature", type=float, default=None,
                     help="log_softmax(logits / T) for every request")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the plain-read probe over the same rows (the practical ceiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -256,6 +258,10 @@ def main():
                                "note": "lp_assemble_ragged on the host, one thread; copy back "
                                        "of the (R, C) outputs timed separately"}
 
+    if not args.no_probe and case.vocab % 4 == 0:
+        result["probe"] = bench_probe(copies, n_copies, read_rows, case.vocab, steps, stream, torch,
+                                      dev, R, alg_bytes, avg_launch_ms)
+
     if args.shards:
         result["shards"] = bench_shards(args, case, plan, info, copies, n_copies, torch, dev,
                                         stream, ws)
@@ -278,6 +284,29 @@ def main():
         result["cpu_baseline"] = cpu_baseline(case, base, ntl, cols=int(info["columns"]))
 
     print(json.dumps(result), flush=True)
+
+
+def bench_probe(copies, n_copies, rows, vocab, steps, stream, torch, dev, R, alg_bytes, kernel_ms):
+    """The plain streaming read (lp_bench_stream_read: one workgroup per row,
+    nontemporal 16-byte loads, a sum per row) over as many rows of the same
+    width, cycling through the same copies: what the memory system gives a
+    kernel that only reads these bytes."""
+    partial = torch.empty(max(rows, 1), dtype=torch.float32, device=dev)
+    launch = [R.binding.stream_read_launcher(c, rows, vocab, partial, stream) for c in copies]
+    for i in range(3):
+        launch[i % n_copies]()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        launch[i % n_copies]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    gbs = rows * vocab * 4 / (us * 1e-6) / 1e9
+    return {"us": us, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "kernel_time_over_probe": kernel_ms * 1e3 / us,
+            "note": "plain read of the same number of rows and row width, same copies cycled"}
 
 
 def bench_shards(args, case, plan, info, copies, n_copies, torch, dev, stream, ws):

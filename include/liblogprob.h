@@ -269,14 +269,16 @@ const char *lp_status_string(lp_status status);
 int lp_last_hip_error(void);
 
 /*
- * Measurement aid: a plain streaming read of n fp32 values (each read once,
- * 16-byte loads) that writes one partial sum per workgroup into
- * partial_out[grid].  It gives the practical HBM read ceiling on the same
- * bytes the log-probability kernels stream.  *grid_out receives the
- * workgroup count used (partial_out must hold that many floats: at most 65536).
+ * Measurement aid: a plain streaming read of `rows` rows of row_len fp32
+ * values (device, contiguous, 16-byte aligned, row_len a multiple of 4; each
+ * value read once with nontemporal 16-byte loads, one workgroup per row)
+ * that writes each row's sum to partial_out[rows] (device).  It gives the
+ * practical HBM read ceiling on the same bytes and row shape the
+ * log-probability kernels stream.  LP_ERR_UNSUPPORTED for a misaligned x or
+ * row_len.
  */
-lp_status lp_bench_stream_read(const float *x, uint64_t n, float *partial_out,
-                               uint32_t *grid_out, void *stream);
+lp_status lp_bench_stream_read(const float *x, uint32_t rows, uint32_t row_len, float *partial_out,
+                               void *stream);
 
 #ifdef __cplusplus
 }

@@ -96,7 +96,7 @@ def load():
     lib.lp_status_string.argtypes = [ctypes.c_int]
     lib.lp_status_string.restype = ctypes.c_char_p
     lib.lp_last_hip_error.argtypes = []
-    lib.lp_bench_stream_read.argtypes = [vp, u64, vp, P(u32), vp]
+    lib.lp_bench_stream_read.argtypes = [vp, u32, u32, vp, vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
                  "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_temperature",
                  "lp_plan_descriptors", "lp_assemble_ragged",
@@ -317,6 +317,18 @@ class Plan:
 
 def _nbytes(t) -> int:
     return 0 if t is None else int(t.numel() * t.element_size())
+
+
+def stream_read_launcher(x, rows: int, row_len: int, partial, stream=None):
+    """A zero-argument callable running the plain-read probe
+    (lp_bench_stream_read) over ``rows`` rows of ``row_len`` floats of x."""
+    lib = load()
+    args = (_dev_ptr(x), ctypes.c_uint32(rows), ctypes.c_uint32(row_len), _dev_ptr(partial),
+            _stream_ptr(stream))
+
+    def launch():
+        _check(lib.lp_bench_stream_read(*args), "lp_bench_stream_read")
+    return launch
 
 
 def status_string(code: int) -> str:

@@ -738,24 +738,39 @@ __global__ __launch_bounds__(256) void pad_kernel(float *out_lp, uint32_t *out_i
 
 // ------------------------------------------------------------------ streaming-read probe
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const float4 *x, uint64_t n4,
-                                                         const float *tail, uint32_t ntail,
+// One workgroup of 8 waves per row of row_len floats (16-byte aligned rows),
+// each lane reading 4 nontemporal 16-byte loads per step -- the row-shaped
+// plain read that sustains the most bandwidth on these shapes -- and writing
+// the row's sum (so nothing is optimised away).
+__global__ __launch_bounds__(512) void stream_read_kernel(const float *x, uint32_t row_len,
                                                          float *partial) {
-    __shared__ float red[4];
-    const uint64_t stride = uint64_t(gridDim.x) * 256u;
-    float acc0 = 0.f, acc1 = 0.f;
-    for (uint64_t i = uint64_t(blockIdx.x) * 256u + threadIdx.x; i < n4; i += stride) {
-        const float4 v = x[i];
-        acc0 += v.x + v.y;
-        acc1 += v.z + v.w;
+    __shared__ float red[8];
+    constexpr uint32_t kThreads = 512;
+    const f32x4 *row = reinterpret_cast<const f32x4 *>(x + uint64_t(blockIdx.x) * row_len);
+    const uint32_t n4 = row_len / 4;
+    float acc = 0.0f;
+    uint32_t i = threadIdx.x;
+    for (; i + 3 * kThreads < n4; i += 4 * kThreads) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(row + i + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
     }
-    if (blockIdx.x == 0 && threadIdx.x < ntail) acc0 += tail[threadIdx.x];
-    float acc = acc0 + acc1;
+    for (; i < n4; i += kThreads) {
+        const f32x4 v = row[i];
+        acc += (v.x + v.y) + (v.z + v.w);
+    }
+    if (threadIdx.x < row_len - n4 * 4) acc += x[uint64_t(blockIdx.x) * row_len + n4 * 4 + threadIdx.x];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
     __syncthreads();
-    if (threadIdx.x == 0) partial[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int k = 0; k < 8; ++k) t += red[k];
+        partial[blockIdx.x] = t;
+    }
 }
 
 }  // namespace dev
@@ -1004,19 +1019,14 @@ lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64
     return LP_OK;
 }
 
-lp_status lp_bench_stream_read(const float *x, uint64_t n, float *partial_out, uint32_t *grid_out,
+lp_status lp_bench_stream_read(const float *x, uint32_t rows, uint32_t row_len, float *partial_out,
                                void *stream) {
-    if (x == nullptr || partial_out == nullptr || grid_out == nullptr) return LP_ERR_NULL_ARG;
-    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return LP_ERR_UNSUPPORTED;
-    const uint64_t n4 = n / 4;
-    const uint32_t ntail = static_cast<uint32_t>(n - n4 * 4);
-    uint64_t grid = n4 / (256ull * 16ull);
-    if (grid < 1) grid = 1;
-    if (grid > 65536) grid = 65536;
-    *grid_out = static_cast<uint32_t>(grid);
-    hipLaunchKernelGGL(lp::dev::stream_read_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(x), n4,
-                       x + n4 * 4, ntail, partial_out);
+    if (rows == 0) return LP_OK;
+    if (x == nullptr || partial_out == nullptr) return LP_ERR_NULL_ARG;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0 || (row_len & 3u) != 0 || row_len == 0)
+        return LP_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(lp::dev::stream_read_kernel, dim3(rows), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), x, row_len, partial_out);
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }

@@ -443,16 +443,19 @@ def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, token
     row of the request."""
     import torch
 
-    lp, ids, out_off = compute_log_probabilities_ragged(
-        input_row_offsets, logits, next_token_logits, tokens, sampled_tokens, batch_top_n,
-        batch_echo, stream=stream, levels=levels, temperature=temperature)
+    off = np.asarray(input_row_offsets)
     vocab = int(next_token_logits.shape[1])
-    plan = Plan(np.asarray(input_row_offsets), batch_echo, batch_top_n, vocab, logits is not None,
+    plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
                 None if logits is None else int(logits.shape[0]), levels=levels)
     try:
+        if temperature is not None:
+            plan.set_temperature(temperature)
+        lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, None, None, None,
+                       stream, torch)
         torch.cuda.synchronize(lp.device)
         lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
         toks, vals, counts = plan.assemble(lp_h, ids_h)
+        out_off = plan.out_off.copy()
     finally:
         plan.close()
     C = lp_h.shape[1]

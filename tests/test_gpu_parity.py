@@ -178,6 +178,18 @@ def test_levels(R, levels, vocab, split, waves, depth):
     assert_parity(*got, ref, f"levels={levels} vocab={vocab} split={split}")
 
 
+@pytest.mark.parametrize("vocab", [1, 2, 5, 62, 63, 64, 65])
+def test_levels6_small_vocab(R, vocab):
+    """63 ranked slots over vocabularies around and below 63 (the rest pads)."""
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(vocab + 900, vocab, 6)
+    top_n = np.where(top_n > 0, 63, 0)
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=6)
+    for split in (None, 2, 16):
+        got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split,
+                          levels=6)
+        assert_parity(*got, ref, f"levels 6 vocab={vocab} split={split}")
+
+
 @pytest.mark.parametrize("levels", [1, 5, 6])
 def test_levels_direct_rows(R, levels):
     """Next-token rows (the direct-row kernels) at other heap depths, with the
@@ -289,6 +301,28 @@ def test_vocab_shards(R, levels, n_shards):
     whole = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
                         levels=levels)
     assert np.array_equal(got[1], whole[1])
+
+
+@pytest.mark.parametrize("vocab,n_shards,levels", [(7, 3, 3), (64, 64, 1), (130, 16, 6), (5, 5, 2),
+                                                   (1027, 64, 4)])
+def test_vocab_shards_edges(R, vocab, n_shards, levels):
+    """Shards narrower than one 16-byte load, one shard per id, 64 shards,
+    the deepest heap with fewer ids than slots."""
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(vocab + n_shards, vocab, levels)
+    bounds = _shard_bounds(vocab, n_shards, np.random.default_rng(vocab))
+    log(f"shard edges vocab={vocab} shards={n_shards} levels={levels}")
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+    got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds)
+    assert_parity(*got, ref, f"shard edges vocab={vocab} n={n_shards}")
+
+
+def test_vocab_shards_padding_only(R):
+    """Every top_n 0: the merge pads every row without reading records."""
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(5, 300, 3)
+    top_n = np.zeros_like(top_n)
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo)
+    got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, 3, [(0, 100), (100, 300)])
+    assert_parity(*got, ref, "shards, padding only")
 
 
 def test_vocab_shards_decode_tp8(R):

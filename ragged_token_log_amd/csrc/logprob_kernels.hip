@@ -437,17 +437,19 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
 
-    // All float4s of the segment are read through one buffer resource whose
-    // range ends at the last of them: a load past the end returns zeros
-    // without touching memory.  So refills are unconditional, no buffer value
-    // ever merges two paths, and the compiler keeps each buffer in place
-    // instead of copying buffers at the loop's back edge (a copy would first
-    // wait for every load in flight).
+    // The full chunks are read through a buffer resource whose range ends at
+    // the last of them: a load past the end returns zeros without touching
+    // memory.  So refills are unconditional, no buffer value ever merges two
+    // paths, and the compiler keeps each buffer in place instead of copying
+    // buffers at the loop's back edge (a copy would first wait for every load
+    // in flight).  The partial chunk has a range of its own, so the refills
+    // past the end never read it a second time.
+    const StreamRange chunks = make_stream_range(row + a0, nchunks * uint32_t(kChunkF4 * 16));
     const StreamRange body = make_stream_range(row + a0, nf4 * 16u);
     auto load_chunk = [&](f32x4 (&x)[kU], uint32_t ch) __attribute__((always_inline)) {
         const uint32_t off = ch * uint32_t(kChunkF4 * 16) + uint32_t(lane) * 16u;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) x[u] = stream_load(body, off + uint32_t(u * kWave * 16));
+        for (int u = 0; u < kU; ++u) x[u] = stream_load(chunks, off + uint32_t(u * kWave * 16));
     };
     // Scheduling barriers keep the loads where they are: after the last use
     // of the buffer's old values (so the new ones can take the same

@@ -159,6 +159,17 @@ def test_split_and_workspace():
     assert big.split == 1
 
 
+@pytest.mark.parametrize("vocab,waves,depth", [(32000, 8, 1), (65536, 8, 1), (65537, 16, 1),
+                                               (128256, 16, 1), (131072, 16, 1), (131073, 4, 2),
+                                               (151936, 4, 2)])
+def test_many_rows_shape_by_row_length(vocab, waves, depth):
+    """Plans of many rows pick the workgroup shape by row length."""
+    plan = R.Plan(np.arange(1025, dtype=np.uint32), np.ones(1024, bool), np.full(1024, 5), vocab,
+                  True)
+    info = plan.info()
+    assert (info["split"], info["waves"], info["depth"]) == (1, waves, depth)
+
+
 def test_segments_stay_within_the_streamed_range():
     # one workgroup streams at most 2^28 elements of a row: a wider row is
     # always cut into segments, and a split leaving longer segments is refused

@@ -99,24 +99,6 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) { return readlane_u64(v, 0); }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-    v = fmaxf(v, dpp_f32<kDppXor1>(v));
-    v = fmaxf(v, dpp_f32<kDppXor2>(v));
-    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppMirror>(v));
-    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
-                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
-}
-
-__device__ __forceinline__ float wave_min_f32(float v) {
-    v = fminf(v, dpp_f32<kDppXor1>(v));
-    v = fminf(v, dpp_f32<kDppXor2>(v));
-    v = fminf(v, dpp_f32<kDppHalfMirror>(v));
-    v = fminf(v, dpp_f32<kDppMirror>(v));
-    return fminf(fminf(readlane_f32(v, 0), readlane_f32(v, 16)),
-                 fminf(readlane_f32(v, 32), readlane_f32(v, 48)));
-}
-
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<kDppXor1>(v));
     v = max(v, dpp_u32<kDppXor2>(v));
@@ -265,36 +247,20 @@ __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
 // A bound from one real element per lane (or -inf for none): if kK lanes
 // hold values >= t (counting lanes that tie), no element below t can be in
 // the top kK, so the bound may be just under the smallest key of value t.
-// t is the kK-th largest of the 64 lane values, found by rounds of wave max
-// (or, for kK > 32, as the (65 - kK)-th smallest by rounds of wave min).  A
-// -inf t excludes nothing.
+// t is the kK-th largest of the 64 lane values, found bit by bit from the
+// top on their order-mapped high words: a bit stays set when at least kK
+// lanes are at or above the prefix with it, 32 compare-and-count steps for
+// any kK.  A -inf t excludes nothing.
 template <int kK>
 __device__ __forceinline__ uint64_t bound_from_lane_values(float v) {
-    float t = -INFINITY;
-    uint32_t cnt = 0;
-    if constexpr (kK <= 32) {
-#pragma unroll 1
-        for (int r = 0; r < kK; ++r) {
-            const float mx = wave_max_f32(v);
-            cnt += uint32_t(__popcll(__ballot(v == mx)));
-            t = mx;
-            if (cnt >= uint32_t(kK)) break;
-            v = (v == mx) ? -INFINITY : v;
-        }
-        if (cnt < uint32_t(kK)) return 0ull;
-    } else {
-        constexpr uint32_t kNeed = uint32_t(kWave + 1 - kK);
-#pragma unroll 1
-        for (uint32_t r = 0; r < kNeed; ++r) {
-            const float mn = wave_min_f32(v);
-            cnt += uint32_t(__popcll(__ballot(v == mn)));
-            t = mn;
-            if (cnt >= kNeed) break;
-            v = (v == mn) ? INFINITY : v;
-        }
+    const uint32_t u = uint32_t(order_key(v, kPadId) >> 32);
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t trial = t | (1u << b);
+        if (__popcll(__ballot(u >= trial)) >= kK) t = trial;
     }
-    const uint64_t k = order_key(t, kPadId);  // low word 0: smallest key of value t
-    return k > 0 ? k - 1 : 0ull;
+    return t > 0 ? (uint64_t(t) << 32) - 1 : 0ull;  // low word 0: smallest key of value t
 }
 
 // Inserts the wave-uniform key k into the sorted list in lanes 0..kK-1: lane

@@ -403,6 +403,18 @@ def test_tie_edge_stress_full_size(R):
     _full_size(R, gen.tie_edge_stress(), 60, 51)
 
 
+@pytest.mark.parametrize("vocab,waves,depth", [(32000, 8, 1), (128256, 16, 1)])
+def test_many_rows_row_length_shapes(R, vocab, waves, depth):
+    """Thousands of rows of the widths whose default shape differs (8 waves
+    one chunk deep, 16 waves one chunk deep), sampled rows against the
+    oracle."""
+    c = gen.prefill_echo_large(seed=44, batch=4, vocab=vocab)
+    info = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, True).info()
+    assert info["read_rows"] >= 1024
+    assert (info["split"], info["waves"], info["depth"]) == (1, waves, depth)
+    _full_size(R, c, 40, 43)
+
+
 def test_deterministic_and_split_independent(R):
     c = gen.ragged_echo_mix(seed=9, batch=6, lmin=30, lmax=90)
     logits = _dev(gen.host_logits(c))

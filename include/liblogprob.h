@@ -158,8 +158,11 @@ lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
  * lp_stage_ragged -- builds the row descriptors on the host (tokens and
  * sampled tokens are host arrays, as in [MAX] §compute_log_probabilities_ragged)
  * and enqueues their copy into the device workspace on `stream` (a
- * hipStream_t; NULL = default stream).  The plan's pinned staging buffer is
- * reused; a second call waits until the previous copy from it has finished.
+ * hipStream_t; NULL = default stream).  The descriptors go through a
+ * process-wide pool of pinned host buffers (one per upload in flight, per
+ * device): a buffer is reused once the copy from it has finished, so the call
+ * neither allocates nor waits in the steady state, and the plan may be
+ * destroyed as soon as it returns.
  */
 lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens,
                           const uint32_t *sampled_tokens, void *workspace,
@@ -258,8 +261,8 @@ lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64
                           float *out_logprobs, uint32_t *out_token_ids, void *workspace,
                           uint64_t workspace_bytes, void *stream);
 
-/* Frees the plan.  Waits for a pending descriptor copy from its staging
- * buffer first.  NULL is a no-op. */
+/* Frees the plan (host memory only; it never waits for the device).  NULL
+ * is a no-op. */
 void lp_plan_destroy(lp_plan *plan);
 
 /* Static text for a status ("LP_OK", "LP_ERR_SHAPE", ...). */

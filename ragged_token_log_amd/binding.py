@@ -76,19 +76,19 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
     P = ctypes.POINTER
-    lib.lp_plan_ragged.argtypes = [u32, u32, u32, P(u32), P(ctypes.c_uint8), P(i32),
-                                   ctypes.c_int, u64, P(vp), P(u32), P(u64), P(u64)]
+    # host arrays go in as plain addresses (numpy's .ctypes.data)
+    lib.lp_plan_ragged.argtypes = [u32, u32, u32, vp, vp, vp, ctypes.c_int, u64, P(vp), vp,
+                                   P(u64), P(u64)]
     lib.lp_plan_get_info.argtypes = [vp, P(PlanInfo)]
     lib.lp_plan_set_split.argtypes = [vp, u32]
     lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_set_depth.argtypes = [vp, u32]
-    lib.lp_plan_set_temperature.argtypes = [vp, P(ctypes.c_float)]
-    lib.lp_plan_descriptors.argtypes = [vp, P(u32), P(u32), P(u32)]
-    lib.lp_assemble_ragged.argtypes = [vp, P(ctypes.c_float), P(u32), P(u32), P(ctypes.c_float),
-                                       P(u32)]
-    lib.lp_stage_ragged.argtypes = [vp, P(u32), P(u32), vp, u64, vp]
+    lib.lp_plan_set_temperature.argtypes = [vp, vp]
+    lib.lp_plan_descriptors.argtypes = [vp, vp, vp, vp]
+    lib.lp_assemble_ragged.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lp_stage_ragged.argtypes = [vp, vp, vp, vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
-    lib.lp_compute_ragged.argtypes = [vp, vp, vp, P(u32), P(u32), vp, vp, vp, u64, vp]
+    lib.lp_compute_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
     lib.lp_shard_records.argtypes = [vp, u32, u32, vp, vp, vp, vp, u64, vp]
     lib.lp_merge_shards.argtypes = [vp, u32, vp, vp, vp, vp, u64, vp]
     lib.lp_plan_destroy.argtypes = [vp]
@@ -120,10 +120,10 @@ def _u32(a, n=None):
     return arr
 
 
-def _ptr(arr, ctype):
-    if arr is None:
-        return None
-    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+def _ptr(arr, ctype=None):
+    """The address of a contiguous host array of `ctype` elements (None for
+    NULL)."""
+    return None if arr is None else arr.ctypes.data
 
 
 def _dev_ptr(t):
@@ -167,9 +167,16 @@ class Plan:
         self.out_off = out_off
         self.out_rows = int(rows.value)
         self.input_row_offsets = off
-        self.columns = int(self.info()["columns"])
+        self._columns = None
 
     # ---------------------------------------------------------------- facts
+    @property
+    def columns(self) -> int:
+        """Output columns per row (2^levels, one slot per lane)."""
+        if self._columns is None:
+            self._columns = int(self.info()["columns"])
+        return self._columns
+
     def info(self) -> dict:
         inf = PlanInfo()
         _check(self._lib.lp_plan_get_info(self._h, ctypes.byref(inf)), "lp_plan_get_info")

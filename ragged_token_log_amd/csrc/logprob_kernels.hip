@@ -37,6 +37,9 @@
 
 #include <cstdint>
 #include <cstring>
+#include <memory>
+#include <mutex>
+#include <vector>
 
 #include "lp_internal.h"
 
@@ -756,17 +759,68 @@ static thread_local int g_last_hip_error = 0;
         }                                         \
     } while (0)
 
-void release_staging(lp_plan &p) {
-    if (p.staging_event != nullptr) {
-        if (p.staging_pending) (void)hipEventSynchronize(static_cast<hipEvent_t>(p.staging_event));
-        (void)hipEventDestroy(static_cast<hipEvent_t>(p.staging_event));
-        p.staging_event = nullptr;
+// Pinned host staging for descriptor uploads, shared by every plan of the
+// process: a slot belongs to one device and is reused once the event recorded
+// after its last copy has completed, so planning, staging and destroying a
+// plan neither allocate pinned memory nor wait in the steady state.  Slots are
+// never freed before the process ends (the pool only grows to the number of
+// uploads in flight at once).
+struct StagingSlot {
+    void *host = nullptr;
+    uint64_t bytes = 0;
+    hipEvent_t done = nullptr;
+    int device = -1;
+    bool busy = false;   // taken by a stage call that has not recorded its event yet
+};
+
+static std::mutex g_staging_mutex;
+static std::vector<std::unique_ptr<StagingSlot>> g_staging;
+
+// A free slot of at least `bytes` on `device` (the smallest such), a finished
+// smaller one grown to `bytes`, or a new one.
+static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) {
+    std::lock_guard<std::mutex> lock(g_staging_mutex);
+    StagingSlot *fit = nullptr, *small = nullptr;
+    for (auto &up : g_staging) {
+        StagingSlot *sl = up.get();
+        if (sl->busy || sl->device != device) continue;
+        if (hipEventQuery(sl->done) != hipSuccess) continue;   // its copy is still in flight
+        if (sl->bytes >= bytes) {
+            if (fit == nullptr || sl->bytes < fit->bytes) fit = sl;
+        } else if (small == nullptr) {
+            small = sl;
+        }
     }
-    if (p.staging != nullptr) {
-        (void)hipHostFree(p.staging);
-        p.staging = nullptr;
+    if (fit == nullptr && small != nullptr) {
+        void *h = nullptr;
+        LP_HIP_TRY(hipHostMalloc(&h, bytes, hipHostMallocDefault));
+        (void)hipHostFree(small->host);
+        small->host = h;
+        small->bytes = bytes;
+        fit = small;
     }
-    p.staging_pending = false;
+    if (fit == nullptr) {
+        auto sl = std::make_unique<StagingSlot>();
+        LP_HIP_TRY(hipHostMalloc(&sl->host, bytes, hipHostMallocDefault));
+        const hipError_t e = hipEventCreateWithFlags(&sl->done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            (void)hipHostFree(sl->host);
+            g_last_hip_error = int(e);
+            return LP_ERR_HIP;
+        }
+        sl->bytes = bytes;
+        sl->device = device;
+        fit = sl.get();
+        g_staging.push_back(std::move(sl));
+    }
+    fit->busy = true;
+    *out = fit;
+    return LP_OK;
+}
+
+static void staging_release(StagingSlot *sl) {
+    std::lock_guard<std::mutex> lock(g_staging_mutex);
+    sl->busy = false;
 }
 
 template <int kK, int kWaves, int kDepth>
@@ -860,23 +914,18 @@ lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens, const uint32_t 
     if (st != LP_OK) return st;
     const uint64_t bytes = plan->out_rows * sizeof(lp::RowDesc);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (plan->staging == nullptr || plan->staging_bytes < bytes) {
-        lp::release_staging(*plan);
-        LP_HIP_TRY(hipHostMalloc(&plan->staging, bytes, hipHostMallocDefault));
-        plan->staging_bytes = bytes;
-        hipEvent_t ev;
-        LP_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-        plan->staging_event = ev;
-    } else if (plan->staging_pending) {
-        LP_HIP_TRY(hipEventSynchronize(static_cast<hipEvent_t>(plan->staging_event)));
-        plan->staging_pending = false;
-    }
-    st = lp::build_descriptors(*plan, tokens, sampled_tokens,
-                               static_cast<lp::RowDesc *>(plan->staging));
+    int device = 0;
+    LP_HIP_TRY(hipGetDevice(&device));
+    lp::StagingSlot *slot = nullptr;
+    st = lp::staging_acquire(bytes, device, &slot);
     if (st != LP_OK) return st;
-    LP_HIP_TRY(hipMemcpyAsync(workspace, plan->staging, bytes, hipMemcpyHostToDevice, s));
-    LP_HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(plan->staging_event), s));
-    plan->staging_pending = true;
+    st = lp::build_descriptors(*plan, tokens, sampled_tokens, static_cast<lp::RowDesc *>(slot->host));
+    hipError_t e = hipSuccess;
+    if (st == LP_OK) e = hipMemcpyAsync(workspace, slot->host, bytes, hipMemcpyHostToDevice, s);
+    if (st == LP_OK && e == hipSuccess) e = hipEventRecord(slot->done, s);
+    lp::staging_release(slot);
+    if (st != LP_OK) return st;
+    LP_HIP_TRY(e);
     return LP_OK;
 }
 

@@ -81,11 +81,6 @@ struct lp_plan {
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 8 (slots + 2) when split > 1
     uint64_t workspace_bytes = 0;
-    // pinned staging for the descriptor upload (allocated on first stage)
-    void *staging = nullptr;
-    uint64_t staging_bytes = 0;
-    void *staging_event = nullptr;   // hipEvent_t recorded after the last upload
-    bool staging_pending = false;
 };
 
 namespace lp {
@@ -94,6 +89,4 @@ lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
                             const uint32_t *sampled, RowDesc *out);
 // Recomputes workspace sizes after a split change.
 void size_workspace(lp_plan &p);
-// Releases pinned staging (defined with the device code).
-void release_staging(lp_plan &p);
 }  // namespace lp

@@ -330,8 +330,6 @@ lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_
 }
 
 void lp_plan_destroy(lp_plan *plan) {
-    if (plan == nullptr) return;
-    lp::release_staging(*plan);
     delete plan;
 }
 

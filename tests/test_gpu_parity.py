@@ -415,6 +415,30 @@ def test_many_rows_row_length_shapes(R, vocab, waves, depth):
     _full_size(R, c, 40, 43)
 
 
+def test_staging_pool_plans_in_flight(R):
+    """Several plans staged and launched back to back on one stream, each
+    destroyed as soon as its call returns (descriptors go through the
+    process-wide pinned pool): every output matches the oracle."""
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    cases, outs = [], []
+    for i in range(6):
+        off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(500 + i, 3000 + 500 * i, 3,
+                                                                       rows_per_req=(1 + i, 3, 2, 5))
+        plan = R.Plan(off, echo, top_n, ntl.shape[1], True)
+        lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+        lg, nt = _dev(logits), _dev(ntl)
+        plan.compute(lg, nt, tokens, sampled, lp, ids, ws, stream)
+        out_off = plan.out_off.copy()
+        plan.close()
+        cases.append((off, logits, ntl, tokens, sampled, top_n, echo))
+        outs.append((lp, ids, out_off, lg, nt, ws))
+    torch.cuda.synchronize()
+    for i, (c, o) in enumerate(zip(cases, outs)):
+        ref = oracle(*c)
+        assert_parity(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2], ref, f"plan {i} in flight")
+
+
 def test_deterministic_and_split_independent(R):
     c = gen.ragged_echo_mix(seed=9, batch=6, lmin=30, lmax=90)
     logits = _dev(gen.host_logits(c))

@@ -359,10 +359,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device code (the kernels' namespace in the HIP source):
+    host-side edits leave recorded counters valid; the launch shape is
+    checked separately."""
     import hashlib
 
     with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        text = f.read()
+    begin, end = text.index(b"namespace dev {"), text.index(b"}  // namespace dev")
+    return hashlib.sha256(text[begin:end]).hexdigest()[:16]
 
 
 def shape_text(info):

@@ -35,6 +35,12 @@ design notes):
   R9  an all -inf row has NaN logprobs (IEEE x - lse with lse = -inf).
   R10 NaN or +inf logits are outside the contract and rejected.
   R11 an empty request (L_n = 0) is an error.
+  R23 a top-k front end (the FlashInfer page's TopK processor on logits, then
+      Softmax) keeps exactly the k best tokens of the ranking (R4 order, so
+      ties at the boundary go to the lowest ids); k = 0 keeps all.
+  R24 with a top-k front end, log-probabilities are renormalised over the
+      kept tokens (after the temperature); only kept tokens are listed.
+  R25 a chosen token outside the kept set has log-probability -inf.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, invariants, the worked example of [SGL]).  The
@@ -228,10 +234,22 @@ def rank_descending(row_f32) -> np.ndarray:
     return np.argsort(-canon.astype(np.float64), kind="stable")
 
 
-def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float = 1.0):
+def check_top_k(k, cols: int) -> int:
+    """A request's top-k front end: 0 (none) up to the ranked slots
+    (readings R23, R24)."""
+    k = int(k)
+    if k < 0 or k > cols - 1:
+        raise OracleError("LP_ERR_TOP_K", f"top_k={k} outside [0, {cols - 1}]")
+    return k
+
+
+def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float = 1.0,
+                top_k: int = 0):
     """One output row: ``cols - 1`` top slots (padded past min(top_n, V)) and
     the chosen token in the last slot.  [MAX] §log_probabilities_ragged_graph
-    (lp_logits / lp_tokens) and §compute_top 的结果组装."""
+    (lp_logits / lp_tokens) and §compute_top 的结果组装.  With ``top_k`` > 0,
+    the FlashInfer page's TopK on logits and Softmax come first: the
+    distribution is the softmax of the kept logits alone (R23-R25)."""
     lp_out = np.full(cols, -np.inf, dtype=np.float32)
     id_out = np.full(cols, PAD_ID, dtype=np.uint32)
     if top_n == 0:
@@ -239,9 +257,16 @@ def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float 
     x = np.asarray(row_f32, dtype=np.float32)
     if np.any(np.isnan(x)) or np.any(np.isposinf(x)):
         raise OracleError("LP_ERR_UNSUPPORTED", "NaN or +inf logits (R10)")
-    lp, _ = log_softmax_f64(x, temperature)
     order = rank_descending(x)
-    take = order[: min(top_n, x.shape[0], cols - 1)]
+    if top_k == 0:
+        lp, _ = log_softmax_f64(x, temperature)
+        listed = order
+    else:
+        kept = order[: min(top_k, x.shape[0])]
+        lp = np.full(x.shape[0], -np.inf)
+        lp[kept], _ = log_softmax_f64(x[kept], temperature)
+        listed = kept
+    take = listed[: min(top_n, x.shape[0], cols - 1)]
     for j, t in enumerate(take):
         lp_out[j] = np.float32(lp[t])
         id_out[j] = t
@@ -252,7 +277,8 @@ def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float 
 
 def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logits,
                                      tokens, sampled_tokens, batch_top_n, batch_echo,
-                                     levels=DEFAULT_LEVELS, rows=None, batch_temperature=None):
+                                     levels=DEFAULT_LEVELS, rows=None, batch_temperature=None,
+                                     batch_top_k=None):
     """The whole path for one batch.
 
     Arguments follow [MAX] §compute_log_probabilities_ragged：执行计算并组装结果.
@@ -264,7 +290,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     Returns ``(out_lp (R, cols) float32, out_ids (R, cols) uint32,
     out_off (batch+1) uint32)``.  If ``rows`` is given, only those output rows
     are computed (the rest stay padding) -- used to check very large inputs
-    row by row.
+    row by row.  ``batch_top_k`` (one per request, 0 = none) adds the top-k
+    front end of R23-R25.
     """
     has_logits = logits is not None
     lshape = tuple(logits.shape) if has_logits else None
@@ -283,6 +310,12 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
         temps = [check_temperature(t) for t in batch_temperature]
         if len(temps) != batch:
             raise OracleError("LP_ERR_SHAPE", "one temperature per request")
+    if batch_top_k is None:
+        top_ks = [0] * batch
+    else:
+        top_ks = [check_top_k(k, cols) for k in batch_top_k]
+        if len(top_ks) != batch:
+            raise OracleError("LP_ERR_SHAPE", "one top_k per request")
     req = np.repeat(np.arange(batch), np.diff(out_off.astype(np.int64)))
     out_lp = np.full((n_out, cols), -np.inf, dtype=np.float32)
     out_ids = np.full((n_out, cols), PAD_ID, dtype=np.uint32)
@@ -290,7 +323,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     for o in which:
         t = tasks[o]
         row = src[t.src_row] if t.top_n > 0 else None
-        out_lp[o], out_ids[o] = compute_row(row, t.chosen, t.top_n, cols, temps[req[o]])
+        out_lp[o], out_ids[o] = compute_row(row, t.chosen, t.top_n, cols, temps[req[o]],
+                                            top_ks[req[o]])
     return out_lp, out_ids, out_off
 
 

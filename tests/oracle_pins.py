@@ -459,3 +459,79 @@ def pin_temperature():
             assert e.code == "LP_ERR_TEMPERATURE"
         else:
             raise AssertionError(f"temperature {bad} accepted")
+
+
+# ------------------------------------------------------------------ top-k front end
+
+def pin_top_k():
+    """The top-k front end (the FlashInfer page's TopK on logits, then
+    Softmax): hand closed forms, boundary ties, a 50-digit brute force over
+    the kept set, reductions to the untruncated row, and the rejected k."""
+    pad = LO.PAD_ID
+    # x = (1, 2, 3), k = 2: ids 2 and 1 are kept; log p = -log(1 + e^-1) and
+    # -log(1 + e); id 0 is dropped (-inf)
+    x = np.array([1.0, 2.0, 3.0], np.float32)
+    a, b = -math.log1p(math.exp(-1.0)), -math.log1p(math.e)
+    lp, ids = LO.compute_row(x, 0, 7, 8, 1.0, 2)
+    assert ids.tolist() == [2, 1] + [pad] * 5 + [0], ids
+    assert abs(lp[0] - a) < 1e-6 and abs(lp[1] - b) < 1e-6 and lp[7] == -np.inf, lp
+    assert np.all(lp[2:7] == -np.inf)
+    lp, ids = LO.compute_row(x, 1, 1, 8, 1.0, 2)       # top_n 1 lists one; chosen kept
+    assert ids.tolist() == [2] + [pad] * 6 + [1] and abs(lp[7] - b) < 1e-6, (lp, ids)
+    # at temperature 2 the kept pair differs by 1/2
+    lp, _ = LO.compute_row(x, 2, 7, 8, 2.0, 2)
+    assert abs(lp[0] + math.log1p(math.exp(-0.5))) < 1e-6, lp
+    assert abs(lp[7] + math.log1p(math.exp(-0.5))) < 1e-6, lp
+    # k = 1: the top token has log p = 0; anything else is -inf
+    lp, ids = LO.compute_row(np.array([0.3, 5.0, -2.0, 5.0], np.float32), 3, 7, 8, 1.0, 1)
+    assert ids[0] == 1 and lp[0] == 0.0 and lp[7] == -np.inf and ids[7] == 3, (lp, ids)
+    # boundary ties: of three equal maxima, k = 2 keeps ids 0 and 1 (R23)
+    lp, ids = LO.compute_row(np.array([1.0, 1.0, 1.0, 0.0], np.float32), 2, 7, 8, 1.0, 2)
+    assert ids[:3].tolist() == [0, 1, pad], ids
+    assert abs(lp[0] + math.log(2.0)) < 1e-6 and abs(lp[1] + math.log(2.0)) < 1e-6
+    assert lp[7] == -np.inf
+    # a kept -inf token keeps log p = -inf
+    lp, ids = LO.compute_row(np.array([0.0, -np.inf, -np.inf], np.float32), 1, 7, 8, 1.0, 2)
+    assert ids[:2].tolist() == [0, 1] and lp[0] == 0.0 and lp[1] == -np.inf and lp[7] == -np.inf
+    # brute force at 50 digits over the kept values / T
+    rng = np.random.default_rng(23)
+    for trial in range(12):
+        n = int(rng.integers(3, 40))
+        xs = (rng.standard_normal(n) * 2).astype(np.float32)
+        k = int(rng.integers(1, 8))
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        kept = brute_top_ids([float(v) for v in xs], k)
+        want, _ = mp_logprobs([float(xs[i]) / T for i in kept])
+        chosen = int(rng.integers(0, n))
+        lp, ids = LO.compute_row(xs, chosen, 7, 8, T, k)
+        listed = kept[:7]
+        assert ids[: len(listed)].tolist() == listed, (trial, ids, kept)
+        for j in range(len(listed)):
+            assert abs(float(lp[j]) - float(want[j])) < 1e-6, (trial, j)
+        if chosen in kept:
+            assert abs(float(lp[7]) - float(want[kept.index(chosen)])) < 1e-6, trial
+        else:
+            assert lp[7] == -np.inf, trial
+        # the kept probabilities sum to one
+        assert abs(sum(math.exp(float(w)) for w in want) - 1.0) < 1e-12
+    # k at or beyond V keeps every token: the untruncated row
+    xs = np.array([0.5, -1.0, 2.0, 0.0, 1.5], np.float32)
+    for k in (5, 7):
+        got = LO.compute_row(xs, 4, 7, 8, 1.0, k)
+        ref = LO.compute_row(xs, 4, 7, 8, 1.0, 0)
+        assert np.array_equal(got[1], ref[1]) and np.allclose(got[0], ref[0], atol=1e-7), k
+    # through the batch entry: one k per request, 0 = none
+    off = np.array([0, 1, 3], np.uint32)
+    logits = np.array([[1, 2, 3], [3, 2, 1], [0, 0, 5]], np.float32)
+    lp, ids, _ = LO.compute_log_probabilities_ragged(
+        off, logits, logits[[0, 2]], np.array([0, 1, 0], np.uint32), np.array([0, 2], np.uint32),
+        [7, 7], [False, True], batch_top_k=[2, 0])
+    assert ids[0, :3].tolist() == [2, 1, pad] and abs(lp[0, 0] - a) < 1e-6 and lp[0, 7] == -np.inf
+    assert ids[1, :3].tolist() == [0, 1, 2] and ids[2, 0] == 2     # request 1 is untruncated
+    for bad, cols in ((8, 8), (-1, 8), (2, 2)):
+        try:
+            LO.check_top_k(bad, cols)
+        except LO.OracleError as e:
+            assert e.code == "LP_ERR_TOP_K"
+        else:
+            raise AssertionError(f"top_k {bad} accepted with {cols} columns")

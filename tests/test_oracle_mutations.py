@@ -80,23 +80,56 @@ def _counts_swapped(off, echo):
     return _orig["output_counts_and_offsets"](off, [not bool(e) for e in echo])
 
 
-def _row_pad_zero(row, chosen, top_n, cols, temperature=1.0):
-    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature)
+def _row_pad_zero(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature, top_k)
     ids = ids.copy()
     ids[ids == LO.PAD_ID] = 0
     return lp, ids
 
 
-def _row_last_col_top1(row, chosen, top_n, cols, temperature=1.0):
-    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature)
+def _row_last_col_top1(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature, top_k)
     if top_n > 0:
         lp = lp.copy()
         lp[cols - 1] = lp[0]
     return lp, ids
 
 
-def _row_ignores_top_n(row, chosen, top_n, cols, temperature=1.0):
-    return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols, temperature)
+def _row_ignores_top_n(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    return _orig["compute_row"](row, chosen, 7 if top_n > 0 else 0, cols, temperature, top_k)
+
+
+def _row_topk_ignored(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    return _orig["compute_row"](row, chosen, top_n, cols, temperature, 0)
+
+
+def _row_topk_no_renormalise(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    # plausible slip: mask the dropped tokens but keep the full-row softmax
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature, 0)
+    if top_k > 0 and top_n > 0:
+        lp, ids = lp.copy(), ids.copy()
+        lp[top_k:cols - 1] = -np.inf
+        ids[top_k:cols - 1] = LO.PAD_ID
+        if chosen not in _orig["rank_descending"](row)[:top_k]:
+            lp[cols - 1] = -np.inf
+    return lp, ids
+
+
+def _row_topk_one_more(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    return _orig["compute_row"](row, chosen, top_n, cols, temperature, top_k + 1 if top_k else 0)
+
+
+def _row_topk_chosen_unmasked(row, chosen, top_n, cols, temperature=1.0, top_k=0):
+    # plausible slip: a dropped chosen token still gets x/T - lse(kept)
+    lp, ids = _orig["compute_row"](row, chosen, top_n, cols, temperature, top_k)
+    if top_k > 0 and top_n > 0 and lp[cols - 1] == -np.inf:
+        x = np.asarray(row, np.float64) / temperature
+        kept = _orig["rank_descending"](row)[:top_k]
+        m = np.max(x[kept])
+        lp = lp.copy()
+        with np.errstate(invalid="ignore"):
+            lp[cols - 1] = np.float32(x[chosen] - (m + np.log(np.sum(np.exp(x[kept] - m)))))
+    return lp, ids
 
 
 def _top_no_overwrite(lp_row, id_row, top_n, vocab):
@@ -152,6 +185,10 @@ MUTANTS = {
     "pad_id_zero": ("compute_row", _row_pad_zero),
     "chosen_col_is_top1": ("compute_row", _row_last_col_top1),
     "top_n_ignored": ("compute_row", _row_ignores_top_n),
+    "topk_ignored": ("compute_row", _row_topk_ignored),
+    "topk_no_renormalise": ("compute_row", _row_topk_no_renormalise),
+    "topk_one_more": ("compute_row", _row_topk_one_more),
+    "topk_chosen_unmasked": ("compute_row", _row_topk_chosen_unmasked),
 }
 
 
@@ -174,6 +211,7 @@ def _run_all_pins():
     P.pin_assembly_hand_examples()
     P.pin_assembly_worked_example()
     P.pin_temperature()
+    P.pin_top_k()
 
 
 def test_pins_pass_on_true_oracle():

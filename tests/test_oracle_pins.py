@@ -89,3 +89,7 @@ def test_assembly_worked_example():
 
 def test_temperature():
     P.pin_temperature()
+
+
+def test_top_k():
+    P.pin_top_k()

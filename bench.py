@@ -92,6 +92,8 @@ def main():
                          "each reduced to records, then merged (all on this GPU)")
     ap.add_argument("--temperature", type=float, default=None,
                     help="log_softmax(logits / T) for every request")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="top-k front end (TopK on logits, then Softmax) for every request")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the plain-read probe over the same rows (the practical ceiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,6 +148,8 @@ def main():
         plan.set_waves(args.waves)
     if args.temperature is not None:
         plan.set_temperature(args.temperature)
+    if args.top_k:
+        plan.set_top_k(args.top_k)
     info = plan.info()
     lp, ids, ws = R.alloc_outputs(plan, dev, torch)
     plan.stage(case.tokens, case.sampled, ws, stream)   # descriptors resident in HBM
@@ -206,6 +210,7 @@ def main():
         "config": {"workload": case.name, "batch": case.batch, "vocab": case.vocab,
                    "levels": args.levels, "max_top_n": int(np.max(case.top_n)),
                    "temperature": args.temperature if args.temperature is not None else 1.0,
+                   "top_k": args.top_k,
                    "out_rows": int(info["out_rows"]), "read_rows": read_rows,
                    "split": int(info["split"]), "waves": int(info["waves"]),
                    "logits_copies_cycled": n_copies},
@@ -231,6 +236,10 @@ def main():
                 p2.set_split(args.split)
             if args.waves:
                 p2.set_waves(args.waves)
+            if args.temperature is not None:
+                p2.set_temperature(args.temperature)
+            if args.top_k:
+                p2.set_top_k(args.top_k)
             src = copies[i % n_copies]
             p2.compute(src if case.has_logits else None, None if case.has_logits else src,
                        case.tokens, case.sampled, lp, ids, ws, stream)

@@ -59,8 +59,9 @@ typedef enum lp_status {
     LP_ERR_WORKSPACE = 9,         /* workspace NULL or smaller than the plan asks */
     LP_ERR_HIP = 10,              /* a HIP runtime call failed; see lp_last_hip_error() */
     LP_ERR_NOMEM = 11,            /* host allocation failed */
-    LP_ERR_TEMPERATURE = 12       /* a temperature that is not a positive finite number
+    LP_ERR_TEMPERATURE = 12,      /* a temperature that is not a positive finite number
                                      with a finite reciprocal */
+    LP_ERR_TOP_K = 13             /* a top-k front end outside 0..2^levels - 1 */
 } lp_status;
 
 /* Facts about a plan (all host values). */
@@ -145,8 +146,25 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
 lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature);
 
 /*
+ * Per-request top-k front end (host, B int32; NULL restores 0 = none for all).
+ * The FlashInfer page's TopK processor on logits keeps the k highest-scored
+ * tokens and masks the others to -inf, and its Softmax then normalises over
+ * the kept ones; [SGL] §output 从 forward() 到响应对象的完整路径 names top-k
+ * truncation between the temperature scaling and the softmax the logprobs
+ * reuse.  With k_n > 0, request n's rows keep exactly the k_n best tokens of
+ * the ranking (ties at the boundary go to the lowest ids), their
+ * log-probabilities are log_softmax over the kept logits alone (after the
+ * temperature), only kept tokens are listed (at most min(top_n, k_n)), and a
+ * chosen token outside the kept set gets -inf.  LP_ERR_TOP_K, with the plan
+ * unchanged, if some k_n < 0 or k_n > 2^levels - 1 (the kernels rank only
+ * that many tokens).  Applies to descriptors built after the call.
+ */
+lp_status lp_plan_set_top_k(lp_plan *plan, const int32_t *batch_top_k);
+
+/*
  * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of
- * 4 uint32 to desc_out: {logits row read, chosen token, top_n, 1/temperature bits}, in output
+ * 4 uint32 to desc_out: {logits row read, chosen token, top_n | k << 16 (k the top-k front
+ * end; 0 on rows of top_n 0), 1/temperature bits}, in output
  * row order.  tokens: host, T uint32 (may be NULL when no request echoes);
  * sampled_tokens: host, B uint32.  LP_ERR_TOKEN_RANGE if an id >= V.  The
  * fourth word holds the fp32 bits of the row's 1 / temperature.

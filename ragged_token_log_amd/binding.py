@@ -20,13 +20,14 @@ STATUS_NAMES = {
     0: "LP_OK", 1: "LP_ERR_NULL_ARG", 2: "LP_ERR_OFFSETS", 3: "LP_ERR_SHAPE",
     4: "LP_ERR_TOP_N_NEGATIVE", 5: "LP_ERR_TOP_N_TOO_LARGE", 6: "LP_ERR_ECHO_NEEDS_LOGITS",
     7: "LP_ERR_TOKEN_RANGE", 8: "LP_ERR_UNSUPPORTED", 9: "LP_ERR_WORKSPACE",
-    10: "LP_ERR_HIP", 11: "LP_ERR_NOMEM", 12: "LP_ERR_TEMPERATURE",
+    10: "LP_ERR_HIP", 11: "LP_ERR_NOMEM", 12: "LP_ERR_TEMPERATURE", 13: "LP_ERR_TOP_K",
 }
 
 # every symbol include/liblogprob.h declares
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
-    "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_descriptors", "lp_assemble_ragged",
+    "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_set_top_k", "lp_plan_descriptors",
+    "lp_assemble_ragged",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_shard_records",
     "lp_merge_shards", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
@@ -84,6 +85,7 @@ def load():
     lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_set_depth.argtypes = [vp, u32]
     lib.lp_plan_set_temperature.argtypes = [vp, vp]
+    lib.lp_plan_set_top_k.argtypes = [vp, vp]
     lib.lp_plan_descriptors.argtypes = [vp, vp, vp, vp]
     lib.lp_assemble_ragged.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.lp_stage_ragged.argtypes = [vp, vp, vp, vp, u64, vp]
@@ -99,6 +101,7 @@ def load():
     lib.lp_bench_stream_read.argtypes = [vp, u32, u32, vp, vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
                  "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_temperature",
+                 "lp_plan_set_top_k",
                  "lp_plan_descriptors", "lp_assemble_ragged",
                  "lp_stage_ragged", "lp_launch_ragged", "lp_shard_records", "lp_merge_shards",
                  "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
@@ -213,6 +216,20 @@ class Plan:
             raise LogprobError(3, "temperature must be a scalar or one value per request")
         _check(self._lib.lp_plan_set_temperature(self._h, _ptr(t, ctypes.c_float)),
                "lp_plan_set_temperature")
+
+    def set_top_k(self, top_k):
+        """Per-request top-k front end (a scalar for all, a length-batch
+        sequence, or None for none; 0 = none)."""
+        if top_k is None:
+            _check(self._lib.lp_plan_set_top_k(self._h, None), "lp_plan_set_top_k")
+            return
+        k = np.asarray(top_k, dtype=np.int64)
+        if k.ndim == 0:
+            k = np.full(self.batch, k)
+        if k.shape != (self.batch,):
+            raise LogprobError(3, "top_k must be a scalar or one value per request")
+        k = np.ascontiguousarray(np.clip(k, -1, 1 << 20).astype(np.int32))
+        _check(self._lib.lp_plan_set_top_k(self._h, _ptr(k, ctypes.c_int32)), "lp_plan_set_top_k")
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
         """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
@@ -381,7 +398,7 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
                                      depth: int | None = None, stream=None,
-                                     levels: int = LEVELS, temperature=None):
+                                     levels: int = LEVELS, temperature=None, top_k=None):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -395,6 +412,9 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     "log_probabilities_ragged_graph"): C = 2**levels output columns (one at
     levels 0), top_n <= C - 1.  ``temperature`` (a scalar or one per
     request) gives log_softmax(logits / temperature); None means 1.
+    ``top_k`` (a scalar or one per request, 0 or None = none, at most C - 1)
+    adds the FlashInfer page's TopK-then-Softmax front end: the k best tokens
+    are kept and the log-probabilities renormalised over them.
 
     Returns ``(logprobs (R, C) float32, token_ids (R, C) uint32,
     output_row_offsets (batch+1,) uint32 numpy)``, the tensors on the GPU.
@@ -416,11 +436,13 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     try:
         if temperature is not None:
             plan.set_temperature(temperature)
+        if top_k is not None:
+            plan.set_top_k(top_k)
         lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
                        depth, stream, torch)
         out_off = plan.out_off.copy()
     finally:
-        plan.close()   # waits only for the descriptor upload, not the kernels
+        plan.close()   # host memory only: the enqueued work does not depend on the plan
     return lp, ids, out_off
 
 
@@ -442,7 +464,7 @@ def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, 
 
 def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens, sampled_tokens,
                              batch_top_n, batch_echo, *, levels: int = LEVELS, temperature=None,
-                             stream=None):
+                             top_k=None, stream=None):
     """The whole call of the MAX page's ``compute_log_probabilities_ragged``:
     the device computation, the copy back, and the host assembly
     (lp_assemble_ragged).  Returns one entry per request: None when its
@@ -457,6 +479,8 @@ def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, token
     try:
         if temperature is not None:
             plan.set_temperature(temperature)
+        if top_k is not None:
+            plan.set_top_k(top_k)
         lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, None, None, None,
                        stream, torch)
         torch.cuda.synchronize(lp.device)

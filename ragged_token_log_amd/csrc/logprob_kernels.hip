@@ -320,18 +320,44 @@ __device__ __forceinline__ float logprob(float x, float M, float inv_temp, float
 
 // One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK
 // the chosen token.
+// Sum over the wave, in a fixed order (every lane gets it).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Writes an output row from the row's best keys (lane i < kK holds the
+// (i+1)-th), its max M and scaled sum S.  top_word is the descriptor's third
+// word: top_n, and in its high half the top-k front end's k.  With k > 0 the
+// row's distribution is the softmax of the k kept logits alone (the TopK
+// processor on logits, then Softmax, of the FlashInfer page): S becomes
+// their sum, only kept tokens are listed, and a chosen token outside them
+// gets -inf.
 template <int kK>
 __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint64_t o, int lane,
-                                          uint64_t key, uint32_t top_n, float M, float S,
+                                          uint64_t key, uint32_t top_word, float M, float S,
                                           float inv_temp, float x_chosen, uint32_t chosen) {
     constexpr uint64_t kC = uint64_t(kK) + 1;
+    uint32_t listed = top_word & 0xFFFFu;
+    const uint32_t keep = top_word >> 16;
+    bool chosen_kept = true;
+    if (keep != 0) {
+        const bool kept = uint32_t(lane) < keep && key != 0;
+        const float ms = (M == -INFINITY) ? 0.0f : M;
+        S = wave_sum_f32(kept ? fast_exp2((key_value(key) - ms) * (kLog2e * inv_temp)) : 0.0f);
+        chosen_kept = __ballot(kept && key_id(key) == chosen) != 0;
+        if (keep < listed) listed = keep;
+    }
     const float ln_s = logf(S);
     if (lane < kK) {
-        const bool valid = uint32_t(lane) < top_n && key != 0;
+        const bool valid = uint32_t(lane) < listed && key != 0;
         out_lp[o * kC + lane] = valid ? logprob(key_value(key), M, inv_temp, ln_s) : -INFINITY;
         out_id[o * kC + lane] = valid ? key_id(key) : kPadId;
     } else if (lane == kK) {
-        out_lp[o * kC + lane] = logprob(x_chosen, M, inv_temp, ln_s);
+        out_lp[o * kC + lane] = chosen_kept ? logprob(x_chosen, M, inv_temp, ln_s) : -INFINITY;
         out_id[o * kC + lane] = chosen;
     }
 }

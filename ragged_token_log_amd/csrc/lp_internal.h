@@ -43,7 +43,8 @@ inline uint64_t segment_length(uint32_t vocab, uint32_t split) {
 struct RowDesc {
     uint32_t src_row;   // logits row to read (row of `logits` or of next_token_logits)
     uint32_t chosen;    // token whose log-probability goes in the last column
-    uint32_t top_n;     // 0 => padding only, logits not read
+    uint32_t top_n;     // low 16 bits: top_n (0 => padding only, logits not read);
+                        // high 16 bits: the top-k front end's k (0 = none)
     uint32_t inv_temp_bits;  // fp32 bits of 1 / temperature of the row's request
 };
 static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
@@ -72,6 +73,7 @@ struct lp_plan {
     std::vector<uint8_t> echo;       // B
     std::vector<int32_t> top_n;      // B
     std::vector<float> inv_temp;     // B: 1 / temperature (1 unless set)
+    std::vector<uint32_t> top_k;     // B: top-k front end (0 = none unless set)
     uint64_t out_rows = 0;
     uint64_t read_rows = 0;
     uint32_t split = 1;

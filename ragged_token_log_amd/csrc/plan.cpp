@@ -106,6 +106,7 @@ lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
             d.src_row = static_cast<uint32_t>(src_end - count + k);
             d.chosen = (pos + 1 < len) ? tokens[p.in_off[n] + pos + 1] : sampled[n];
             d.top_n = static_cast<uint32_t>(p.top_n[n]);
+            if (d.top_n > 0) d.top_n |= p.top_k[n] << 16;
             uint32_t bits;
             std::memcpy(&bits, &p.inv_temp[n], 4);
             d.inv_temp_bits = bits;
@@ -164,6 +165,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         p->echo.resize(batch);
         p->top_n.resize(batch);
         p->inv_temp.assign(batch, 1.0f);
+        p->top_k.assign(batch, 0u);
         p->out_off.resize(size_t(batch) + 1);
         uint64_t acc = 0, read = 0;
         p->out_off[0] = 0;
@@ -262,6 +264,18 @@ lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature)
     return LP_OK;
 }
 
+lp_status lp_plan_set_top_k(lp_plan *plan, const int32_t *batch_top_k) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (batch_top_k == nullptr) {
+        plan->top_k.assign(plan->batch, 0u);
+        return LP_OK;
+    }
+    for (uint32_t n = 0; n < plan->batch; ++n)
+        if (batch_top_k[n] < 0 || uint32_t(batch_top_k[n]) > plan->slots) return LP_ERR_TOP_K;
+    for (uint32_t n = 0; n < plan->batch; ++n) plan->top_k[n] = uint32_t(batch_top_k[n]);
+    return LP_OK;
+}
+
 lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
                               const uint32_t *sampled_tokens, uint32_t *desc_out) {
     if (plan == nullptr || (desc_out == nullptr && plan->out_rows > 0)) return LP_ERR_NULL_ARG;
@@ -348,6 +362,7 @@ const char *lp_status_string(lp_status status) {
         case LP_ERR_HIP: return "LP_ERR_HIP";
         case LP_ERR_NOMEM: return "LP_ERR_NOMEM";
         case LP_ERR_TEMPERATURE: return "LP_ERR_TEMPERATURE";
+        case LP_ERR_TOP_K: return "LP_ERR_TOP_K";
     }
     return "LP_ERR_UNKNOWN";
 }

@@ -282,3 +282,26 @@ def test_temperature_in_descriptors_and_errors():
     assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [2.0, 2.0, 0.5]
     plan.set_temperature(None)
     assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [1.0] * 3
+
+
+def test_top_k_in_descriptors_and_errors():
+    """The top-k front end rides in the high half of the descriptor's third
+    word (rows of top_n 0 keep a zero word); values beyond the ranked slots
+    are refused and leave the plan unchanged."""
+    off = np.array([0, 2, 3, 4], np.uint32)
+    plan = R.Plan(off, [1, 0, 0], [3, 2, 0], 50, True)
+    tokens = np.arange(4, dtype=np.uint32)
+    sampled = np.array([4, 5, 6], np.uint32)
+    plan.set_top_k([5, 0, 7])
+    desc = plan.descriptors(tokens, sampled)
+    assert desc[:, 2].tolist() == [3 | 5 << 16, 3 | 5 << 16, 2, 0]
+    for bad in ([8, 0, 0], [-1, 0, 0], [0, 0, 100]):
+        _expect("LP_ERR_TOP_K", lambda b=bad: plan.set_top_k(b))
+    assert plan.descriptors(tokens, sampled)[:, 2].tolist() == [3 | 5 << 16, 3 | 5 << 16, 2, 0]
+    plan.set_top_k(2)
+    assert plan.descriptors(tokens, sampled)[:, 2].tolist() == [3 | 2 << 16, 3 | 2 << 16, 2 | 2 << 16, 0]
+    plan.set_top_k(None)
+    assert plan.descriptors(tokens, sampled)[:, 2].tolist() == [3, 3, 2, 0]
+    wide = R.Plan(off, [1, 0, 0], [3, 2, 0], 500, True, levels=6)
+    wide.set_top_k([63, 1, 0])
+    _expect("LP_ERR_TOP_K", lambda: wide.set_top_k([64, 0, 0]))

@@ -10,8 +10,8 @@ import pytest
 
 import gen
 import oracle.logprob_oracle as LO
-from tests.gpu_helpers import (DeviceRows, assert_parity, check_all_rows_properties, log, oracle,
-                               run_library)
+from tests.gpu_helpers import (DeviceRows, assert_lp_close, assert_parity, check_all_rows_properties,
+                               log, oracle, run_library)
 
 pytestmark = pytest.mark.gpu
 
@@ -242,6 +242,51 @@ def test_temperature(R, levels, vocab, split):
     _assert_close_rel(lp.cpu().numpy(), ref[0], f"temperature levels={levels} split={split}")
 
 
+@pytest.mark.parametrize("levels", [1, 3, 5, 6])
+@pytest.mark.parametrize("vocab", [5, 1027, 40001])
+@pytest.mark.parametrize("split", [None, 3])
+def test_top_k_front_end(R, levels, vocab, split):
+    """The FlashInfer page's TopK on logits then Softmax, per request, with
+    temperatures: kept set, renormalised log-probabilities, dropped chosen
+    tokens at -inf."""
+    log(f"top-k front end levels={levels} vocab={vocab} split={split}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(5 * vocab + levels, vocab, levels)
+    cap = LO.max_top_n(levels)
+    rng = np.random.default_rng(vocab + 17 * levels)
+    top_k = rng.integers(0, cap + 1, len(top_n))
+    top_k[0], top_k[1] = 1, cap
+    temps = np.array([0.5, 1.0, 2.0, 0.8, 1.3, 3.0], np.float32)[: len(top_n)]
+    ref = LO.compute_log_probabilities_ragged(off, logits, ntl, tokens, sampled, list(top_n),
+                                              list(echo), levels=levels, batch_temperature=temps,
+                                              batch_top_k=top_k)
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo, split=split, levels=levels,
+        temperature=temps, top_k=top_k)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_off, ref[2])
+    assert np.array_equal(ids.cpu().numpy(), ref[1]), "ids"
+    _assert_close_rel(lp.cpu().numpy(), ref[0], f"top-k levels={levels} split={split}")
+
+
+@pytest.mark.parametrize("top_k", [1, 3, 7])
+def test_top_k_decode_shape(R, top_k):
+    """Decode rows (direct rows): the sampled token is the boosted id, kept
+    (finite renormalised log-probability) in the rows where it ranks within
+    k and -inf elsewhere, as the oracle says row by row."""
+    c = gen.decode_peaked()
+    ntl = gen.host_logits(c)
+    ref = LO.compute_log_probabilities_ragged(c.offsets, None, ntl, c.tokens, c.sampled,
+                                              list(c.top_n), list(c.echo),
+                                              batch_top_k=[top_k] * c.batch)
+    lp, ids, _ = R.compute_log_probabilities_ragged(c.offsets, None, _dev(ntl), c.tokens, c.sampled,
+                                                    c.top_n, c.echo, top_k=top_k)
+    torch.cuda.synchronize()
+    got_lp = lp.cpu().numpy()
+    assert np.array_equal(ids.cpu().numpy(), ref[1])
+    assert np.isfinite(ref[0][:, 7]).any()        # some rows keep their sampled token
+    assert_lp_close(got_lp, ref[0], f"decode top_k={top_k}")
+
+
 def test_temperature_decode_shape(R):
     """The decode workload (direct rows) at T = 0.6 and T = 1.5."""
     c = gen.decode_peaked()
@@ -265,10 +310,12 @@ def _shard_bounds(vocab, n_shards, rng):
     return list(zip(b[:-1], b[1:]))
 
 
-def _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds):
+def _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds, top_k=None):
     dev = torch.device("cuda")
     has_logits = logits is not None
     plan = R.Plan(off, echo, top_n, ntl.shape[1], has_logits, levels=levels)
+    if top_k is not None:
+        plan.set_top_k(top_k)
     words = plan.info()["record_words"]
     lp, ids, ws = R.alloc_outputs(plan, dev, torch)
     stream = torch.cuda.current_stream()
@@ -316,6 +363,20 @@ def test_vocab_shards_edges(R, vocab, n_shards, levels):
     assert_parity(*got, ref, f"shard edges vocab={vocab} n={n_shards}")
 
 
+@pytest.mark.parametrize("levels", [3, 5])
+def test_vocab_shards_top_k(R, levels):
+    """The top-k front end applied after the shard merge."""
+    vocab = 20011
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(41 + levels, vocab, levels)
+    cap = LO.max_top_n(levels)
+    top_k = np.array([1, cap, 2, 0, cap // 2, 3])[: len(top_n)]
+    bounds = _shard_bounds(vocab, 4, np.random.default_rng(levels))
+    ref = LO.compute_log_probabilities_ragged(off, logits, ntl, tokens, sampled, list(top_n),
+                                              list(echo), levels=levels, batch_top_k=top_k)
+    got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds, top_k)
+    assert_parity(*got, ref, f"shards top_k levels={levels}")
+
+
 def test_vocab_shards_padding_only(R):
     """Every top_n 0: the merge pads every row without reading records."""
     off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(5, 300, 3)
@@ -343,14 +404,20 @@ def _same_value(a, b):
 
 @pytest.mark.parametrize("levels", [1, 3, 5])
 @pytest.mark.parametrize("vocab", [5, 1027, 32000])
-def test_log_probabilities_objects(R, levels, vocab):
+@pytest.mark.parametrize("with_top_k", [False, True])
+def test_log_probabilities_objects(R, levels, vocab, with_top_k):
     """The whole call: device path, copy back and host assembly
     (lp_assemble_ragged) against the oracle's rows and its compute_top."""
-    log(f"log_probabilities_ragged levels={levels} vocab={vocab}")
+    log(f"log_probabilities_ragged levels={levels} vocab={vocab} top_k={with_top_k}")
     off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(7 * levels + vocab, vocab, levels)
+    top_k = None
+    if with_top_k:
+        top_k = np.minimum(np.array([2, 1, 3, 5, 1, 4])[: len(top_n)], LO.max_top_n(levels))
     got = R.log_probabilities_ragged(off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
-                                     levels=levels)
-    ref_lp, ref_ids, ref_off = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+                                     levels=levels, top_k=top_k)
+    ref_lp, ref_ids, ref_off = LO.compute_log_probabilities_ragged(
+        off, logits, ntl, tokens, sampled, list(top_n), list(echo), levels=levels,
+        batch_top_k=top_k)
     want = LO.assemble(ref_lp, ref_ids, ref_off, top_n, vocab)
     assert len(got) == len(want)
     for n, (g, w) in enumerate(zip(got, want)):

@@ -392,6 +392,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     static_assert(kK >= 1 && kK < kWave, "one lane per column");
     __shared__ float s_lmax[kThreads];
     __shared__ uint64_t s_keys[kWaves * kK];
+    __shared__ uint64_t s_top[kK];
     __shared__ uint64_t s_T;
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
@@ -636,15 +637,36 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
     lds_acquire();
 
-    constexpr int kPer = (kWaves * kK + kWave - 1) / kWave;
-    uint64_t e[kPer];
+    constexpr int kN = kWaves * kK;
+    constexpr int kPer = (kN + kWave - 1) / kWave;
+    uint64_t top;
+    if constexpr (kPer == 1) {
+        // at most one key per lane: each key's rank is the number of keys
+        // above it (the keys are distinct but for empty slots, 0), counted
+        // with broadcast reads and independent compares rather than kK
+        // rounds of wave-wide maxima; the best kK go to their rank
+        // (lanes exchange values through s_top: the fences keep the
+        // compiler from forwarding a lane's own store to its read-back)
+        if (lane < kK) s_top[lane] = 0ull;
+        const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
+        lds_release();
+        if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_top[lane] : 0ull;
+    } else {
+        uint64_t e[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < uint32_t(kWaves * kK) ? s_keys[idx] : 0ull;
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t idx = uint32_t(lane + kWave * i);
+            e[i] = idx < uint32_t(kN) ? s_keys[idx] : 0ull;
+        }
+        uint32_t found;
+        top = wave_select<kK, kPer>(e, lane, &found);
     }
-    uint32_t found;
-    const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {
         M = s_m[lane];

@@ -227,6 +227,8 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
 // in LDS, which every wave raises (atomic max) whenever its own bound rises:
 // any wave's 7th key bounds the whole row, since the 7 keys above it are real
 // elements of the row.  A seed starts T off from the first chunks' lane maxima.
+// For 31 or more slots the waves also publish one sorted position of their
+// lists, whose minimum over the waves bounds the row more tightly.
 
 // The smallest value a key above T can have (below the key of -inf, nothing
 // is excluded): a float compare with it is a superset test for candidates,
@@ -394,6 +396,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ uint64_t s_keys[kWaves * kK];
     __shared__ uint64_t s_top[kK];
     __shared__ uint64_t s_T;
+    __shared__ uint64_t s_pub[kWaves];
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
 
@@ -402,6 +405,9 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: loop control stays scalar
     const uint32_t o = blockIdx.x / a.split;
     const uint32_t seg = blockIdx.x - o * a.split;
+    constexpr int kPubJ = (kK + kWaves - 1) / kWaves - 1;        // published slot
+    constexpr int kPubM = (kK + kPubJ) / (kPubJ + 1);           // waves needed
+    constexpr bool kPubBound = kK >= 31 && kPubM >= kWaves - 1;  // its min or second min
     const RowDesc d = load_desc_uniform(a.desc, o);
 
     if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads record rows)
@@ -526,6 +532,24 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
             cols &= cols - 1;
             column(xv[j], lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u), tv);
         }
+        if constexpr (kPubBound) {
+            // A bound from every wave's (kPubJ+1)-th key: kPubM of them at or
+            // above x mean kPubM * (kPubJ + 1) >= kK real keys at or above x
+            // (the waves' shares are disjoint, and a published key only
+            // grows, so stale reads are weaker, never wrong).  Tighter than
+            // the largest K-th key of one wave; it pays only for large K.
+            const uint64_t mine = readlane_u64(list, kPubJ);
+            if (lane == 0) __hip_atomic_store(&s_pub[wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            uint64_t lo1 = ~0ull, lo2 = ~0ull;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const uint64_t v = w == wave ? mine : __hip_atomic_load(&s_pub[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                lo2 = v < lo1 ? lo1 : (v < lo2 ? v : lo2);
+                lo1 = v < lo1 ? v : lo1;
+            }
+            const uint64_t b = uniform64(kPubM == kWaves ? lo1 : lo2);
+            T = umax64(T, b);
+        }
         if (T != T0 && lane == 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
@@ -549,6 +573,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // LDS set-up (before any data can have arrived, so the barrier costs only
     // the spread of the waves' start)
     s_lmax[tid] = -INFINITY;
+    if (tid < kWaves) s_pub[tid] = 0;
     if (tid == 0) {
         s_T = 0;
         s_done = 0;

@@ -3,34 +3,34 @@
 //
 // What is computed follows [MAX] "MAX Python SDK 中 log_probabilities 模块解析：
 // ragged 批量 Token 对数概率的计算图构建与执行" (§log_probabilities_ragged_graph:
-// per output row, 7 ranked slots plus one slot for the chosen token; §图支持的
-// 最大 top-n: top_n <= 7) and [SGL] "logprob、finish reason 与 output
-// processing" (§logprob 的数值形态: a logprob is log p, so <= 0).  The pages keep
-// the 7 candidates in a min-heap; this file does not.  On gfx950 the work is an
-// HBM stream with a few VALU ops per element, so the design aims at reading
-// each logit exactly once with 16-byte loads and doing as little per element
-// as possible:
+// per output row, 2^levels - 1 ranked slots plus one slot for the chosen
+// token; §图支持的最大 top-n: top_n <= 2^levels - 1) and [SGL] "logprob、finish
+// reason 与 output processing" (§logprob 的数值形态: a logprob is log p, so
+// <= 0), with the FlashInfer page's Temperature and TopK-then-Softmax as
+// options.  The pages keep the candidates in a min-heap; this file does not.
+// On gfx950 the work is an HBM stream with a few VALU ops per element, so the
+// design aims at reading each logit exactly once with 16-byte loads and doing
+// as little per element as possible:
 //
-//  * Each row (or row segment) is one workgroup of 4, 8 or 16 waves.  Waves
-//    take interleaved chunks of 64 lanes x kU float4, read with nontemporal
-//    buffer loads, two chunks in flight per wave.  Per chunk a lane reduces
-//    its 16 values to a chunk max and updates a running (m, s) with
-//    s = sum e^(x-m) (exp2 with log2(e) applied after an exact subtraction).
+//  * Each row (or row segment, or vocabulary shard) is one workgroup of 4, 8
+//    or 16 waves.  Waves take interleaved chunks of 64 lanes x kU float4,
+//    read with nontemporal buffer loads, one or two chunks in flight per
+//    wave.  Per chunk a lane reduces its 16 values to a chunk max and updates
+//    a running (m, s) with s = sum 2^((x - m) log2(e) / T), the subtraction
+//    first.
 //  * Ranking uses a 64-bit order key: the fp32 bits mapped to an unsigned
 //    order (with -0.0 folded onto +0.0) in the high word, the complemented
 //    token id in the low word.  A larger key is a better (value, id) pair, so
 //    ties go to the lowest id and every merge uses one total order.
-//  * The workgroup keeps one shared list of the 7 best keys entered so far in
-//    LDS, filled by cascades of atomic max operations, and every wave filters
-//    its chunks against one bound T: a seed taken from all waves' first
-//    chunks (one barrier), raised to the list's 7th key as it fills.  A chunk
-//    whose lane maxima stay below T costs one compare; the few columns that
-//    beat it enter their keys one at a time.
-//  * The waves' (m, s) pairs merge through LDS; the last wave to finish
-//    writes lp = x - (m + ln s) for the 7 listed keys and the chosen token.
-//  * With too few rows to fill 256 CUs, a row is split into segments, one
-//    workgroup each, which write (m, s, 7 keys) records; a second kernel (one
-//    wave per row) merges a row's records in segment order and writes it.
+//  * Each wave keeps its K best keys sorted across lanes 0..K-1 and filters
+//    its chunks against a bound T (its own K-th key, a workgroup maximum of
+//    such keys in LDS, and a seed from the first chunks' lane maxima).  A
+//    chunk whose lane maxima stay below T costs one compare; the few columns
+//    that beat it enter their keys one at a time.
+//  * The waves' lists and (m, s) pairs meet in LDS; the last wave to finish
+//    selects the K best and writes lp = (x - M) / T - ln S for them and for
+//    the chosen token, or, for segments and shards, a record of (M, S, K
+//    keys, chosen logit) that a second kernel (one wave per row) merges.
 //
 // No MFMA: there is no contraction here.
 #include <hip/hip_runtime.h>
@@ -220,13 +220,14 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
 
 // ------------------------------------------------------------------ candidates
 //
-// Each wave keeps the 7 best keys it has seen, sorted, one per lane in lanes
-// 0..6 (0 = empty).  A wave filters its elements against a bound T: a key at
-// or below T cannot be in the row's top 7, because 7 real keys above it are
-// known.  T is the larger of the wave's own 7th key and a workgroup-wide bound
-// in LDS, which every wave raises (atomic max) whenever its own bound rises:
-// any wave's 7th key bounds the whole row, since the 7 keys above it are real
-// elements of the row.  A seed starts T off from the first chunks' lane maxima.
+// Each wave keeps the K best keys it has seen (K = 2^levels - 1, 7 by
+// default), sorted, one per lane in lanes 0..K-1 (0 = empty).  A wave filters
+// its elements against a bound T: a key at or below T cannot be in the row's
+// top K, because K real keys above it are known.  T is the larger of the
+// wave's own K-th key and a workgroup-wide bound in LDS, which every wave
+// raises (atomic max) whenever its own bound rises: any wave's K-th key bounds
+// the whole row, since the K keys above it are real elements of the row.  A
+// seed starts T off from the first chunks' lane maxima.
 // For 31 or more slots the waves also publish one sorted position of their
 // lists, whose minimum over the waves bounds the row more tightly.
 

@@ -506,6 +506,43 @@ def test_staging_pool_plans_in_flight(R):
         assert_parity(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2], ref, f"plan {i} in flight")
 
 
+def test_staging_pool_two_threads(R):
+    """Two host threads call the library at once, each on its own stream:
+    the pinned staging pool (a mutex-guarded process-wide list) hands each
+    upload its own slot, and every result matches the oracle."""
+    import threading
+
+    batches = [_levels_batch(700 + i, 5000 + 3000 * i, 3, rows_per_req=(2 + i, 5, 1, 3))
+               for i in range(2)]
+    refs = [oracle(*b) for b in batches]
+    dev_inputs = [(_dev(b[1]), _dev(b[2])) for b in batches]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            off, _, _, tokens, sampled, top_n, echo = batches[i]
+            lg, nt = dev_inputs[i]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for it in range(25):
+                    lp, ids, out_off = R.compute_log_probabilities_ragged(
+                        off, lg, nt, tokens, sampled, top_n, echo, stream=stream)
+                    stream.synchronize()
+                    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), out_off, refs[i],
+                                  f"thread {i} call {it}")
+        except Exception as e:          # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    assert not any(t.is_alive() for t in threads), "a worker did not finish"
+    assert not errors, errors[0]
+
+
 def test_deterministic_and_split_independent(R):
     c = gen.ragged_echo_mix(seed=9, batch=6, lmin=30, lmax=90)
     logits = _dev(gen.host_logits(c))

@@ -368,15 +368,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the device code (the kernels' namespace in the HIP source):
-    host-side edits leave recorded counters valid; the launch shape is
-    checked separately."""
+    """Hash of the device code (the kernels' namespace in the HIP source,
+    comments and blank lines left out): host-side and comment edits leave
+    recorded counters valid; the launch shape is checked separately."""
     import hashlib
+
+    import re
 
     with open(KERNEL_SOURCE, "rb") as f:
         text = f.read()
     begin, end = text.index(b"namespace dev {"), text.index(b"}  // namespace dev")
-    return hashlib.sha256(text[begin:end]).hexdigest()[:16]
+    code = re.sub(rb"//[^\n]*", b"", text[begin:end])             # comments do not count
+    code = b"\n".join(line.rstrip() for line in code.splitlines() if line.strip())
+    return hashlib.sha256(code).hexdigest()[:16]
 
 
 def shape_text(info):

@@ -124,8 +124,8 @@ def _u32(a, n=None):
 
 
 def _ptr(arr, ctype=None):
-    """The address of a contiguous host array of `ctype` elements (None for
-    NULL)."""
+    """The address of a contiguous host array (None for NULL); ``ctype``
+    only names the element type the C side expects."""
     return None if arr is None else arr.ctypes.data
 
 
@@ -232,7 +232,9 @@ class Plan:
         _check(self._lib.lp_plan_set_top_k(self._h, _ptr(k, ctypes.c_int32)), "lp_plan_set_top_k")
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
-        """(R, 4) uint32: logits row read, chosen token, top_n, 0."""
+        """(R, 4) uint32, as the device reads them: logits row read, chosen
+        token, top_n | k << 16 (k the top-k front end), fp32 bits of
+        1 / temperature."""
         tok = _u32(tokens) if tokens is not None else None
         smp = _u32(sampled_tokens, self.batch)
         out = np.zeros((self.out_rows, 4), dtype=np.uint32)
@@ -421,6 +423,21 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     """
     import torch
 
+    plan = _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo,
+                         levels, temperature, top_k, torch)
+    try:
+        lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
+                       depth, stream, torch)
+        out_off = plan.out_off.copy()
+    finally:
+        plan.close()   # host memory only: the enqueued work does not depend on the plan
+    return lp, ids, out_off
+
+
+def _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo, levels,
+                  temperature, top_k, torch) -> Plan:
+    """Checks the device tensors (2-D fp32 contiguous on one GPU, matching
+    rows and vocabulary) and plans the batch with its options."""
     off = np.asarray(input_row_offsets)
     if off.ndim != 1:
         raise LogprobError(3, "input_row_offsets must be 1-D")
@@ -438,12 +455,10 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
             plan.set_temperature(temperature)
         if top_k is not None:
             plan.set_top_k(top_k)
-        lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
-                       depth, stream, torch)
-        out_off = plan.out_off.copy()
-    finally:
-        plan.close()   # host memory only: the enqueued work does not depend on the plan
-    return lp, ids, out_off
+    except BaseException:
+        plan.close()
+        raise
+    return plan
 
 
 def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, depth, stream,
@@ -472,18 +487,14 @@ def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, token
     row of the request."""
     import torch
 
-    off = np.asarray(input_row_offsets)
-    vocab = int(next_token_logits.shape[1])
-    plan = Plan(off, batch_echo, batch_top_n, vocab, logits is not None,
-                None if logits is None else int(logits.shape[0]), levels=levels)
+    plan = _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo,
+                         levels, temperature, top_k, torch)
     try:
-        if temperature is not None:
-            plan.set_temperature(temperature)
-        if top_k is not None:
-            plan.set_top_k(top_k)
+        if stream is None:
+            stream = torch.cuda.current_stream(next_token_logits.device)
         lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, None, None, None,
                        stream, torch)
-        torch.cuda.synchronize(lp.device)
+        stream.synchronize()
         lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
         toks, vals, counts = plan.assemble(lp_h, ids_h)
         out_off = plan.out_off.copy()

@@ -29,7 +29,7 @@ void size_workspace(lp_plan &p) {
 
 // Kernel shape: waves per workgroup, chunks in flight per wave and
 // vocabulary segments per row.  Rows are independent, so a launch with many
-// rows runs one workgroup of 4 waves per row, two chunks in flight per wave.
+// rows runs one workgroup per row, its shape by row length (measured below).
 // A few hundred rows (two or three workgroups per CU) run 8 waves with one
 // chunk in flight each: their whole batch is in flight at once, and fewer
 // bytes queued per wave shorten the last rows' wait.  Fewer rows than CUs
@@ -296,7 +296,11 @@ lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_
         float value;
     };
     std::vector<Entry> e;
-    e.reserve(C);
+    try {
+        e.reserve(C + 1);   // a row's entries and the chosen token: no reallocation below
+    } catch (...) {
+        return LP_ERR_NOMEM;
+    }
     for (uint32_t n = 0; n < plan->batch; ++n) {
         const int32_t top_n = plan->top_n[n];
         for (uint64_t o = plan->out_off[n]; o < plan->out_off[n + 1]; ++o) {

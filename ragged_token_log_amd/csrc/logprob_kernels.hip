@@ -39,6 +39,7 @@
 #include <cstring>
 #include <memory>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "lp_internal.h"
@@ -874,7 +875,13 @@ static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) 
         fit = small;
     }
     if (fit == nullptr) {
-        auto sl = std::make_unique<StagingSlot>();
+        std::unique_ptr<StagingSlot> sl(new (std::nothrow) StagingSlot());
+        if (!sl) return LP_ERR_NOMEM;
+        try {
+            g_staging.reserve(g_staging.size() + 1);   // the push below cannot throw then
+        } catch (...) {
+            return LP_ERR_NOMEM;
+        }
         LP_HIP_TRY(hipHostMalloc(&sl->host, bytes, hipHostMallocDefault));
         const hipError_t e = hipEventCreateWithFlags(&sl->done, hipEventDisableTiming);
         if (e != hipSuccess) {

@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ragged_echo_mix")
     ap.add_argument("--split", type=int, default=None, help="force the plan's split")
-    ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8)")
+    ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8|16)")
     ap.add_argument("--levels", type=int, default=3,
                     help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
     ap.add_argument("--top-n", type=int, default=None,

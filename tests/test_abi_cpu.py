@@ -305,3 +305,25 @@ def test_top_k_in_descriptors_and_errors():
     wide = R.Plan(off, [1, 0, 0], [3, 2, 0], 500, True, levels=6)
     wide.set_top_k([63, 1, 0])
     _expect("LP_ERR_TOP_K", lambda: wide.set_top_k([64, 0, 0]))
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as C11 and a C program linked against the library
+    plans, inspects, assembles and reports errors with no GPU."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(R.binding.LIB_PATH)
+    exe = tmp_path / "c_abi_check"
+    build = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I",
+                            os.path.join(root, "include"),
+                            os.path.join(root, "tests", "native", "c_abi_check.c"),
+                            "-L", lib_dir, "-llogprob", "-lm", f"-Wl,-rpath,{lib_dir}",
+                            "-o", str(exe)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip().endswith("ok"), run.stdout + run.stderr

@@ -221,8 +221,11 @@ def log_softmax_f64(row, temperature: float = 1.0) -> tuple[np.ndarray, float]:
     x = np.asarray(row, dtype=np.float64) / np.float64(temperature)
     m = np.max(x)
     with np.errstate(invalid="ignore"):
-        lse = m + np.log(np.sum(np.exp(x - m)))
-        return x - lse, float(lse)
+        d = x - m                           # exact for the max and its ties
+        log_sum = np.log(np.sum(np.exp(d)))
+        # (x - m) - log sum is log p with nothing absorbed into a huge m
+        # (m + log sum would round log sum away once |m| passes ~1e16)
+        return d - log_sum, float(m + log_sum)
 
 
 def rank_descending(row_f32) -> np.ndarray:
@@ -267,10 +270,11 @@ def compute_row(row_f32, chosen: int, top_n: int, cols: int, temperature: float 
         lp[kept], _ = log_softmax_f64(x[kept], temperature)
         listed = kept
     take = listed[: min(top_n, x.shape[0], cols - 1)]
-    for j, t in enumerate(take):
-        lp_out[j] = np.float32(lp[t])
-        id_out[j] = t
-    lp_out[cols - 1] = np.float32(lp[chosen])
+    with np.errstate(over="ignore"):      # beyond the fp32 range a logprob rounds to -inf
+        for j, t in enumerate(take):
+            lp_out[j] = np.float32(lp[t])
+            id_out[j] = t
+        lp_out[cols - 1] = np.float32(lp[chosen])
     id_out[cols - 1] = chosen
     return lp_out, id_out
 

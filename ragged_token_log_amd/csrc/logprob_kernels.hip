@@ -317,9 +317,12 @@ struct RowArgs {
 
 // log p = (x - M) / temperature - ln S for a row whose max is M and whose
 // S = sum of e^((x - M) / temperature): the subtraction comes first, so a
-// large common offset of the row costs no accuracy.
+// large common offset of the row costs no accuracy, and it is done in fp64,
+// so logits at opposite ends of the fp32 range still give the finite value
+// that the division by a large temperature brings back into range (a few
+// lanes per row: the cost is nil).
 __device__ __forceinline__ float logprob(float x, float M, float inv_temp, float ln_s) {
-    return (x - M) * inv_temp - ln_s;
+    return float((double(x) - double(M)) * double(inv_temp) - double(ln_s));
 }
 
 // One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK

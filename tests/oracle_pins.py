@@ -435,6 +435,22 @@ def pin_temperature():
     for T in (0.3, 4.0):
         lp, _ = LO.log_softmax_f64(np.full(1000, 2.5, np.float32), T)
         assert np.allclose(lp, -math.log(1000), atol=1e-12)
+    # k tied maxima near the top of the float32 range, the rest far below:
+    # each tie has p = 1/k exactly, so log p = -ln k at any T, however large
+    # x / T gets (a log-sum added to a huge maximum would round ln k away)
+    big = np.float32(3.0e38)
+    for k in (2, 5, 64):
+        x = np.concatenate([np.full(k, big, np.float32),
+                            np.array([0.0, -big, 1e-45], np.float32)])
+        for T in (0.01, 1.0, 100.0):
+            lp, _ = LO.log_softmax_f64(x, T)
+            assert np.all(np.abs(lp[:k] + math.log(k)) < 1e-12), (k, T, lp[:k])
+            lo = LO.compute_row(x, k, 7, 8, T)[0]
+            assert np.all(lo[:min(k, 7)] == np.float32(-math.log(k))), (k, T, lo)
+            # the zero logit sits 3e38 / T below the ties
+            with np.errstate(over="ignore"):          # -3e40 rounds to -inf
+                want = np.float32(-3.0e38 / T - math.log(k))
+            assert lo[7] == want, (k, T, lo[7])
     # brute force at 50 digits on x / T
     rng = np.random.default_rng(17)
     for T in (0.2, 0.7, 3.0):

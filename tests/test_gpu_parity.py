@@ -506,6 +506,47 @@ def test_staging_pool_plans_in_flight(R):
         assert_parity(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2], ref, f"plan {i} in flight")
 
 
+@pytest.mark.parametrize("temperature", [0.01, 1.0, 100.0])
+def test_extreme_values(R, temperature):
+    """Logits at the ends of the fp32 range, subnormals and signed zeros, at
+    temperatures where (x - max) / T overflows: log-probabilities that
+    overflow fp32 become -inf on both sides, the rest agree."""
+    rng = np.random.default_rng(int(temperature * 100) + 5)
+    vocab = 4099
+    rows = []
+    big = np.float32(3.0e38)
+    for kind in range(6):
+        x = (rng.standard_normal(vocab) * 3).astype(np.float32)
+        if kind == 0:
+            x[rng.integers(vocab, size=5)] = big
+            x[rng.integers(vocab, size=5)] = -big
+        elif kind == 1:
+            x = (rng.standard_normal(vocab) * 1e30).astype(np.float32)
+        elif kind == 2:
+            x = (rng.standard_normal(vocab) * 1e-39).astype(np.float32)   # subnormals
+        elif kind == 3:
+            x = np.where(rng.random(vocab) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+            x[rng.integers(vocab)] = np.float32(1e-45)
+        elif kind == 4:
+            x[:] = -big
+            x[rng.integers(vocab)] = big
+        rows.append(x)
+    logits = np.stack(rows)
+    off = np.arange(len(rows) + 1, dtype=np.uint32)
+    tokens = rng.integers(0, vocab, len(rows)).astype(np.uint32)
+    sampled = rng.integers(0, vocab, len(rows)).astype(np.uint32)
+    top_n = np.full(len(rows), 7)
+    echo = np.ones(len(rows), bool)
+    temps = [temperature] * len(rows)
+    ref = LO.compute_log_probabilities_ragged(off, logits, logits, tokens, sampled, list(top_n),
+                                              list(echo), batch_temperature=temps)
+    lp, ids, out_off = R.compute_log_probabilities_ragged(off, _dev(logits), _dev(logits), tokens,
+                                                          sampled, top_n, echo, temperature=temps)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref[1])
+    _assert_close_rel(lp.cpu().numpy(), ref[0], f"extreme values T={temperature}")
+
+
 def test_staging_pool_two_threads(R):
     """Two host threads call the library at once, each on its own stream:
     the pinned staging pool (a mutex-guarded process-wide list) hands each

@@ -49,6 +49,16 @@ def _lsm_dropped_max(row, temperature=1.0):
         return x - lse, float(lse)
 
 
+def _lsm_sum_added_to_max(row, temperature=1.0):
+    # the same log-softmax with the log-sum added to the maximum before the
+    # subtraction: exact on paper, but ln k vanishes beside a maximum of 3e40
+    x = np.asarray(row, dtype=np.float64) / temperature
+    m = np.max(x)
+    with np.errstate(invalid="ignore"):
+        lse = m + np.log(np.sum(np.exp(x - m)))
+        return x - lse, float(lse)
+
+
 def _tasks_chosen_same_position(off, echo, top_n, tokens, sampled, has_logits):
     tasks = _orig["row_tasks"](off, echo, top_n, tokens, sampled, has_logits)
     out, o = [], 0
@@ -179,6 +189,7 @@ MUTANTS = {
     "lse_no_shift": ("log_softmax_f64", _lsm_no_shift),
     "logprob_sign": ("log_softmax_f64", _lsm_wrong_sign),
     "lse_dropped_max": ("log_softmax_f64", _lsm_dropped_max),
+    "lse_sum_added_to_max": ("log_softmax_f64", _lsm_sum_added_to_max),
     "chosen_same_position": ("row_tasks", _tasks_chosen_same_position),
     "echo_first_rows": ("row_tasks", _tasks_first_rows),
     "counts_swapped": ("output_counts_and_offsets", _counts_swapped),

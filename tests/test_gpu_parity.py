@@ -470,6 +470,93 @@ def test_tie_edge_stress_full_size(R):
     _full_size(R, gen.tie_edge_stress(), 60, 51)
 
 
+_BEYOND_2P24 = {}
+
+
+def _beyond_2p24_case():
+    """Three rows of 2^24 + 37 entries and the oracle's result for them
+    (computed once: the oracle sorts each row in full)."""
+    if not _BEYOND_2P24:
+        vocab = (1 << 24) + 37
+        b = 1 << 24
+        rng = np.random.default_rng(24)
+        x0 = (rng.standard_normal(vocab) * 2).astype(np.float32)
+        for i in (vocab - 1, b + 1, b - 1, 5):
+            x0[i] = 20.0                         # equal maxima on both sides of 2^24
+        x1 = (rng.integers(-3, 4, vocab) * 0.5).astype(np.float32)
+        x1[b - 3: b + 30] = 9.0                   # a run of ties straddling 2^24
+        x2 = np.full(vocab, -np.inf, np.float32)
+        x2[[b, b + 2, vocab - 1, vocab - 5]] = np.array([1.0, 2.0, 2.0, -1.0], np.float32)
+        logits = np.stack([x0, x1, x2])
+        off = np.array([0, 1, 3], np.uint32)      # request 0: one row; request 1: two rows, echo
+        echo = np.array([False, True])
+        top_n = np.array([7, 7])
+        ntl = logits[off[1:].astype(np.int64) - 1]
+        tokens = np.array([b + 7, 3, b + 2], np.uint32)
+        sampled = np.array([vocab - 1, b + 5], np.uint32)
+        args = (off, logits, ntl, tokens, sampled, top_n, echo)
+        _BEYOND_2P24.update(vocab=vocab, args=args, ref=oracle(*args))
+    return _BEYOND_2P24
+
+
+@pytest.mark.parametrize("split", [None, 5])
+def test_ids_beyond_float_exact_integers(R, split):
+    """Rows of 2^24 + 37 entries: ids above 2^24, past the integers float32
+    holds exactly, rank, break ties by id across that boundary, fill the
+    chosen slot and pass through the segment records (split 5) like any
+    other id.  Every row is compared with the oracle in full."""
+    log(f"ids beyond 2^24: split={split}")
+    case = _beyond_2p24_case()
+    vocab, b = case["vocab"], 1 << 24
+    off, logits, ntl, tokens, sampled, top_n, echo = case["args"]
+    got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
+                      split=split)
+    assert_parity(*got, case["ref"], f"ids beyond 2^24 split={split}")
+    assert got[1][0, :4].tolist() == [5, b - 1, b + 1, vocab - 1]
+    assert got[1][1, :7].tolist() == list(range(b - 3, b + 4))
+
+
+@pytest.mark.parametrize("vocab,split", [((1 << 28) + 5, None), ((1 << 28) + 5, 2), (1 << 28, 1)])
+def test_rows_at_the_segment_limit(R, vocab, split):
+    """One row of 2^28 (+ 5) entries: the most one workgroup streams is 2^28
+    (split 1 at 2^28), a longer row is cut into segments (the default plan,
+    or 2 forced) and the record merge returns the planted maxima from all
+    of them.  The planted values are the only entries at or above 9.5
+    (counted on the host), which fixes the ranking; the log-probabilities
+    are the oracle's log-softmax of the whole row."""
+    log(f"row at the segment limit: vocab={vocab} split={split}")
+    rng = np.random.default_rng(vocab)
+    x = rng.standard_normal(vocab, dtype=np.float32)
+    planted = [(3, 12.0), (vocab - 1, 12.0), (vocab - 4, 11.5), (vocab // 2 + 2, 11.0),
+               (100, 10.0), (vocab - 2, 10.0), (77777777, 9.5)]
+    for i, v in planted:
+        x[i] = v
+    assert np.count_nonzero(x >= 9.5) == len(planted)
+    want_ids = [i for i, _ in sorted(planted, key=lambda p: (-p[1], p[0]))]
+    off = np.array([0, 1], np.uint32)
+    echo = np.array([False])
+    top_n = np.array([7])
+    chosen = vocab - 3
+    plan = R.Plan(off, echo, top_n, vocab, False)
+    if split is not None:
+        plan.set_split(split)
+    info = plan.info()
+    plan.close()
+    assert split is None or info["split"] == split
+    assert vocab <= 1 << 28 or info["split"] >= 2
+    xd = _dev(x[None, :])
+    lp, ids, out_off = run_library(R, torch, off, None, xd, np.zeros(1, np.uint32),
+                                   np.array([chosen], np.uint32), top_n, echo, split=split)
+    del xd
+    torch.cuda.empty_cache()
+    log("row at the segment limit: library done")
+    assert out_off.tolist() == [0, 1]
+    assert ids[0].tolist() == want_ids + [chosen]
+    ref_lp, _ = LO.log_softmax_f64(x)
+    want_lp = ref_lp[np.array(want_ids + [chosen])].astype(np.float32)
+    assert_lp_close(lp[0], want_lp, f"row at the segment limit vocab={vocab} split={split}")
+
+
 @pytest.mark.parametrize("vocab,waves,depth", [(32000, 8, 1), (128256, 16, 1)])
 def test_many_rows_row_length_shapes(R, vocab, waves, depth):
     """Thousands of rows of the widths whose default shape differs (8 waves

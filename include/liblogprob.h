@@ -2,8 +2,9 @@
  * liblogprob -- ragged batched token log-probabilities on MI355X (gfx950).
  *
  * For every selected fp32 logits row the library computes, over the whole
- * vocabulary, the log-softmax, the top-n (n <= 7) log-probabilities with their
- * token ids, and the log-probability of the chosen token in one extra slot.
+ * vocabulary, the log-softmax, the top-n (n <= 2^levels - 1: 7 at the default
+ * levels = 3, up to 63 at levels = 6) log-probabilities with their token ids,
+ * and the log-probability of the chosen token in one extra slot.
  *
  * Pages the contract follows:
  *   [MAX] "MAX Python SDK 中 log_probabilities 模块解析：ragged 批量 Token 对数概率的
@@ -55,12 +56,12 @@ typedef enum lp_status {
     LP_ERR_TOP_N_TOO_LARGE = 5,   /* some top_n > 2^levels - 1 ([MAX] §图支持的最大 top-n) */
     LP_ERR_ECHO_NEEDS_LOGITS = 6, /* echo requested without full logits ([MAX] §echo 的前置条件) */
     LP_ERR_TOKEN_RANGE = 7,       /* a token or sampled token >= vocab */
-    LP_ERR_UNSUPPORTED = 8,       /* levels != 3, or a split outside 1..64 */
+    LP_ERR_UNSUPPORTED = 8,       /* levels > 6, or a split, wave count or depth
+                                     the kernels do not provide */
     LP_ERR_WORKSPACE = 9,         /* workspace NULL or smaller than the plan asks */
     LP_ERR_HIP = 10,              /* a HIP runtime call failed; see lp_last_hip_error() */
     LP_ERR_NOMEM = 11,            /* host allocation failed */
-    LP_ERR_TEMPERATURE = 12,      /* a temperature that is not a positive finite number
-                                     with a finite reciprocal */
+    LP_ERR_TEMPERATURE = 12,      /* a temperature outside [2^-126, 2^120] (or NaN) */
     LP_ERR_TOP_K = 13             /* a top-k front end outside 0..2^levels - 1 */
 } lp_status;
 
@@ -68,8 +69,8 @@ typedef enum lp_status {
 typedef struct lp_plan_info {
     uint32_t batch;           /* B */
     uint32_t vocab;           /* V */
-    uint32_t levels;          /* 3 */
-    uint32_t columns;         /* 2^levels = 8 */
+    uint32_t levels;          /* 0..6 (3 by default in the bindings) */
+    uint32_t columns;         /* C = 2^levels (1 at levels 0, 8 at levels 3) */
     uint64_t out_rows;        /* R = output_row_offsets[B] */
     uint64_t read_rows;       /* output rows whose request has top_n > 0 (logits rows read) */
     uint32_t split;           /* vocabulary segments per row: 1 = one workgroup per row;
@@ -90,14 +91,16 @@ typedef struct lp_plan_info {
  *
  * [MAX] §compute_log_probabilities_ragged and §ragged 数据编排: validates the
  * per-request arguments, computes the echo-dependent output row counts and
- * their uint32 offsets, and chooses the kernel variant (split).
+ * their uint32 offsets, and chooses the kernel shape (split, waves, depth)
+ * from the number of rows read and the row length.
  *
  *   batch              B (may be 0: nothing to compute)
  *   vocab              V >= 1
- *   levels             must be 3 (C = 8 columns, top_n <= 7)
+ *   levels             0..6: C = 2^levels columns (levels 0: the chosen
+ *                      slot alone), top_n <= C - 1
  *   input_row_offsets  host, B+1 uint32, off[0] = 0, strictly increasing
  *   batch_echo         host, B bytes, nonzero = echo
- *   batch_top_n        host, B int32 in [0, 7]
+ *   batch_top_n        host, B int32 in [0, C - 1]
  *   has_logits         nonzero if full (T, V) logits will be given; then
  *                      logits_rows must equal T.  Zero: only (B, V)
  *                      next_token_logits exist and no request may echo.
@@ -118,9 +121,11 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
 lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info);
 
 /*
- * Overrides the plan's split (vocabulary segments per row, 1..64) and updates
- * its workspace size.  The result does not depend on the split beyond fp32
- * rounding of the log-probabilities: ids and offsets are identical.
+ * Overrides the plan's split (vocabulary segments per row) and updates its
+ * workspace size.  LP_ERR_UNSUPPORTED unless 1 <= split <= min(64,
+ * floor(1024 / (C - 1))) and each segment holds at most 2^28 entries (the
+ * most one workgroup streams).  The result does not depend on the split
+ * beyond fp32 rounding of the log-probabilities: ids and offsets are identical.
  */
 lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
 
@@ -140,7 +145,10 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
  * §output 从 forward() 到响应对象的完整路径 applies before the softmax whose
  * result the logprobs reuse.  The ranking stays on the raw logits (for T > 0
  * it is the same order).  LP_ERR_TEMPERATURE, with the plan unchanged, if
- * some T_n is not positive and finite or 1/T_n is not finite and nonzero.
+ * some T_n lies outside [2^-126, 2^120] (or is NaN): inside it T_n, 1/T_n
+ * and log2(e)/T_n are normal fp32 numbers, and two logits further apart
+ * than the fp32 range (whose difference the kernels take as -inf) differ by
+ * more than 256 after the division.
  * Applies to descriptors built after the call.
  */
 lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature);
@@ -194,8 +202,8 @@ lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens,
  *                      plan has no full logits
  *   next_token_logits  device, (B, V) fp32 row-major; read only when the plan
  *                      has no full logits (may be NULL otherwise)
- *   out_logprobs       device out, (R, 8) fp32
- *   out_token_ids      device out, (R, 8) uint32
+ *   out_logprobs       device out, (R, C) fp32
+ *   out_token_ids      device out, (R, C) uint32
  *   workspace          device, >= workspace_bytes of the plan, 256-byte aligned
  *
  * One kernel launch (two when split > 1).  Enqueue only: no host

@@ -199,16 +199,15 @@ def row_tasks(input_row_offsets, batch_echo, batch_top_n, tokens, sampled_tokens
 
 
 def check_temperature(t) -> float:
-    """A request's temperature: positive and finite (the FlashInfer page's
-    Temperature processor rejects a non-positive value), with a finite,
-    nonzero reciprocal (reading R19)."""
+    """A request's temperature (reading R19): positive, as the FlashInfer
+    page's Temperature processor requires, and within [2^-126, 2^120].  There
+    T, 1/T and log2(e)/T are normal fp32 numbers, and two logits whose
+    difference exceeds the fp32 range (|x - y| > 3.4e38) differ by more than
+    256 after the division, a weight below e^-256.  The bounds also reject
+    NaN and infinities."""
     t = float(np.float32(t))
-    if not (t > 0.0 and math.isfinite(t)):
+    if not (2.0 ** -126 <= t <= 2.0 ** 120):
         raise OracleError("LP_ERR_TEMPERATURE", f"temperature={t}")
-    with np.errstate(over="ignore"):
-        inv = float(np.float32(1.0) / np.float32(t))
-    if not (0.0 < inv < math.inf):
-        raise OracleError("LP_ERR_TEMPERATURE", f"temperature={t}: 1/T not finite")
     return t
 
 

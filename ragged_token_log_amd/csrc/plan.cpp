@@ -256,9 +256,11 @@ lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature)
     }
     for (uint32_t n = 0; n < plan->batch; ++n) {
         const float t = batch_temperature[n];
-        // positive and finite, with a finite, nonzero reciprocal
-        if (!(t > 0.0f) || !(t < 3.0e38f) || !(1.0f / t > 0.0f) || !(1.0f / t < 3.0e38f))
-            return LP_ERR_TEMPERATURE;
+        // within [2^-126, 2^120]: T, 1/T and the kernels' exponent scale
+        // log2(e)/T are normal fp32 numbers, and a logit difference that
+        // overflows fp32 (taken as -inf by the kernels) has a weight below
+        // e^-256 after the division.  NaN fails both compares.
+        if (!(t >= 0x1p-126f && t <= 0x1p120f)) return LP_ERR_TEMPERATURE;
     }
     for (uint32_t n = 0; n < plan->batch; ++n) plan->inv_temp[n] = 1.0f / batch_temperature[n];
     return LP_OK;

@@ -468,7 +468,11 @@ def pin_temperature():
         z = x.astype(np.float64) / T
         ref = z - (z.max() + math.log(np.exp(z - z.max()).sum()))
         assert np.allclose(lp[:7], ref[ids[:7]].astype(np.float32), atol=1e-6)
-    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+    # accepted: [2^-126, 2^120]
+    for good in (2.0 ** -126, 2.0 ** 120, 1e-30, 1e30):
+        assert LO.check_temperature(good) == float(np.float32(good))
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45, 2.0 ** -127, 3.5e-39,
+                2.0 ** 121, 2.0 ** 126, 3.0e38):
         try:
             LO.check_temperature(bad)
         except LO.OracleError as e:

@@ -277,9 +277,14 @@ def test_temperature_in_descriptors_and_errors():
     desc = plan.descriptors(tokens, sampled)
     inv = desc[:, 3].view(np.float32)
     assert inv.tolist() == [2.0, 2.0, 0.5]           # rows of request 0, then request 1
-    for bad in ([0.0, 1.0], [-1.0, 1.0], [np.inf, 1.0], [np.nan, 1.0], [1e-45, 1.0]):
+    for bad in ([0.0, 1.0], [-1.0, 1.0], [np.inf, 1.0], [np.nan, 1.0], [1e-45, 1.0],
+                [2.0 ** -127, 1.0], [1.0, 3.5e-39], [1.0, 2.0 ** 121], [3.0e38, 1.0]):
         _expect("LP_ERR_TEMPERATURE", lambda b=bad: plan.set_temperature(b))
     assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [2.0, 2.0, 0.5]
+    # both ends of the accepted range [2^-126, 2^120]
+    plan.set_temperature([2.0 ** -126, 2.0 ** 120])
+    inv = plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist()
+    assert inv == [2.0 ** 126, 2.0 ** 126, 2.0 ** -120]
     plan.set_temperature(None)
     assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [1.0] * 3
 

@@ -593,12 +593,15 @@ def test_staging_pool_plans_in_flight(R):
         assert_parity(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2], ref, f"plan {i} in flight")
 
 
-@pytest.mark.parametrize("temperature", [0.01, 1.0, 100.0])
+@pytest.mark.parametrize("temperature", [2.0 ** -126, 0.01, 1.0, 100.0, 2.0 ** 120])
 def test_extreme_values(R, temperature):
     """Logits at the ends of the fp32 range, subnormals and signed zeros, at
-    temperatures where (x - max) / T overflows: log-probabilities that
-    overflow fp32 become -inf on both sides, the rest agree."""
-    rng = np.random.default_rng(int(temperature * 100) + 5)
+    temperatures where (x - max) / T overflows, up to both ends of the
+    accepted range [2^-126, 2^120] (at 2^-126 the subnormal row becomes an
+    ordinary distribution; at 2^120 logits 6e38 apart still differ by 451
+    after the division): log-probabilities that overflow fp32 become -inf
+    on both sides, the rest agree."""
+    rng = np.random.default_rng(int(min(temperature, 1e4) * 100) + 5)
     vocab = 4099
     rows = []
     big = np.float32(3.0e38)

@@ -413,7 +413,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     ``levels`` is the heap depth of the MAX page's graph (section
     "log_probabilities_ragged_graph"): C = 2**levels output columns (one at
     levels 0), top_n <= C - 1.  ``temperature`` (a scalar or one per
-    request) gives log_softmax(logits / temperature); None means 1.
+    request, each in [2^-126, 2^120]) gives log_softmax(logits /
+    temperature); None means 1.
     ``top_k`` (a scalar or one per request, 0 or None = none, at most C - 1)
     adds the FlashInfer page's TopK-then-Softmax front end: the k best tokens
     are kept and the log-probabilities renormalised over them.

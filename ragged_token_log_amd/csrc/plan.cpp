@@ -39,8 +39,9 @@ void size_workspace(lp_plan &p) {
 static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t *waves,
                            uint32_t *depth, uint32_t *split) {
     constexpr uint64_t kManyRows = 1024;
-    constexpr uint64_t kSomeRows = 384;
     constexpr uint64_t kCUs = 256;
+    constexpr uint64_t kSplitBelow = 128;
+    constexpr uint32_t kShortRow = 65536;
     constexpr uint32_t kMinSegment = 32768;
     // fewest segments that keep each within kMaxSegment (1 for any real vocabulary)
     uint32_t min_split = 1;
@@ -62,17 +63,29 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         }
         return;
     }
-    if (read_rows >= kSomeRows) {
+    // Below that, measured on decode batches of 32..2048 rows at V = 32000,
+    // 128256, 151936 and 256000 (every waves x depth x split, interleaved):
+    if (read_rows > kCUs) {
+        // more rows than compute units: 8 waves, one chunk deep (2-8 % ahead
+        // of two deep at 320 rows, 1-3 % behind or level at 512)
         *waves = 8;
         *depth = 1;
         return;
     }
-    if (read_rows >= kCUs) {
-        *waves = 8;
-        return;
-    }
+    // one row per compute unit at most: 16 waves one chunk deep on short
+    // rows (3-10 % ahead of two deep), 8 waves two deep on long ones (1-4 %)
+    *waves = vocab <= kShortRow ? 16 : 8;
+    *depth = vocab <= kShortRow ? 1 : 2;
+    if (read_rows >= kSplitBelow) return;
+    // Fewer rows still: each long row is cut into as many segments as keep
+    // the workgroups within one per compute unit (floor, not ceil: a few
+    // compute units holding two segments double the tail), each segment at
+    // least kMinSegment long; 16 waves, one chunk deep.  At 32-96 rows of
+    // 151936 or 256000 this is 7-40 % faster than whole rows; at 128 rows
+    // the merge launch costs more than the split gains.
     *waves = 16;
-    uint64_t s = (kCUs + read_rows - 1) / read_rows;
+    *depth = 1;
+    uint64_t s = kCUs / read_rows;
     uint64_t by_vocab = vocab / kMinSegment;
     if (by_vocab < 1) by_vocab = 1;
     if (s > by_vocab) s = by_vocab;

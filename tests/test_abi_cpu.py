@@ -170,6 +170,23 @@ def test_many_rows_shape_by_row_length(vocab, waves, depth):
     assert (info["split"], info["waves"], info["depth"]) == (1, waves, depth)
 
 
+@pytest.mark.parametrize("rows,vocab,shape", [
+    (4, 32000, (1, 16, 1)), (32, 32000, (1, 16, 1)), (200, 32000, (1, 16, 1)),
+    (32, 128256, (3, 16, 1)), (32, 151936, (4, 16, 1)), (64, 151936, (4, 16, 1)),
+    (32, 256000, (7, 16, 1)), (96, 256000, (2, 16, 1)), (127, 256000, (2, 16, 1)),
+    (128, 128256, (1, 8, 2)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),
+    (257, 128256, (1, 8, 1)), (600, 151936, (1, 8, 1))])
+def test_few_rows_shape(rows, vocab, shape):
+    """Plans of at most 1023 read rows: (split, waves, depth) from the row
+    count and the row length; long rows of small batches are cut into at
+    most one workgroup per compute unit."""
+    plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool), np.full(rows, 7),
+                  vocab, False)
+    info = plan.info()
+    assert (info["split"], info["waves"], info["depth"]) == shape
+    assert rows * info["split"] <= 256 or info["split"] == 1
+
+
 def test_segments_stay_within_the_streamed_range():
     # one workgroup streams at most 2^28 elements of a row: a wider row is
     # always cut into segments, and a split leaving longer segments is refused

@@ -36,22 +36,59 @@ void size_workspace(lp_plan &p) {
 // get more waves per row; too few to occupy 256 CUs even then are split
 // into segments (one workgroup each, at least kMinSegment elements), whose
 // partial results a second kernel merges.
+// Shape of the row kernel (waves per workgroup, chunks in flight per wave,
+// segments per row) from the number of rows read, the row length and the
+// ranked slots.  Measured on gfx950: 34.6k-row sweeps for the first rule,
+// then decode batches of 32..2048 rows at V = 32000, 128256, 151936 and
+// 256000, every waves x depth x split timed in interleaved passes.
+constexpr uint64_t kManyRows = 1024;
+constexpr uint64_t kCUs = 256;
+constexpr uint64_t kSplitBelow = 128;
+constexpr uint32_t kShortRow = 65536;
+constexpr uint32_t kMinSegment = 32768;
+
+// Segments per row for a batch too small to fill the chip: as many as keep
+// the workgroups within one per compute unit (floor, not ceil: a few compute
+// units holding two segments double the tail), each at least kMinSegment
+// long and within what the merge holds.
+static uint32_t few_rows_split(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t min_split) {
+    uint64_t s = kCUs / read_rows;
+    uint64_t by_vocab = vocab / kMinSegment;
+    if (by_vocab < 1) by_vocab = 1;
+    if (s > by_vocab) s = by_vocab;
+    if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
+    if (s < min_split) s = min_split;
+    return static_cast<uint32_t>(s);
+}
+
 static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t *waves,
                            uint32_t *depth, uint32_t *split) {
-    constexpr uint64_t kManyRows = 1024;
-    constexpr uint64_t kCUs = 256;
-    constexpr uint64_t kSplitBelow = 128;
-    constexpr uint32_t kShortRow = 65536;
-    constexpr uint32_t kMinSegment = 32768;
     // fewest segments that keep each within kMaxSegment (1 for any real vocabulary)
     uint32_t min_split = 1;
     while (segment_length(vocab, min_split) > kMaxSegment) ++min_split;
     *split = min_split;
     *depth = 2;
-    if (read_rows >= kManyRows || read_rows == 0) {
-        // Measured on gfx950 with 34.6k rows: 8 waves streaming one chunk at
-        // a time are fastest up to 64K elements per row, 16 waves up to 128K,
-        // and 4 waves two chunks deep beyond.
+    const bool many = read_rows >= kManyRows || read_rows == 0;
+
+    if (slots >= 31) {
+        // Levels 5 and 6: every wave of every segment pays ~K ln(n / K)
+        // insertions, so fewer waves and fewer segments pay.  1024 rows or
+        // more: 4 waves (16-68 % ahead of 8 or 16).  Fewer: 8 waves, whole
+        // rows, except 31 slots over fewer than 128 rows of at least 131072,
+        // which still gain from segments (38 against 43 us at 32 rows of
+        // 256000; at 128256 the split loses 17 %).
+        *waves = many ? 4 : 8;
+        if (!many && slots == 31 && read_rows < kSplitBelow && vocab >= 131072) {
+            *waves = 16;
+            *depth = 1;
+            *split = few_rows_split(read_rows, vocab, slots, min_split);
+        }
+        return;
+    }
+    if (many) {
+        // 8 waves one chunk deep up to 64K entries per row, 16 waves up to
+        // 128K, 4 waves two deep beyond (at 34.6k rows: 636 against 655 us at
+        // 32000, 2504 against 2551 at 128256, 3016 against 3025 at 151936)
         if (vocab <= 65536) {
             *waves = 8;
             *depth = 1;
@@ -63,35 +100,26 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         }
         return;
     }
-    // Below that, measured on decode batches of 32..2048 rows at V = 32000,
-    // 128256, 151936 and 256000 (every waves x depth x split, interleaved):
     if (read_rows > kCUs) {
-        // more rows than compute units: 8 waves, one chunk deep (2-8 % ahead
-        // of two deep at 320 rows, 1-3 % behind or level at 512)
+        // more rows than compute units: 8 waves one chunk deep (2-8 % ahead
+        // of two deep at 320 rows, level at 512)
         *waves = 8;
         *depth = 1;
         return;
     }
-    // one row per compute unit at most: 16 waves one chunk deep on short
-    // rows (3-10 % ahead of two deep), 8 waves two deep on long ones (1-4 %)
-    *waves = vocab <= kShortRow ? 16 : 8;
-    *depth = vocab <= kShortRow ? 1 : 2;
-    if (read_rows >= kSplitBelow) return;
-    // Fewer rows still: each long row is cut into as many segments as keep
-    // the workgroups within one per compute unit (floor, not ceil: a few
-    // compute units holding two segments double the tail), each segment at
-    // least kMinSegment long; 16 waves, one chunk deep.  At 32-96 rows of
-    // 151936 or 256000 this is 7-40 % faster than whole rows; at 128 rows
-    // the merge launch costs more than the split gains.
+    if (read_rows >= kSplitBelow) {
+        // one row per compute unit at most: 16 waves one chunk deep on short
+        // rows (3-10 % ahead of two deep), 8 waves two deep on long ones
+        // (1-4 %); a split's merge launch costs more than it gains here
+        *waves = vocab <= kShortRow ? 16 : 8;
+        *depth = vocab <= kShortRow ? 1 : 2;
+        return;
+    }
+    // fewer rows still: 16 waves one chunk deep over segments (7-40 % ahead
+    // of whole rows at 32-96 rows of 151936 or 256000)
     *waves = 16;
     *depth = 1;
-    uint64_t s = kCUs / read_rows;
-    uint64_t by_vocab = vocab / kMinSegment;
-    if (by_vocab < 1) by_vocab = 1;
-    if (s > by_vocab) s = by_vocab;
-    if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
-    if (s < min_split) s = min_split;
-    *split = static_cast<uint32_t>(s);
+    *split = few_rows_split(read_rows, vocab, slots, min_split);
 }
 
 lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,

@@ -187,6 +187,21 @@ def test_few_rows_shape(rows, vocab, shape):
     assert rows * info["split"] <= 256 or info["split"] == 1
 
 
+@pytest.mark.parametrize("levels,rows,vocab,shape", [
+    (5, 2048, 32000, (1, 4, 2)), (6, 2048, 128256, (1, 4, 2)), (5, 1024, 256000, (1, 4, 2)),
+    (5, 512, 128256, (1, 8, 2)), (6, 32, 256000, (1, 8, 2)), (6, 96, 151936, (1, 8, 2)),
+    (5, 32, 256000, (7, 16, 1)), (5, 64, 151936, (4, 16, 1)), (5, 32, 128256, (1, 8, 2)),
+    (5, 128, 256000, (1, 8, 2)), (4, 32, 151936, (4, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
+def test_shape_by_ranked_slots(levels, rows, vocab, shape):
+    """With 31 or more ranked slots every wave's insertions weigh more: 4
+    waves for many rows, 8 for fewer, segments only for 31 slots over few
+    long rows; 15 slots or fewer keep the shapes of 7."""
+    plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool),
+                  np.full(rows, (1 << levels) - 1), vocab, False, levels=levels)
+    info = plan.info()
+    assert (info["split"], info["waves"], info["depth"]) == shape
+
+
 def test_segments_stay_within_the_streamed_range():
     # one workgroup streams at most 2^28 elements of a row: a wider row is
     # always cut into segments, and a split leaving longer segments is refused

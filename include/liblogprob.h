@@ -130,7 +130,8 @@ lp_status lp_plan_get_info(const lp_plan *plan, lp_plan_info *info);
 lp_status lp_plan_set_split(lp_plan *plan, uint32_t split);
 
 /* Overrides the waves per workgroup (4, 8 or 16); LP_ERR_UNSUPPORTED otherwise.
- * Results do not depend on it beyond fp32 rounding of the log-probabilities. */
+ * Results do not depend on it beyond fp32 rounding of the log-probabilities.
+ * Once waves or depth is set, shard record kernels use the plan's shape too. */
 lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
 
 /* Overrides the chunks in flight per wave (1 or 2); LP_ERR_UNSUPPORTED
@@ -269,7 +270,9 @@ lp_status lp_assemble_ragged(const lp_plan *plan, const float *lp, const uint32_
  *   records    device out, R * record_words 8-byte words, row-major by output
  *              row (rows of top_n == 0 requests are not written)
  *   workspace  as for lp_launch_ragged, after lp_stage_ragged
- * LP_ERR_SHAPE if the range does not fit in [0, V); one kernel launch.
+ * LP_ERR_SHAPE if the range does not fit in [0, V); one kernel launch,
+ * whose workgroup shape is chosen for a row of shard_vocab entries unless the
+ * caller set the plan's waves or depth.
  *
  * lp_merge_shards -- merges, for every output row, num_shards records laid
  * out shard-major: record (s, o) at word (s * R + o) * record_words of

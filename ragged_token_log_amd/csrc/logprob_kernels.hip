@@ -919,13 +919,14 @@ enum class Launch { kRows, kRecords, kMerge, kRecordsThenMerge };
 
 template <int kK>
 static void launch_k(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
-                     const dev::RowArgs &ra, const dev::MergeArgs &ma) {
+                     const dev::RowArgs &ra, const dev::MergeArgs &ma, uint32_t waves,
+                     uint32_t depth) {
     if (what != Launch::kMerge) {
-        const bool deep = p.depth == 2, direct = p.direct_rows != 0;
-        if (p.waves == 16) {
+        const bool deep = depth == 2, direct = p.direct_rows != 0;
+        if (waves == 16) {
             if (deep) launch_shape<kK, 16, 2>(direct, grid, s, ra);
             else launch_shape<kK, 16, 1>(direct, grid, s, ra);
-        } else if (p.waves == 8) {
+        } else if (waves == 8) {
             if (deep) launch_shape<kK, 8, 2>(direct, grid, s, ra);
             else launch_shape<kK, 8, 1>(direct, grid, s, ra);
         } else {
@@ -942,14 +943,15 @@ static void launch_k(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
 // The kernels for the plan's slot count; false if the library is not built
 // for it.
 static bool launch_for_slots(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
-                             const dev::RowArgs &ra, const dev::MergeArgs &ma) {
+                             const dev::RowArgs &ra, const dev::MergeArgs &ma, uint32_t waves,
+                             uint32_t depth) {
     switch (p.slots) {
-        case 1: launch_k<1>(p, what, grid, s, ra, ma); return true;
-        case 3: launch_k<3>(p, what, grid, s, ra, ma); return true;
-        case 7: launch_k<7>(p, what, grid, s, ra, ma); return true;
-        case 15: launch_k<15>(p, what, grid, s, ra, ma); return true;
-        case 31: launch_k<31>(p, what, grid, s, ra, ma); return true;
-        case 63: launch_k<63>(p, what, grid, s, ra, ma); return true;
+        case 1: launch_k<1>(p, what, grid, s, ra, ma, waves, depth); return true;
+        case 3: launch_k<3>(p, what, grid, s, ra, ma, waves, depth); return true;
+        case 7: launch_k<7>(p, what, grid, s, ra, ma, waves, depth); return true;
+        case 15: launch_k<15>(p, what, grid, s, ra, ma, waves, depth); return true;
+        case 31: launch_k<31>(p, what, grid, s, ra, ma, waves, depth); return true;
+        case 63: launch_k<63>(p, what, grid, s, ra, ma, waves, depth); return true;
         default: return false;
     }
 }
@@ -1049,7 +1051,8 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     ma.out_id = out_token_ids;
     const dim3 grid(static_cast<uint32_t>(blocks));
     const lp::Launch what = plan->split > 1 ? lp::Launch::kRecordsThenMerge : lp::Launch::kRows;
-    if (!lp::launch_for_slots(*plan, what, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    if (!lp::launch_for_slots(*plan, what, grid, s, ra, ma, plan->waves, plan->depth))
+        return LP_ERR_UNSUPPORTED;
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }
@@ -1076,7 +1079,9 @@ lp_status lp_shard_records(const lp_plan *plan, uint32_t vocab_begin, uint32_t s
     if (src == nullptr || records == nullptr) return LP_ERR_NULL_ARG;
     lp_status st = lp::check_workspace(plan, workspace, workspace_bytes);
     if (st != LP_OK) return st;
-    if (plan->out_rows * plan->waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
+    uint32_t waves = 0, depth = 0;
+    lp::shard_shape(*plan, shard_vocab, &waves, &depth);
+    if (plan->out_rows * waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     lp::dev::RowArgs ra = lp::row_args(*plan, src, shard_vocab, vocab_begin, 1, workspace);
     ra.records = 1;
@@ -1085,7 +1090,8 @@ lp_status lp_shard_records(const lp_plan *plan, uint32_t vocab_begin, uint32_t s
     ra.rec = records;
     lp::dev::MergeArgs ma{};
     const dim3 grid(static_cast<uint32_t>(plan->out_rows));
-    if (!lp::launch_for_slots(*plan, lp::Launch::kRecords, grid, s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    if (!lp::launch_for_slots(*plan, lp::Launch::kRecords, grid, s, ra, ma, waves, depth))
+        return LP_ERR_UNSUPPORTED;
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }
@@ -1115,7 +1121,8 @@ lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64
     ma.rec = records;
     ma.out_lp = out_logprobs;
     ma.out_id = out_token_ids;
-    if (!lp::launch_for_slots(*plan, lp::Launch::kMerge, dim3(1), s, ra, ma)) return LP_ERR_UNSUPPORTED;
+    if (!lp::launch_for_slots(*plan, lp::Launch::kMerge, dim3(1), s, ra, ma, plan->waves, plan->depth))
+        return LP_ERR_UNSUPPORTED;
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }

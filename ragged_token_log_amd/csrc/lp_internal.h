@@ -79,6 +79,7 @@ struct lp_plan {
     uint32_t split = 1;
     uint32_t waves = 4;              // waves per workgroup: 4, 8 or 16
     uint32_t depth = 2;              // chunks in flight per wave: 1 or 2
+    bool shape_set = false;          // waves or depth set by the caller
     uint32_t direct_rows = 0;        // 1: output row o reads logits row o (all top_n > 0)
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 8 (slots + 2) when split > 1
@@ -91,4 +92,8 @@ lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
                             const uint32_t *sampled, RowDesc *out);
 // Recomputes workspace sizes after a split change.
 void size_workspace(lp_plan &p);
+// Waves and depth for the record kernel of one vocabulary shard of
+// `shard_vocab` columns: chosen for that row length, unless the caller set
+// the plan's shape.
+void shard_shape(const lp_plan &p, uint32_t shard_vocab, uint32_t *waves, uint32_t *depth);
 }  // namespace lp

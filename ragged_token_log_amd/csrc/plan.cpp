@@ -44,6 +44,7 @@ void size_workspace(lp_plan &p) {
 constexpr uint64_t kManyRows = 1024;
 constexpr uint64_t kCUs = 256;
 constexpr uint64_t kSplitBelow = 128;
+constexpr uint32_t kVeryShortRow = 20480;
 constexpr uint32_t kShortRow = 65536;
 constexpr uint32_t kMinSegment = 32768;
 
@@ -86,10 +87,15 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         return;
     }
     if (many) {
-        // 8 waves one chunk deep up to 64K entries per row, 16 waves up to
-        // 128K, 4 waves two deep beyond (at 34.6k rows: 636 against 655 us at
-        // 32000, 2504 against 2551 at 128256, 3016 against 3025 at 151936)
-        if (vocab <= 65536) {
+        // 4 waves one chunk deep up to 20K entries per row, 8 waves up to
+        // 64K, 16 waves up to 128K, 4 waves two deep beyond (at 34.6k rows:
+        // 410 against 435 us for 8 waves at 18992, 202-211 against 291 at
+        // 8192; 636 against 655 us for 4 waves at 32000, 2504 against 2551
+        // at 128256, 3016 against 3025 at 151936)
+        if (vocab <= kVeryShortRow) {
+            *waves = 4;
+            *depth = 1;
+        } else if (vocab <= kShortRow) {
             *waves = 8;
             *depth = 1;
         } else if (vocab <= 131072) {
@@ -100,9 +106,10 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         }
         return;
     }
-    if (read_rows > kCUs) {
-        // more rows than compute units: 8 waves one chunk deep (2-8 % ahead
-        // of two deep at 320 rows, level at 512)
+    if (read_rows > kCUs || vocab <= kVeryShortRow) {
+        // more rows than compute units, or rows of at most 20K entries: 8
+        // waves one chunk deep (2-8 % ahead of two deep at 320 rows, level
+        // at 512; 7-14 % ahead of 16 waves on rows of 8192 and 16000)
         *waves = 8;
         *depth = 1;
         return;
@@ -120,6 +127,16 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
     *waves = 16;
     *depth = 1;
     *split = few_rows_split(read_rows, vocab, slots, min_split);
+}
+
+void shard_shape(const lp_plan &p, uint32_t shard_vocab, uint32_t *waves, uint32_t *depth) {
+    if (p.shape_set) {
+        *waves = p.waves;
+        *depth = p.depth;
+        return;
+    }
+    uint32_t split = 1;   // a shard is one segment of each row
+    choose_variant(p.read_rows, shard_vocab, p.slots, waves, depth, &split);
 }
 
 lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
@@ -279,6 +296,7 @@ lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (waves != 4 && waves != 8 && waves != 16) return LP_ERR_UNSUPPORTED;
     plan->waves = waves;
+    plan->shape_set = true;
     return LP_OK;
 }
 
@@ -286,6 +304,7 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (depth != 1 && depth != 2) return LP_ERR_UNSUPPORTED;
     plan->depth = depth;
+    plan->shape_set = true;
     return LP_OK;
 }
 

@@ -159,7 +159,8 @@ def test_split_and_workspace():
     assert big.split == 1
 
 
-@pytest.mark.parametrize("vocab,waves,depth", [(32000, 8, 1), (65536, 8, 1), (65537, 16, 1),
+@pytest.mark.parametrize("vocab,waves,depth", [(8192, 4, 1), (18992, 4, 1), (20480, 4, 1),
+                                               (20481, 8, 1), (32000, 8, 1), (65536, 8, 1), (65537, 16, 1),
                                                (128256, 16, 1), (131072, 16, 1), (131073, 4, 2),
                                                (151936, 4, 2)])
 def test_many_rows_shape_by_row_length(vocab, waves, depth):
@@ -172,6 +173,7 @@ def test_many_rows_shape_by_row_length(vocab, waves, depth):
 
 @pytest.mark.parametrize("rows,vocab,shape", [
     (4, 32000, (1, 16, 1)), (32, 32000, (1, 16, 1)), (200, 32000, (1, 16, 1)),
+    (32, 8192, (1, 8, 1)), (200, 16000, (1, 8, 1)), (32, 24000, (1, 16, 1)),
     (32, 128256, (3, 16, 1)), (32, 151936, (4, 16, 1)), (64, 151936, (4, 16, 1)),
     (32, 256000, (7, 16, 1)), (96, 256000, (2, 16, 1)), (127, 256000, (2, 16, 1)),
     (128, 128256, (1, 8, 2)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),

@@ -766,14 +766,41 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const float inv_temp = __uint_as_float(d.inv_temp_bits);
     wave_lse(m, s, kLog2e * inv_temp);
     const uint32_t nkeys = a.nseg * uint32_t(kK);
-    uint64_t e[kPer];
+    uint64_t top;
+    if (nkeys <= uint32_t(kWave)) {
+        // at most one key per lane: each key's rank is the number of keys
+        // above it (keys of different records are distinct; empty slots are
+        // 0 and never placed), counted with broadcast LDS reads from this
+        // wave's own slots; the best kK go to their rank.  The fences keep
+        // the compiler from forwarding a lane's own store to its read-back.
+        __shared__ uint64_t s_k[4][kWave];
+        __shared__ uint64_t s_t[4][kWave];
+        const int w = int(threadIdx.x >> 6);
+        const uint64_t mine = uint32_t(lane) < nkeys
+                                  ? recs[uint64_t(uint32_t(lane) / kK) * a.rec_seg_stride + 1 + uint32_t(lane) % kK]
+                                  : 0ull;
+        s_k[w][lane] = mine;
+        if (lane < kK) s_t[w][lane] = 0ull;
+        lds_release();
+        lds_acquire();
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (uint32_t j = 0; j < nkeys; ++j) rank += s_k[w][j] > mine ? 1u : 0u;
+        lds_release();
+        if (mine != 0 && rank < uint32_t(kK)) s_t[w][rank] = mine;
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_t[w][lane] : 0ull;
+    } else {
+        uint64_t e[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const uint32_t idx = uint32_t(lane + kWave * i);
-        e[i] = idx < nkeys ? recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK] : 0ull;
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t idx = uint32_t(lane + kWave * i);
+            e[i] = idx < nkeys ? recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK] : 0ull;
+        }
+        uint32_t found;
+        top = wave_select<kK, kPer>(e, lane, &found);
     }
-    uint32_t found;
-    const uint64_t top = wave_select<kK, kPer>(e, lane, &found);
     write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m, s, inv_temp, x_chosen, d.chosen);
 }
 

@@ -219,6 +219,22 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
     return mine;
 }
 
+// Fewest slots for which the end of the row kernel ranks the waves' keys by
+// binary search (with more keys than lanes); fewer take wave-wide maxima.
+constexpr int kRankMergeMinK = 15;
+
+// The number of keys above `key` in a list of kK keys sorted in descending
+// order (0 for empty slots), kK = 2^L - 1: a branchless binary search of L
+// probes.
+template <int kK>
+__device__ __forceinline__ uint32_t count_above(const uint64_t *list, uint64_t key) {
+    uint32_t pos = 0;
+#pragma unroll
+    for (uint32_t step = (uint32_t(kK) + 1) / 2; step > 0; step >>= 1)
+        if (list[pos + step - 1] > key) pos += step;
+    return pos;
+}
+
 // ------------------------------------------------------------------ candidates
 //
 // Each wave keeps the K best keys it has seen (K = 2^levels - 1, 7 by
@@ -684,6 +700,28 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
         lds_release();
         if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_top[lane] : 0ull;
+    } else if constexpr (kK >= kRankMergeMinK) {
+        // more keys than lanes, in kWaves sorted lists: a key's rank is the
+        // number of keys above it in all the lists together (in its own list,
+        // its position, the keys being distinct), each list binary-searched
+        // in log2(kK + 1) probes instead of kK wave-wide rounds of maxima;
+        // the best kK go to their rank
+        if (lane < kK) s_top[lane] = 0ull;
+        lds_release();
+#pragma unroll 1
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = lane + kWave * i;
+            const uint64_t key = idx < kN ? s_keys[idx] : 0ull;
+            if (key != 0) {
+                uint32_t rank = 0;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
+                if (rank < uint32_t(kK)) s_top[rank] = key;
+            }
+        }
         lds_release();
         lds_acquire();
         top = lane < kK ? s_top[lane] : 0ull;

@@ -804,6 +804,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const float inv_temp = __uint_as_float(d.inv_temp_bits);
     wave_lse(m, s, kLog2e * inv_temp);
     const uint32_t nkeys = a.nseg * uint32_t(kK);
+    // this wave's LDS: the records' keys (record r's slot p at r * kK + p)
+    // and the kK best, placed by rank
+    constexpr int kMaxKeys = int(kMaxMergeKeys) < int(kMaxSplit) * kK ? int(kMaxMergeKeys) : int(kMaxSplit) * kK;
+    constexpr int kSlots = kK >= kRankMergeMinK && kMaxKeys > kWave ? kMaxKeys : kWave;
+    __shared__ uint64_t s_k[4][kSlots];
+    __shared__ uint64_t s_t[4][kWave];
+    const int w = int(threadIdx.x >> 6);
     uint64_t top;
     if (nkeys <= uint32_t(kWave)) {
         // at most one key per lane: each key's rank is the number of keys
@@ -811,9 +818,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         // 0 and never placed), counted with broadcast LDS reads from this
         // wave's own slots; the best kK go to their rank.  The fences keep
         // the compiler from forwarding a lane's own store to its read-back.
-        __shared__ uint64_t s_k[4][kWave];
-        __shared__ uint64_t s_t[4][kWave];
-        const int w = int(threadIdx.x >> 6);
         const uint64_t mine = uint32_t(lane) < nkeys
                                   ? recs[uint64_t(uint32_t(lane) / kK) * a.rec_seg_stride + 1 + uint32_t(lane) % kK]
                                   : 0ull;
@@ -826,6 +830,25 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         for (uint32_t j = 0; j < nkeys; ++j) rank += s_k[w][j] > mine ? 1u : 0u;
         lds_release();
         if (mine != 0 && rank < uint32_t(kK)) s_t[w][rank] = mine;
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_t[w][lane] : 0ull;
+    } else if constexpr (kK >= kRankMergeMinK) {
+        // more keys than lanes: every record's keys are sorted, so a key's
+        // rank is the number of keys above it summed over the records, each
+        // a binary search of log2(kK + 1) probes in LDS
+        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave)
+            s_k[w][idx] = recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK];
+        if (lane < kK) s_t[w][lane] = 0ull;
+        lds_release();
+        lds_acquire();
+        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave) {
+            const uint64_t key = s_k[w][idx];
+            if (key == 0) continue;
+            uint32_t rank = 0;
+            for (uint32_t r = 0; r < a.nseg; ++r) rank += count_above<kK>(&s_k[w][r * kK], key);
+            if (rank < uint32_t(kK)) s_t[w][rank] = key;
+        }
         lds_release();
         lds_acquire();
         top = lane < kK ? s_t[w][lane] : 0ull;

@@ -267,21 +267,20 @@ __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// A bound from one real element per lane (or -inf for none): if kK lanes
-// hold values >= t (counting lanes that tie), no element below t can be in
-// the top kK, so the bound may be just under the smallest key of value t.
-// t is the kK-th largest of the 64 lane values, found bit by bit from the
-// top on their order-mapped high words: a bit stays set when at least kK
-// lanes are at or above the prefix with it, 32 compare-and-count steps for
-// any kK.  A -inf t excludes nothing.
-template <int kK>
-__device__ __forceinline__ uint64_t bound_from_lane_values(float v) {
+// A bound from one real element per lane (or -inf for none): if `need`
+// lanes hold values >= t (counting lanes that tie), no element below t can be
+// in the top `need`, so the bound may be just under the smallest key of value
+// t.  t is the need-th largest of the 64 lane values, found bit by bit from
+// the top on their order-mapped high words: a bit stays set when at least
+// `need` lanes are at or above the prefix with it, 32 compare-and-count steps
+// for any count.  A -inf t excludes nothing.
+__device__ __forceinline__ uint64_t bound_from_lane_values(float v, uint32_t need) {
     const uint32_t u = uint32_t(order_key(v, kPadId) >> 32);
     uint32_t t = 0;
 #pragma unroll
     for (int b = 31; b >= 0; --b) {
         const uint32_t trial = t | (1u << b);
-        if (__popcll(__ballot(u >= trial)) >= kK) t = trial;
+        if (uint32_t(__popcll(__ballot(u >= trial))) >= need) t = trial;
     }
     return t > 0 ? (uint64_t(t) << 32) - 1 : 0ull;  // low word 0: smallest key of value t
 }
@@ -430,6 +429,13 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kPubM = (kK + kPubJ) / (kPubJ + 1);           // waves needed
     constexpr bool kPubBound = kK >= 31 && kPubM >= kWaves - 1;  // its min or second min
     const RowDesc d = load_desc_uniform(a.desc, o);
+    // Keys the row needs exactly: its top_n, or with the top-k front end its
+    // k (the kept keys all enter the renormalised sum; k >= the listed
+    // slots).  The bound is the wave's need-th key: need real keys above a
+    // key exclude it.  Slots past `need` are written as padding, so keys
+    // there may be incomplete.
+    const uint32_t need_raw = (d.top_n >> 16) != 0 ? (d.top_n >> 16) : (d.top_n & 0xFFFFu);
+    const uint32_t need = need_raw < 1u ? 1u : (need_raw > uint32_t(kK) ? uint32_t(kK) : need_raw);
 
     if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads record rows)
         if (!a.records && wave == 0) write_padding<kK>(a.out_lp, a.out_id, o, lane);
@@ -515,7 +521,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         while (mask != 0) {
             const int l = __builtin_ctzll(mask);
             list = list_insert<kK>(list, readlane_u64(key, l), lane);
-            T = umax64(T, readlane_u64(list, kK - 1));
+            T = umax64(T, readlane_u64(list, int(need) - 1));
             mask = __ballot(pass && key > T) & ~((2ull << l) - 1ull);
         }
     };
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < kWaves; ++i)
             if (i != wave) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
-        T = bound_from_lane_values<kK>(cmx);
+        T = bound_from_lane_values(cmx, need);
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
         constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);

@@ -34,6 +34,11 @@
  *     allocates no device memory.  Calls never throw; they return lp_status.
  *   - a logits row must hold no NaN or +inf; -inf entries are allowed and rank
  *     lowest.  An all -inf row yields NaN log-probabilities.
+ *   - threads: calls on different plans may run concurrently (the pinned
+ *     staging pool behind lp_stage_ragged is shared and locked).  A plan is
+ *     not locked: calls that modify it (lp_plan_set_*, lp_plan_destroy) must
+ *     not overlap other calls on the same plan; read-only calls on one plan
+ *     (staging, launching, assembly, queries) may overlap each other.
  */
 #ifndef LIBLOGPROB_H
 #define LIBLOGPROB_H
@@ -191,7 +196,7 @@ lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
  * neither allocates nor waits in the steady state, and the plan may be
  * destroyed as soon as it returns.
  */
-lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens,
+lp_status lp_stage_ragged(const lp_plan *plan, const uint32_t *tokens,
                           const uint32_t *sampled_tokens, void *workspace,
                           uint64_t workspace_bytes, void *stream);
 
@@ -218,7 +223,7 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
                            uint64_t workspace_bytes, void *stream);
 
 /* lp_compute_ragged = lp_stage_ragged followed by lp_launch_ragged. */
-lp_status lp_compute_ragged(lp_plan *plan, const float *logits,
+lp_status lp_compute_ragged(const lp_plan *plan, const float *logits,
                             const float *next_token_logits, const uint32_t *tokens,
                             const uint32_t *sampled_tokens, float *out_logprobs,
                             uint32_t *out_token_ids, void *workspace,

@@ -1086,7 +1086,7 @@ extern "C" {
 
 int lp_last_hip_error(void) { return lp::g_last_hip_error; }
 
-lp_status lp_stage_ragged(lp_plan *plan, const uint32_t *tokens, const uint32_t *sampled_tokens,
+lp_status lp_stage_ragged(const lp_plan *plan, const uint32_t *tokens, const uint32_t *sampled_tokens,
                           void *workspace, uint64_t workspace_bytes, void *stream) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (plan->out_rows == 0) return LP_OK;
@@ -1151,7 +1151,7 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     return LP_OK;
 }
 
-lp_status lp_compute_ragged(lp_plan *plan, const float *logits, const float *next_token_logits,
+lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const float *next_token_logits,
                             const uint32_t *tokens, const uint32_t *sampled_tokens,
                             float *out_logprobs, uint32_t *out_token_ids, void *workspace,
                             uint64_t workspace_bytes, void *stream) {

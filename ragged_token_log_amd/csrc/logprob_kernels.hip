@@ -219,8 +219,10 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
     return mine;
 }
 
-// Fewest slots for which the end of the row kernel ranks the waves' keys by
-// binary search (with more keys than lanes); fewer take wave-wide maxima.
+// Fewest slots for which a row's sorted key lists are ranked by binary search
+// when they hold more keys than a wave has lanes (the end of the row kernel,
+// the merge kernel); with at most one key per lane the row kernel's end
+// searches from 7 slots up.
 constexpr int kRankMergeMinK = 15;
 
 // The number of keys above `key` in a list of kK keys sorted in descending
@@ -692,29 +694,16 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kN = kWaves * kK;
     constexpr int kPer = (kN + kWave - 1) / kWave;
     uint64_t top;
-    if constexpr (kPer == 1) {
-        // at most one key per lane: each key's rank is the number of keys
-        // above it (the keys are distinct but for empty slots, 0), counted
-        // with broadcast reads and independent compares rather than kK
-        // rounds of wave-wide maxima; the best kK go to their rank
-        // (lanes exchange values through s_top: the fences keep the
-        // compiler from forwarding a lane's own store to its read-back)
-        if (lane < kK) s_top[lane] = 0ull;
-        const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
-        uint32_t rank = 0;
-#pragma unroll 8
-        for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
-        lds_release();
-        if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
-        lds_release();
-        lds_acquire();
-        top = lane < kK ? s_top[lane] : 0ull;
-    } else if constexpr (kK >= kRankMergeMinK) {
-        // more keys than lanes, in kWaves sorted lists: a key's rank is the
-        // number of keys above it in all the lists together (in its own list,
-        // its position, the keys being distinct), each list binary-searched
-        // in log2(kK + 1) probes instead of kK wave-wide rounds of maxima;
-        // the best kK go to their rank
+    // The waves' lists are sorted: from 7 slots up (with one key per lane,
+    // or from 15 with more) a binary search ranks each key in fewer LDS
+    // round trips than counting; below, counting; 7 slots over more keys
+    // than lanes take kK wave-wide rounds.
+    constexpr bool kSearch = kK >= kRankMergeMinK || (kK >= 7 && kPer == 1);
+    if constexpr (kSearch) {
+        // a key's rank is the number of keys above it in all the lists
+        // together (in its own list, its position, the keys being distinct),
+        // each list binary-searched in log2(kK + 1) probes; the best kK go
+        // to their rank
         if (lane < kK) s_top[lane] = 0ull;
         lds_release();
 #pragma unroll 1
@@ -728,6 +717,23 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                 if (rank < uint32_t(kK)) s_top[rank] = key;
             }
         }
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_top[lane] : 0ull;
+    } else if constexpr (kPer == 1) {
+        // at most one key per lane: each key's rank is the number of keys
+        // above it (the keys are distinct but for empty slots, 0), counted
+        // with broadcast reads and independent compares rather than kK
+        // rounds of wave-wide maxima; the best kK go to their rank
+        // (lanes exchange values through s_top: the fences keep the
+        // compiler from forwarding a lane's own store to its read-back)
+        if (lane < kK) s_top[lane] = 0ull;
+        const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
+        lds_release();
+        if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
         lds_release();
         lds_acquire();
         top = lane < kK ? s_top[lane] : 0ull;

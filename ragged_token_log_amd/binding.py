@@ -125,8 +125,9 @@ def _u32(a, n=None):
 
 def _ptr(arr, ctype=None):
     """The address of a contiguous host array (None for NULL); ``ctype``
-    only names the element type the C side expects."""
-    return None if arr is None else arr.ctypes.data
+    only names the element type the C side expects.  Read from the array
+    interface: ``arr.ctypes`` builds a helper object per call."""
+    return None if arr is None else arr.__array_interface__["data"][0]
 
 
 def _dev_ptr(t):

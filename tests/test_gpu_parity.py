@@ -688,6 +688,34 @@ def test_deterministic_and_split_independent(R):
         np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
 
 
+@pytest.mark.parametrize("levels", [4, 5, 6])
+def test_shapes_agree_at_deep_levels(R, levels):
+    """At 15, 31 and 63 slots the end of the row kernel and the record merge
+    rank keys by binary search over sorted lists, and each row's bound uses
+    the keys it needs (top_n drawn up to the cap): every shape and split
+    gives the same ids and, within fp32 rounding, the same values, and the
+    default one matches the oracle."""
+    log(f"shapes agree at levels={levels}")
+    cap = LO.max_top_n(levels)
+    c = gen.ragged_echo_mix(seed=20 + levels, batch=6, lmin=20, lmax=70, vocab=20011)
+    rng = np.random.default_rng(levels)
+    top_n = rng.integers(0, cap + 1, len(c.top_n))
+    top_n[0], top_n[1] = cap, 1
+    logits_np = gen.host_logits(c)
+    ntl_np = gen.next_token_rows(c, logits_np)
+    logits, ntl = _dev(logits_np), _dev(ntl_np)
+    args = (c.offsets, logits, ntl, c.tokens, c.sampled, top_n, c.echo)
+    a = run_library(R, torch, *args, levels=levels)
+    ref = oracle(c.offsets, logits_np, ntl_np, c.tokens, c.sampled, top_n, c.echo, levels=levels)
+    assert_parity(*a, ref, f"deep levels={levels} default shape")
+    max_split = min(64, 1024 // cap)     # the merge holds 1024 keys, at most 64 segments
+    for s, w, dp in ((1, 4, 1), (1, 8, 2), (1, 16, 1), (2, 4, 2), (5, 8, 1),
+                     (min(9, max_split), 16, 2), (max_split, 8, 1)):
+        d = run_library(R, torch, *args, split=s, waves=w, depth=dp, levels=levels)
+        assert np.array_equal(a[1], d[1]), (levels, s, w, dp)
+        np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
+
+
 def test_outputs_stay_in_bounds_and_plan_is_reusable(R):
     c = gen.ragged_echo_mix(seed=10, batch=5, lmin=5, lmax=40, vocab=3001)
     logits_np = gen.host_logits(c)

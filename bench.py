@@ -114,7 +114,7 @@ def main():
         write_profile(args.workload, *args.write_profile, split=args.split, waves=args.waves)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the log-probability kernels run on one GPU per process here; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -219,10 +219,9 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
     return mine;
 }
 
-// Fewest slots for which a row's sorted key lists are ranked by binary search
-// when they hold more keys than a wave has lanes (the end of the row kernel,
-// the merge kernel); with at most one key per lane the row kernel's end
-// searches from 7 slots up.
+// Fewest slots for which the end of the row kernel ranks the waves' sorted
+// lists by binary search when they hold more keys than a wave has lanes;
+// with at most one key per lane it searches from 7 slots up.
 constexpr int kRankMergeMinK = 15;
 
 // The number of keys above `key` in a list of kK keys sorted in descending
@@ -819,12 +818,34 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     // this wave's LDS: the records' keys (record r's slot p at r * kK + p)
     // and the kK best, placed by rank
     constexpr int kMaxKeys = int(kMaxMergeKeys) < int(kMaxSplit) * kK ? int(kMaxMergeKeys) : int(kMaxSplit) * kK;
-    constexpr int kSlots = kK >= kRankMergeMinK && kMaxKeys > kWave ? kMaxKeys : kWave;
+    // from 7 slots up every key count is ranked by binary search over the
+    // records (each record's keys are sorted), so the keys are staged in LDS
+    constexpr bool kSearch = kK >= 7;
+    constexpr int kSlots = kSearch && kMaxKeys > kWave ? kMaxKeys : kWave;
     __shared__ uint64_t s_k[4][kSlots];
     __shared__ uint64_t s_t[4][kWave];
     const int w = int(threadIdx.x >> 6);
     uint64_t top;
-    if (nkeys <= uint32_t(kWave)) {
+    if constexpr (kSearch) {
+        // every record's keys are sorted, so a key's rank is the number of
+        // keys above it summed over the records, each a binary search of
+        // log2(kK + 1) probes in LDS; the best kK go to their rank
+        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave)
+            s_k[w][idx] = recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK];
+        if (lane < kK) s_t[w][lane] = 0ull;
+        lds_release();
+        lds_acquire();
+        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave) {
+            const uint64_t key = s_k[w][idx];
+            if (key == 0) continue;
+            uint32_t rank = 0;
+            for (uint32_t r = 0; r < a.nseg; ++r) rank += count_above<kK>(&s_k[w][r * kK], key);
+            if (rank < uint32_t(kK)) s_t[w][rank] = key;
+        }
+        lds_release();
+        lds_acquire();
+        top = lane < kK ? s_t[w][lane] : 0ull;
+    } else if (nkeys <= uint32_t(kWave)) {
         // at most one key per lane: each key's rank is the number of keys
         // above it (keys of different records are distinct; empty slots are
         // 0 and never placed), counted with broadcast LDS reads from this
@@ -842,25 +863,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         for (uint32_t j = 0; j < nkeys; ++j) rank += s_k[w][j] > mine ? 1u : 0u;
         lds_release();
         if (mine != 0 && rank < uint32_t(kK)) s_t[w][rank] = mine;
-        lds_release();
-        lds_acquire();
-        top = lane < kK ? s_t[w][lane] : 0ull;
-    } else if constexpr (kK >= kRankMergeMinK) {
-        // more keys than lanes: every record's keys are sorted, so a key's
-        // rank is the number of keys above it summed over the records, each
-        // a binary search of log2(kK + 1) probes in LDS
-        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave)
-            s_k[w][idx] = recs[uint64_t(idx / kK) * a.rec_seg_stride + 1 + idx % kK];
-        if (lane < kK) s_t[w][lane] = 0ull;
-        lds_release();
-        lds_acquire();
-        for (uint32_t idx = uint32_t(lane); idx < nkeys; idx += kWave) {
-            const uint64_t key = s_k[w][idx];
-            if (key == 0) continue;
-            uint32_t rank = 0;
-            for (uint32_t r = 0; r < a.nseg; ++r) rank += count_above<kK>(&s_k[w][r * kK], key);
-            if (rank < uint32_t(kK)) s_t[w][rank] = key;
-        }
         lds_release();
         lds_acquire();
         top = lane < kK ? s_t[w][lane] : 0ull;

@@ -742,6 +742,30 @@ def test_outputs_stay_in_bounds_and_plan_is_reusable(R):
     plan.close()
 
 
+def test_empty_batch_and_padding_only_batch(R):
+    """No request: empty outputs and offsets [0], nothing launched.  Every
+    top_n 0 (levels 3): no logits row is read and every slot of every
+    output row is padding (-inf, 0xFFFFFFFF), as the oracle gives."""
+    vocab = 1000
+    ntl = _dev(np.zeros((0, vocab), np.float32))
+    lp, ids, out_off = run_library(R, torch, np.zeros(1, np.uint32), None, ntl,
+                                   np.zeros(0, np.uint32), np.zeros(0, np.uint32),
+                                   np.zeros(0, np.int32), np.zeros(0, bool))
+    assert lp.shape == (0, 8) and ids.shape == (0, 8) and out_off.tolist() == [0]
+    rng = np.random.default_rng(3)
+    off = np.array([0, 3, 4, 9], np.uint32)
+    logits = rng.standard_normal((9, vocab)).astype(np.float32)
+    ntl_np = logits[off[1:].astype(np.int64) - 1]
+    tokens = rng.integers(0, vocab, 9).astype(np.uint32)
+    sampled = rng.integers(0, vocab, 3).astype(np.uint32)
+    top_n = np.zeros(3, np.int32)
+    echo = np.array([True, False, True])
+    got = run_library(R, torch, off, _dev(logits), _dev(ntl_np), tokens, sampled, top_n, echo)
+    ref = oracle(off, logits, ntl_np, tokens, sampled, top_n, echo)
+    assert_parity(*got, ref, "padding only")
+    assert np.all(got[1] == 0xFFFFFFFF) and np.all(np.isneginf(got[0]))
+
+
 def test_errors_reported_before_launch(R):
     c = gen.no_echo_next_token()
     ntl = _dev(gen.host_logits(c))

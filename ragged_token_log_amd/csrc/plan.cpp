@@ -27,15 +27,6 @@ void size_workspace(lp_plan &p) {
     p.workspace_bytes = p.desc_bytes + p.partial_bytes;
 }
 
-// Kernel shape: waves per workgroup, chunks in flight per wave and
-// vocabulary segments per row.  Rows are independent, so a launch with many
-// rows runs one workgroup per row, its shape by row length (measured below).
-// A few hundred rows (two or three workgroups per CU) run 8 waves with one
-// chunk in flight each: their whole batch is in flight at once, and fewer
-// bytes queued per wave shorten the last rows' wait.  Fewer rows than CUs
-// get more waves per row; too few to occupy 256 CUs even then are split
-// into segments (one workgroup each, at least kMinSegment elements), whose
-// partial results a second kernel merges.
 // Shape of the row kernel (waves per workgroup, chunks in flight per wave,
 // segments per row) from the number of rows read, the row length and the
 // ranked slots.  Measured on gfx950: 34.6k-row sweeps for the first rule,

@@ -34,7 +34,8 @@ void size_workspace(lp_plan &p) {
 // 256000, every waves x depth x split timed in interleaved passes.
 constexpr uint64_t kManyRows = 1024;
 constexpr uint64_t kCUs = 256;
-constexpr uint64_t kSplitBelow = 128;
+constexpr uint64_t kSplitBelow = 129;   // at most 128 rows: segments (two per row or more)
+constexpr uint64_t kSplitBelowManySlots = 128;
 constexpr uint32_t kVeryShortRow = 20480;
 constexpr uint32_t kShortRow = 65536;
 constexpr uint32_t kMinSegment = 32768;
@@ -70,7 +71,7 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         // which still gain from segments (38 against 43 us at 32 rows of
         // 256000; at 128256 the split loses 17 %).
         *waves = many ? 4 : 8;
-        if (!many && slots == 31 && read_rows < kSplitBelow && vocab >= 131072) {
+        if (!many && slots == 31 && read_rows < kSplitBelowManySlots && vocab >= 131072) {
             *waves = 16;
             *depth = 1;
             *split = few_rows_split(read_rows, vocab, slots, min_split);
@@ -106,18 +107,22 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         return;
     }
     if (read_rows >= kSplitBelow) {
-        // one row per compute unit at most: 16 waves one chunk deep on short
-        // rows (3-10 % ahead of two deep), 8 waves two deep on long ones
-        // (1-4 %); a split's merge launch costs more than it gains here
+        // one row per compute unit at most (129-256 rows): 16 waves one chunk
+        // deep on short rows (3-10 % ahead of two deep), 8 waves two deep on
+        // long ones (1-4 %); two segments a row would leave more workgroups
+        // than compute units (25 against 20 us at 144 rows of 128256)
         *waves = vocab <= kShortRow ? 16 : 8;
         *depth = vocab <= kShortRow ? 1 : 2;
         return;
     }
-    // fewer rows still: 16 waves one chunk deep over segments (7-40 % ahead
-    // of whole rows at 32-96 rows of 151936 or 256000)
-    *waves = 16;
-    *depth = 1;
+    // fewer rows still (at most 128): segments, 16 waves one chunk deep (7-40
+    // % ahead of whole rows at 32-96 rows of 151936 or 256000); two segments
+    // a row from 112 rows up take 8 waves two deep (3-8 % ahead of 16 waves
+    // and of whole rows at 112 and 128 rows of 128256 to 256000)
     *split = few_rows_split(read_rows, vocab, slots, min_split);
+    const bool pairs = *split == 2 && read_rows >= 112;
+    *waves = pairs ? 8 : 16;
+    *depth = pairs ? 2 : 1;
 }
 
 void shard_shape(const lp_plan &p, uint32_t shard_vocab, uint32_t *waves, uint32_t *depth) {

@@ -175,8 +175,9 @@ def test_many_rows_shape_by_row_length(vocab, waves, depth):
     (4, 32000, (1, 16, 1)), (32, 32000, (1, 16, 1)), (200, 32000, (1, 16, 1)),
     (32, 8192, (1, 8, 1)), (200, 16000, (1, 8, 1)), (32, 24000, (1, 16, 1)),
     (32, 128256, (3, 16, 1)), (32, 151936, (4, 16, 1)), (64, 151936, (4, 16, 1)),
-    (32, 256000, (7, 16, 1)), (96, 256000, (2, 16, 1)), (127, 256000, (2, 16, 1)),
-    (128, 128256, (1, 8, 2)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),
+    (32, 256000, (7, 16, 1)), (96, 256000, (2, 16, 1)), (111, 151936, (2, 16, 1)),
+    (112, 151936, (2, 8, 2)), (127, 256000, (2, 8, 2)), (128, 128256, (2, 8, 2)),
+    (129, 128256, (1, 8, 2)), (128, 32000, (1, 16, 1)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),
     (257, 128256, (1, 8, 1)), (600, 151936, (1, 8, 1))])
 def test_few_rows_shape(rows, vocab, shape):
     """Plans of at most 1023 read rows: (split, waves, depth) from the row

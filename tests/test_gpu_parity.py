@@ -742,6 +742,28 @@ def test_outputs_stay_in_bounds_and_plan_is_reusable(R):
     plan.close()
 
 
+def test_default_split_pairs(R):
+    """120 next-token rows of 70001 entries (segments hold at least 32768):
+    the default plan cuts each row in two (8 waves, two chunks deep) and
+    merges the records; every row matches the oracle, special rows
+    included."""
+    vocab, rows = 70001, 120
+    rng = np.random.default_rng(120)
+    ntl_np = _special_rows(rng, rows, vocab)
+    off = np.arange(rows + 1, dtype=np.uint32)
+    echo = np.zeros(rows, bool)
+    top_n = rng.integers(1, 8, rows)
+    sampled = rng.integers(0, vocab, rows).astype(np.uint32)
+    tokens = np.zeros(rows, np.uint32)
+    plan = R.Plan(off, echo, top_n, vocab, False)
+    info = plan.info()
+    plan.close()
+    assert (info["split"], info["waves"], info["depth"]) == (2, 8, 2)
+    got = run_library(R, torch, off, None, _dev(ntl_np), tokens, sampled, top_n, echo)
+    ref = oracle(off, None, ntl_np, tokens, sampled, top_n, echo)
+    assert_parity(*got, ref, "default split pairs")
+
+
 def test_empty_batch_and_padding_only_batch(R):
     """No request: empty outputs and offsets [0], nothing launched.  Every
     top_n 0 (levels 3): no logits row is read and every slot of every

@@ -116,9 +116,28 @@ def _check(status: int, where: str):
         raise LogprobError(status, where, hip)
 
 
-def _u32(a, n=None):
-    arr = np.ascontiguousarray(np.asarray(a), dtype=np.uint32) if a is not None else None
-    if arr is not None and n is not None and arr.shape[0] != n:
+def _ints(a, dtype, lo, hi, code, what):
+    """``a`` as a contiguous array of ``dtype``.  Raises LogprobError(code)
+    when an entry lies outside [lo, hi], and LP_ERR_SHAPE when one is not a
+    whole number: a plain cast would wrap or truncate it into a different,
+    valid-looking value."""
+    arr = np.asarray(a)
+    if arr.size:
+        if arr.dtype.kind == "f":
+            if not np.all(np.isfinite(arr)) or not np.all(np.floor(arr) == arr):
+                raise LogprobError(3, f"{what} must hold whole numbers")
+        elif arr.dtype.kind not in "iub":
+            raise LogprobError(3, f"{what} must hold integers")
+        if arr.min() < lo or arr.max() > hi:
+            raise LogprobError(code, f"{what} outside [{lo}, {hi}]")
+    return np.ascontiguousarray(arr, dtype=dtype)
+
+
+def _u32(a, n=None, what="tokens"):
+    if a is None:
+        return None
+    arr = _ints(a, np.uint32, 0, 0xFFFFFFFF, 7, what)
+    if n is not None and arr.shape[0] != n:
         raise LogprobError(3, "array length")
     return arr
 
@@ -144,12 +163,14 @@ class Plan:
     def __init__(self, input_row_offsets, batch_echo, batch_top_n, vocab: int,
                  has_logits: bool, logits_rows: int | None = None, levels: int = LEVELS):
         lib = load()
-        off = np.ascontiguousarray(np.asarray(input_row_offsets), dtype=np.uint32)
+        off = _ints(input_row_offsets, np.uint32, 0, 0xFFFFFFFF, 2, "input_row_offsets")
         if off.ndim != 1 or off.shape[0] < 1:
             raise LogprobError(3, "input_row_offsets must be 1-D with batch+1 entries")
         batch = off.shape[0] - 1
         echo = np.ascontiguousarray(np.asarray(batch_echo, dtype=bool).astype(np.uint8))
-        top_n = np.ascontiguousarray(np.asarray(batch_top_n), dtype=np.int32)
+        # clipped, not wrapped: the library still names a negative or too large top_n
+        top_n = _ints(np.clip(np.asarray(batch_top_n), -1, 1 << 20) if np.size(batch_top_n)
+                      else batch_top_n, np.int32, -1, 1 << 20, 3, "batch_top_n")
         if echo.shape[0] != batch or top_n.shape[0] != batch:
             raise LogprobError(3, "batch_echo / batch_top_n length != batch")
         if logits_rows is None:
@@ -237,7 +258,7 @@ class Plan:
         token, top_n | k << 16 (k the top-k front end), fp32 bits of
         1 / temperature."""
         tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch)
+        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
         out = np.zeros((self.out_rows, 4), dtype=np.uint32)
         _check(self._lib.lp_plan_descriptors(self._h, _ptr(tok, ctypes.c_uint32),
                                              _ptr(smp, ctypes.c_uint32),
@@ -264,7 +285,7 @@ class Plan:
     # ---------------------------------------------------------------- device work
     def stage(self, tokens, sampled_tokens, workspace, stream=None):
         tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch)
+        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
         _check(self._lib.lp_stage_ragged(self._h, _ptr(tok, ctypes.c_uint32),
                                          _ptr(smp, ctypes.c_uint32), _dev_ptr(workspace),
                                          _nbytes(workspace), _stream_ptr(stream)),
@@ -295,7 +316,7 @@ class Plan:
     def compute(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
                 out_token_ids, workspace, stream=None):
         tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch)
+        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
         _check(self._lib.lp_compute_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
                                            _ptr(tok, ctypes.c_uint32), _ptr(smp, ctypes.c_uint32),
                                            _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),

@@ -1110,7 +1110,15 @@ lp_status lp_stage_ragged(const lp_plan *plan, const uint32_t *tokens, const uin
     st = lp::build_descriptors(*plan, tokens, sampled_tokens, static_cast<lp::RowDesc *>(slot->host));
     hipError_t e = hipSuccess;
     if (st == LP_OK) e = hipMemcpyAsync(workspace, slot->host, bytes, hipMemcpyHostToDevice, s);
-    if (st == LP_OK && e == hipSuccess) e = hipEventRecord(slot->done, s);
+    if (st == LP_OK && e == hipSuccess) {
+        e = hipEventRecord(slot->done, s);
+        // A copy whose end no event marks may still be reading the slot:
+        // the slot stays taken for good rather than be refilled under it.
+        if (e != hipSuccess) {
+            lp::g_last_hip_error = int(e);
+            return LP_ERR_HIP;
+        }
+    }
     lp::staging_release(slot);
     if (st != LP_OK) return st;
     LP_HIP_TRY(e);

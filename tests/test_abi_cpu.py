@@ -367,3 +367,19 @@ def test_plain_c_caller(tmp_path):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0 and run.stdout.strip().endswith("ok"), run.stdout + run.stderr
+
+
+def test_out_of_range_integers_are_rejected_not_wrapped():
+    # a cast to uint32 would turn 2^32 + 1 into 1 and -1 into 2^32 - 1
+    _expect("LP_ERR_OFFSETS", lambda: R.Plan([0, (1 << 32) + 1], [1], [1], 5, True))
+    _expect("LP_ERR_OFFSETS", lambda: R.Plan(np.array([-1, 1], np.int64), [1], [1], 5, True))
+    _expect("LP_ERR_SHAPE", lambda: R.Plan([0.0, 1.5], [1], [1], 5, True))
+    _expect("LP_ERR_TOP_N_TOO_LARGE", lambda: R.Plan([0, 1], [1], [(1 << 32) + 1], 5, True))
+    _expect("LP_ERR_TOP_N_NEGATIVE", lambda: R.Plan([0, 1], [1], [-(1 << 32) + 1], 5, True))
+    _expect("LP_ERR_SHAPE", lambda: R.Plan([0, 1], [1], [0.5], 5, True))
+    plan = R.Plan([0, 2], [1], [1], 5, True)
+    _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([0, (1 << 32) + 1], [1]))
+    _expect("LP_ERR_TOKEN_RANGE", lambda: plan.descriptors([0, 1], np.array([-4], np.int64)))
+    # whole numbers in range still pass, whatever their dtype
+    d = plan.descriptors(np.array([0, 3], np.int64), np.array([2.0]))
+    assert d[:, :2].tolist() == [[0, 3], [1, 2]]

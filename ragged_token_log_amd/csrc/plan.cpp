@@ -39,14 +39,26 @@ constexpr uint64_t kSplitBelowManySlots = 128;
 constexpr uint32_t kVeryShortRow = 20480;
 constexpr uint32_t kShortRow = 65536;
 constexpr uint32_t kMinSegment = 32768;
+constexpr uint32_t kMinLongSegment = 16000;   // rows longer than kShortRow
+constexpr uint32_t kMaxLongSplit = 8;
 
 // Segments per row for a batch too small to fill the chip: as many as keep
 // the workgroups within one per compute unit (floor, not ceil: a few compute
 // units holding two segments double the tail), each at least kMinSegment
-// long and within what the merge holds.
+// long and within what the merge holds.  Rows longer than kShortRow take
+// segments down to kMinLongSegment, up to kMaxLongSplit of them (or as many
+// as kMinSegment allows, if more).  At 8-32 rows of 128256, 8 segments take
+// 11-12 us against 14 us for 3 at levels 3, and 13-15 against 18 us at
+// levels 4; more than 8 lose (8 rows of 256000 at levels 5: 30.6 us in 16
+// segments, 24.7 in 8, 31.3 in 7 of 16 waves).
 static uint32_t few_rows_split(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t min_split) {
     uint64_t s = kCUs / read_rows;
     uint64_t by_vocab = vocab / kMinSegment;
+    if (vocab > kShortRow) {
+        const uint64_t fine = vocab / kMinLongSegment;
+        const uint64_t most = by_vocab > kMaxLongSplit ? by_vocab : kMaxLongSplit;
+        by_vocab = fine < most ? fine : most;
+    }
     if (by_vocab < 1) by_vocab = 1;
     if (s > by_vocab) s = by_vocab;
     if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
@@ -65,17 +77,14 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
 
     if (slots >= 31) {
         // Levels 5 and 6: every wave of every segment pays ~K ln(n / K)
-        // insertions, so fewer waves and fewer segments pay.  1024 rows or
-        // more: 4 waves (16-68 % ahead of 8 or 16).  Fewer: 8 waves, whole
-        // rows, except 31 slots over fewer than 128 rows of at least 131072,
-        // which still gain from segments (38 against 43 us at 32 rows of
-        // 256000; at 128256 the split loses 17 %).
+        // insertions, so fewer waves pay.  1024 rows or more: 4 waves (16-68
+        // % ahead of 8 or 16).  Fewer: 8 waves two deep, whole rows, except
+        // 31 slots over fewer than 128 rows longer than kShortRow, which gain
+        // from segments (8 rows of 128256: 21 against 29 us whole; of 256000:
+        // 25 against 31 us for 7 segments of 16 waves).
         *waves = many ? 4 : 8;
-        if (!many && slots == 31 && read_rows < kSplitBelowManySlots && vocab >= 131072) {
-            *waves = 16;
-            *depth = 1;
+        if (!many && slots == 31 && read_rows < kSplitBelowManySlots && vocab > kShortRow)
             *split = few_rows_split(read_rows, vocab, slots, min_split);
-        }
         return;
     }
     if (many) {
@@ -118,9 +127,11 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
     // fewer rows still (at most 128): segments, 16 waves one chunk deep (7-40
     // % ahead of whole rows at 32-96 rows of 151936 or 256000); two segments
     // a row from 112 rows up take 8 waves two deep (3-8 % ahead of 16 waves
-    // and of whole rows at 112 and 128 rows of 128256 to 256000)
+    // and of whole rows at 112 and 128 rows of 128256 to 256000), and so do
+    // three or more segments at 15 slots (8 rows of 128256 in 8 segments:
+    // 13.3 against 15.9 us; 16.1 against 17.1 us at 40 rows in 4)
     *split = few_rows_split(read_rows, vocab, slots, min_split);
-    const bool pairs = *split == 2 && read_rows >= 112;
+    const bool pairs = (*split == 2 && read_rows >= 112) || (*split > 2 && slots >= 15);
     *waves = pairs ? 8 : 16;
     *depth = pairs ? 2 : 1;
 }

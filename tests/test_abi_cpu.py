@@ -174,8 +174,9 @@ def test_many_rows_shape_by_row_length(vocab, waves, depth):
 @pytest.mark.parametrize("rows,vocab,shape", [
     (4, 32000, (1, 16, 1)), (32, 32000, (1, 16, 1)), (200, 32000, (1, 16, 1)),
     (32, 8192, (1, 8, 1)), (200, 16000, (1, 8, 1)), (32, 24000, (1, 16, 1)),
-    (32, 128256, (3, 16, 1)), (32, 151936, (4, 16, 1)), (64, 151936, (4, 16, 1)),
-    (32, 256000, (7, 16, 1)), (96, 256000, (2, 16, 1)), (111, 151936, (2, 16, 1)),
+    (32, 128256, (8, 16, 1)), (32, 151936, (8, 16, 1)), (64, 151936, (4, 16, 1)),
+    (32, 256000, (8, 16, 1)), (8, 65536, (2, 16, 1)), (8, 65537, (4, 16, 1)),
+    (40, 128256, (6, 16, 1)), (8, 1 << 20, (32, 16, 1)), (8, 256000, (8, 16, 1)), (4, 294912, (9, 16, 1)), (96, 256000, (2, 16, 1)), (111, 151936, (2, 16, 1)),
     (112, 151936, (2, 8, 2)), (127, 256000, (2, 8, 2)), (128, 128256, (2, 8, 2)),
     (129, 128256, (1, 8, 2)), (128, 32000, (1, 16, 1)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),
     (257, 128256, (1, 8, 1)), (600, 151936, (1, 8, 1))])
@@ -193,12 +194,15 @@ def test_few_rows_shape(rows, vocab, shape):
 @pytest.mark.parametrize("levels,rows,vocab,shape", [
     (5, 2048, 32000, (1, 4, 2)), (6, 2048, 128256, (1, 4, 2)), (5, 1024, 256000, (1, 4, 2)),
     (5, 512, 128256, (1, 8, 2)), (6, 32, 256000, (1, 8, 2)), (6, 96, 151936, (1, 8, 2)),
-    (5, 32, 256000, (7, 16, 1)), (5, 64, 151936, (4, 16, 1)), (5, 32, 128256, (1, 8, 2)),
-    (5, 128, 256000, (1, 8, 2)), (4, 32, 151936, (4, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
+    (5, 32, 256000, (8, 8, 2)), (5, 64, 151936, (4, 8, 2)), (5, 32, 128256, (8, 8, 2)),
+    (5, 96, 70001, (2, 8, 2)), (5, 32, 65536, (1, 8, 2)),
+    (5, 128, 256000, (1, 8, 2)), (4, 32, 151936, (8, 8, 2)), (4, 80, 128256, (3, 8, 2)),
+    (4, 96, 128256, (2, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
 def test_shape_by_ranked_slots(levels, rows, vocab, shape):
     """With 31 or more ranked slots every wave's insertions weigh more: 4
-    waves for many rows, 8 for fewer, segments only for 31 slots over few
-    long rows; 15 slots or fewer keep the shapes of 7."""
+    waves for many rows, 8 two deep for fewer, segments only for 31 slots
+    over few long rows; 15 slots keep the segments of 7 but take 8 waves two
+    deep from three segments a row."""
     plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool),
                   np.full(rows, (1 << levels) - 1), vocab, False, levels=levels)
     info = plan.info()

@@ -764,6 +764,31 @@ def test_default_split_pairs(R):
     assert_parity(*got, ref, "default split pairs")
 
 
+@pytest.mark.parametrize("levels,shape", [(3, (8, 16, 1)), (4, (8, 8, 2)), (5, (8, 8, 2))])
+def test_default_segments_of_long_rows(R, levels, shape):
+    """8 next-token rows of 128256 entries: the default plan cuts each row
+    into 8 segments of at least 16000 entries (8 waves two deep from 15
+    ranked slots up) and merges the records; every row matches the oracle,
+    special rows included."""
+    vocab, rows = 128256, 8
+    rng = np.random.default_rng(80 + levels)
+    ntl_np = _special_rows(rng, rows, vocab)
+    off = np.arange(rows + 1, dtype=np.uint32)
+    echo = np.zeros(rows, bool)
+    top_n = rng.integers(1, 1 << levels, rows)
+    top_n[0] = (1 << levels) - 1
+    sampled = rng.integers(0, vocab, rows).astype(np.uint32)
+    tokens = np.zeros(rows, np.uint32)
+    plan = R.Plan(off, echo, top_n, vocab, False, levels=levels)
+    info = plan.info()
+    plan.close()
+    assert (info["split"], info["waves"], info["depth"]) == shape
+    got = run_library(R, torch, off, None, _dev(ntl_np), tokens, sampled, top_n, echo,
+                      levels=levels)
+    ref = oracle(off, None, ntl_np, tokens, sampled, top_n, echo, levels=levels)
+    assert_parity(*got, ref, f"default segments, levels {levels}")
+
+
 def test_empty_batch_and_padding_only_batch(R):
     """No request: empty outputs and offsets [0], nothing launched.  Every
     top_n 0 (levels 3): no logits row is read and every slot of every

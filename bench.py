@@ -2,17 +2,46 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole device path over one synthetic batch of the
-workload: the row kernel (and, for split-vocab plans, the merge kernel)
-reading every selected logits row once.  The logits and the row descriptors
-are resident in HBM when the timed region starts (the descriptors are
-uploaded once beforehand); a second, separately reported loop also runs the
-host plan and the PCIe descriptor upload every step.
+The default workload is the large prefill echo batch: 16 requests whose
+prompt lengths are geometric with mean 2048 (clipped to [1, 4096]), 34637
+echo rows in all, a vocabulary of 151936, top_n 5.  That is 21.05 GB of fp32
+logits read per step, the largest configuration that fits one GPU.
 
-Small workloads fit in the 256 MB Infinity Cache, so the timed loop cycles
-through copies of the logits totalling at least 1 GiB.
+A step is one pass of the whole device path over that batch, with the logits
+and the row descriptors resident in HBM: lp_launch_ragged (the row kernel,
+plus the merge kernel when rows are split).  The timed region is K steps back
+to back on the launch stream between two HIP events on that stream;
+`value` is rows read per second over it, and the roofline's `achieved` is the
+algorithmic bytes of one launch over the mean step.  A second pass of K
+steps with an event pair around each launch gives the spread (median, p10,
+p90); those pairs add about 2 us to each interval, which matters only for
+the short decode launches.
 
-Prints one JSON line (rank 0, N = 1).
+Beside it, each on the same run:
+  compute_ragged  lp_compute_ragged per step: the descriptors built on the
+                  host, uploaded over PCIe, then the launch.  Median, p10 and
+                  p90 of the event intervals on the stream.  This is the
+                  PCIe-inclusive rate; it is never `value`.
+  decode          the decode batch (256 rows of 128256, one boosted token per
+                  row, top_n 7), measured the same way with its own roofline
+                  fraction.
+  probe           a plain streaming read of as many rows of the same width on
+                  the same copies: the practical ceiling for these bytes.
+  cpu_baseline    the CPU oracle on the host, run before the GPU is touched:
+                  one process, then one process per available core (at most
+                  16), each on rows of the same workload drawn on the host.
+                  After the GPU legs, the oracle also recomputes a few of the
+                  timed output rows from their logits copied back, and the
+                  line reports how many were checked and how many differ.
+
+Workloads that fit the 256 MB Infinity Cache are timed while cycling through
+copies of the logits whose read rows total at least 1 GiB.
+
+Prints one JSON line (N = 1; more GPUs are not supported by this build).
+
+    python bench.py --cpu-full
+times the oracle on every workload in full on the host (all cores) and
+prints one JSON line per workload.
 """
 from __future__ import annotations
 
@@ -31,8 +60,14 @@ sys.path.insert(0, ROOT)
 METRIC = "logit rows/s and achieved HBM GB/s (% of peak), ragged top-7 logprobs, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
+DEFAULT_WORKLOAD = "prefill_echo_large"
+SUB_WORKLOAD = "decode_peaked"
 DEFAULT_STEPS = {"no_echo_next_token": 200, "ragged_echo_mix": 200, "decode_peaked": 200,
                  "prefill_echo_large": 20, "tie_edge_stress": 30}
+MAX_CPU_WORKERS = 16          # the host share of one GPU on the GPU machines
+CPU_BUDGET_S = 8.0            # oracle seconds per CPU leg (one core, then all cores)
+CPU_ROWS_PER_WORKER = 24      # rows a worker draws and then runs in repeated passes
+PARITY_ROWS = 8               # timed output rows the oracle recomputes per workload
 
 
 def algorithmic_bytes(plan_info, vocab):
@@ -43,103 +78,241 @@ def algorithmic_bytes(plan_info, vocab):
     return int(plan_info["read_rows"]) * 4 * vocab + int(plan_info["out_rows"]) * (8 * cols + 16)
 
 
-def cpu_baseline(case, logits_dev, ntl_dev, cols=8, budget_s=10.0, max_rows=2000):
-    """The oracle as it stands, on a bounded sample of the same workload: the
-    first read rows in output order (at most max_rows), in repeated passes
-    until about budget_s of oracle time has been spent."""
+# ---------------------------------------------------------------- CPU baseline leg
+
+def _host_facts():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "cores_available": int(avail), "cpu_count": os.cpu_count()}
+
+
+def _sample_tasks(case, requests, k, cols):
+    """(row, chosen, top_n) for the first min(k, count) output rows of each
+    given request, with the rows drawn on the host (gen.request_rows_sample):
+    exactly the rows the workload reads for echo and next-token requests,
+    rows of the same distribution for a non-echo request with full logits."""
+    import gen
+    import oracle.logprob_oracle as LO
+
+    tasks_all = LO.row_tasks(case.offsets, case.echo, case.top_n, case.tokens, case.sampled,
+                             case.has_logits)
+    counts, out_off = LO.output_counts_and_offsets(case.offsets, case.echo)
+    out = []
+    for n in requests:
+        rows = gen.request_rows_sample(case, n, k)
+        for j in range(min(k, int(counts[n]), rows.shape[0])):
+            t = tasks_all[int(out_off[n]) + j]
+            out.append((rows[j], t.chosen, t.top_n))
+    return out
+
+
+def _oracle_passes(tasks, cols, budget_s):
+    """Runs the oracle's row computation over `tasks` in repeated passes
+    until budget_s has been spent; returns (rows done, seconds)."""
+    import oracle.logprob_oracle as LO
+
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for row, chosen, top_n in tasks:
+            LO.compute_row(row, chosen, top_n, cols)
+            done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return done, el
+
+
+def _cpu_worker(case, requests, k, cols, budget_s, barrier, queue):
+    # a forked child: `case` is the parent's object, not a pickled copy
+    tasks = _sample_tasks(case, requests, k, cols)
+    barrier.wait()
+    queue.put(_oracle_passes(tasks, cols, budget_s))
+
+
+def cpu_baseline(case, cols, budget_s=CPU_BUDGET_S, rows_per_worker=CPU_ROWS_PER_WORKER):
+    """The oracle as it stands (never tuned for this), on the host cores, on
+    a bounded sample of the workload: first one process, then one process
+    per available core (at most MAX_CPU_WORKERS) started together, each
+    running its own rows in repeated passes for budget_s.  Must run before
+    this process touches the GPU: the pool is forked."""
+    import multiprocessing as mp
+
+    live = [n for n in range(case.batch) if int(case.top_n[n]) > 0]
+    facts = _host_facts()
+    if not live:
+        return {"value": 0.0, "unit": "rows/s", "cores": 0, "kind": "oracle",
+                "sample": "no request reads a row", "host": facts}
+    one = _sample_tasks(case, live[:1] if case.echo[live[0]] else live[:rows_per_worker],
+                        rows_per_worker, cols)
+    n1, t1 = _oracle_passes(one, cols, budget_s)
+
+    workers = max(1, min(MAX_CPU_WORKERS, facts["cores_available"]))
+    ctx = mp.get_context("fork")
+    barrier, queue = ctx.Barrier(workers), ctx.Queue()
+    procs = []
+    for w in range(workers):
+        if case.echo[live[w % len(live)]]:
+            reqs = [live[w % len(live)]]
+        else:
+            reqs = [live[(w * rows_per_worker + i) % len(live)] for i in range(rows_per_worker)]
+        p = ctx.Process(target=_cpu_worker, args=(case, reqs, rows_per_worker, cols,
+                                                  budget_s, barrier, queue))
+        p.start()
+        procs.append(p)
+    results = [queue.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join(timeout=60)
+    rows_all = sum(r[0] for r in results)
+    span = max(r[1] for r in results)
+    rate = rows_all / span
+    v = case.vocab
+    return {
+        "value": rate, "unit": "rows/s", "cores": workers, "kind": "oracle",
+        "gbs": rate * 4 * v / 1e9,
+        "sample": (f"{case.name}: each of {workers} processes draws up to {rows_per_worker} "
+                   f"read rows on the host (of one echo request, else one row from each of "
+                   f"{rows_per_worker} requests; each request's own seed and distribution) "
+                   f"and runs the oracle over them in repeated passes for {budget_s:.0f} s, all "
+                   f"starting together; {rows_all} rows in {span:.1f} s (float64 log-softmax and "
+                   f"a full stable sort per row)"),
+        "one_core": {"value": n1 / t1, "unit": "rows/s", "rows": n1, "seconds": t1,
+                     "gbs": n1 / t1 * 4 * v / 1e9},
+        "host": facts,
+    }
+
+
+def cpu_check_timed_rows(case, src, lp_dev, ids_dev, cols, nrows=PARITY_ROWS, seed=7):
+    """The oracle on a few of the timed output rows: their logits copied back
+    from the device tensor the GPU read, the oracle's row recomputed on one
+    thread, ids compared bit for bit and logprobs within 1e-5 (NaN and
+    infinities exactly).  Returns the counts and the oracle's one-thread
+    rate on these rows."""
     import oracle.logprob_oracle as LO
 
     tasks = LO.row_tasks(case.offsets, case.echo, case.top_n, case.tokens, case.sampled,
                          case.has_logits)
-    live = [o for o, t in enumerate(tasks) if t.top_n > 0][:max_rows]
-    src = logits_dev if case.has_logits else ntl_dev
-    rows = {}
-    for o in live:
-        r = tasks[o].src_row
-        if r not in rows:
-            rows[r] = src[r].cpu().numpy()
-    done, t_total, passes = 0, 0.0, 0
-    while t_total < budget_s:
-        passes += 1
-        for o in live:
-            t = tasks[o]
-            t0 = time.perf_counter()
-            LO.compute_row(rows[t.src_row], t.chosen, t.top_n, cols)
-            t_total += time.perf_counter() - t0
-            done += 1
-            if t_total >= budget_s and passes > 1:
-                break
-    return {"value": done / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {len(live)} read rows of {case.name}, {passes} passes, "
-                      f"{done} rows in {t_total:.1f} s (float64 log-softmax + full stable sort "
-                      f"per row, one thread)"}
+    live = [o for o, t in enumerate(tasks) if t.top_n > 0]
+    if not live:
+        return {"rows_checked": 0, "mismatches": 0}
+    rng = np.random.default_rng(seed)
+    pick = sorted(set([live[0], live[-1]] +
+                      [int(x) for x in rng.choice(live, size=min(nrows, len(live)), replace=False)]))
+    pick = pick[:max(nrows, 2)]
+    mism, worst, t_or = 0, 0.0, 0.0
+    for o in pick:
+        t = tasks[o]
+        row = src[t.src_row].cpu().numpy()
+        t0 = time.perf_counter()
+        want_lp, want_id = LO.compute_row(row, t.chosen, t.top_n, cols)
+        t_or += time.perf_counter() - t0
+        got_lp = lp_dev[o].cpu().numpy()
+        got_id = ids_dev[o].cpu().numpy()
+        ok = np.array_equal(got_id, want_id)
+        nan_g, nan_w = np.isnan(got_lp), np.isnan(want_lp)
+        ok &= np.array_equal(nan_g, nan_w)
+        inf = np.isinf(want_lp) | np.isinf(got_lp)
+        ok &= np.array_equal(got_lp[inf & ~nan_g], want_lp[inf & ~nan_w])
+        fin = ~nan_g & ~nan_w & ~inf
+        d = float(np.max(np.abs(got_lp[fin].astype(np.float64) - want_lp[fin]), initial=0.0))
+        worst = max(worst, d)
+        ok &= d <= 1e-5
+        mism += 0 if ok else 1
+    return {"rows_checked": len(pick), "mismatches": mism, "max_abs_lp_diff": worst,
+            "rows": pick, "oracle_one_thread_rows_per_s": len(pick) / t_or}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ragged_echo_mix")
-    ap.add_argument("--split", type=int, default=None, help="force the plan's split")
-    ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8|16)")
-    ap.add_argument("--levels", type=int, default=3,
-                    help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
-    ap.add_argument("--top-n", type=int, default=None,
-                    help="replace every nonzero top_n of the workload with this value")
-    ap.add_argument("--shards", type=int, default=0,
-                    help="also time the vocabulary-sharded path: this many equal shards, "
-                         "each reduced to records, then merged (all on this GPU)")
-    ap.add_argument("--temperature", type=float, default=None,
-                    help="log_softmax(logits / T) for every request")
-    ap.add_argument("--top-k", type=int, default=0,
-                    help="top-k front end (TopK on logits, then Softmax) for every request")
-    ap.add_argument("--no-probe", action="store_true",
-                    help="skip the plain-read probe over the same rows (the practical ceiling)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-e2e", action="store_true")
-    ap.add_argument("--copy-probe-mb", type=int, default=0,
-                    help="after timing, run 3 plain device copies of this many MiB "
-                         "(a known-size kernel for calibrating FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--summarize", nargs="+", metavar="DIR",
-                    help="print the rows of rocprofv3 csv output directories")
-    ap.add_argument("--write-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/row_kernel_<workload>_{trace,counters}.txt from a "
-                         "kernel-trace run and FETCH_SIZE / WRITE_SIZE runs of this workload")
-    args = ap.parse_args()
-    if args.summarize:
-        summarize(args.summarize)
-        return
-    if args.write_profile:
-        write_profile(args.workload, *args.write_profile, split=args.split, waves=args.waves)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "the log-probability kernels run on one GPU per process here; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
+def cpu_full(names):
+    """The oracle on every read row of each workload, on the host, one process
+    per available core (at most MAX_CPU_WORKERS) over requests, rows drawn on
+    the host per request (gen.request_logits_host)."""
+    import multiprocessing as mp
 
-    import torch
+    facts = _host_facts()
+    workers = max(1, min(MAX_CPU_WORKERS, facts["cores_available"]))
+    ctx = mp.get_context("fork")
+    for name in names:
+        import gen
 
+        case = gen.WORKLOADS[name]()
+        live = [n for n in range(case.batch) if int(case.top_n[n]) > 0]
+        t0 = time.perf_counter()
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_full_request, [(name, n) for n in live], chunksize=1)
+        wall = time.perf_counter() - t0
+        rows = sum(r[0] for r in res)
+        busy = sum(r[1] for r in res)
+        print(json.dumps({"workload": name, "rows": rows, "wall_s": wall, "cores": workers,
+                          "rows_per_s": rows / wall, "gbs": rows * 4 * case.vocab / wall / 1e9,
+                          "oracle_busy_s": busy, "one_core_rows_per_s": rows / busy,
+                          "host": facts,
+                          "note": "oracle over every read row; wall time includes drawing the "
+                                  "rows on the host; one_core_rows_per_s excludes it"}),
+              flush=True)
+
+
+def _full_request(arg):
     import gen
-    import ragged_token_log_amd as R
+    import oracle.logprob_oracle as LO
 
-    R.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    case = gen.WORKLOADS[args.workload]()
-    if args.top_n is not None:
-        case.top_n = np.where(np.asarray(case.top_n) > 0, args.top_n, 0)
-    steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
-    stream = torch.cuda.current_stream(dev)
+    name, n = arg
+    case = gen.WORKLOADS[name]()
+    tasks = LO.row_tasks(case.offsets, case.echo, case.top_n, case.tokens, case.sampled,
+                         case.has_logits)
+    counts, out_off = LO.output_counts_and_offsets(case.offsets, case.echo)
+    r0, _ = case.request_rows(n)
+    x = gen.request_logits_host(case, n)
+    busy, done = 0.0, 0
+    for j in range(int(counts[n])):
+        t = tasks[int(out_off[n]) + j]
+        t0 = time.perf_counter()
+        LO.compute_row(x[t.src_row - r0], t.chosen, t.top_n, 8)
+        busy += time.perf_counter() - t0
+        done += 1
+    return done, busy
 
-    base = gen.device_logits(case, dev, torch)
-    last = torch.from_numpy(case.offsets[1:].astype(np.int64) - 1).to(dev)
-    ntl = base.index_select(0, last) if case.has_logits else base
-    copy_bytes = base.numel() * 4
-    n_copies = max(1, math.ceil(ROTATE_BYTES / copy_bytes))
-    copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+
+# ---------------------------------------------------------------- GPU legs
+
+def _stats_us(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"mean_us": float(a.mean()), "median_us": float(np.median(a)),
+            "p10_us": float(np.percentile(a, 10)), "p90_us": float(np.percentile(a, 90))}
+
+
+def _timed_calls(calls, n_copies, steps, stream, torch):
+    """Runs steps calls back to back on `stream`, an event pair around each;
+    returns (per-call ms list, total ms from the first event to the last)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     torch.cuda.synchronize()
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        calls[i % n_copies]()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[-1])
 
+
+def _grouped_ms(calls, n_copies, steps, stream, torch):
+    """Mean ms per call over steps calls with no event between them."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        calls[i % n_copies]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def make_plan(R, case, args):
     plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits,
                   levels=args.levels)
     if args.split:
@@ -150,152 +323,74 @@ def main():
         plan.set_temperature(args.temperature)
     if args.top_k:
         plan.set_top_k(args.top_k)
+    return plan
+
+
+def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras=True):
+    """Times one workload: kernel path with resident descriptors (the step),
+    lp_compute_ragged per step, the probe; returns the record and what the
+    parity check needs."""
+    import gen
+
+    base = gen.device_logits(case, dev, torch)
+    plan = make_plan(R, case, args)
     info = plan.info()
-    lp, ids, ws = R.alloc_outputs(plan, dev, torch)
-    plan.stage(case.tokens, case.sampled, ws, stream)   # descriptors resident in HBM
-
-    launchers = [plan.launcher(src if case.has_logits else None,
-                               None if case.has_logits else src, lp, ids, ws, stream)
-                 for src in copies]
-
-    def step(i):
-        launchers[i % n_copies]()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # The timed region runs the K steps back to back on the launch stream.
-    # Events sit only between groups of steps (about ten groups), so that
-    # recording them adds almost nothing to a step; the per-group averages
-    # give the spread.
-    group = max(1, steps // 10)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps // group + 2)]
-    torch.cuda.synchronize()
-    marks[0].record(stream)
-    bounds = [0]
-    for i in range(steps):
-        step(i)
-        if (i + 1) % group == 0 or i + 1 == steps:
-            marks[len(bounds)].record(stream)
-            bounds.append(i + 1)
-    torch.cuda.synchronize()
-    total_ms = marks[0].elapsed_time(marks[len(bounds) - 1])
-    group_ms = [marks[j - 1].elapsed_time(marks[j]) / (bounds[j] - bounds[j - 1])
-                for j in range(1, len(bounds))]
-    ms_per_step = total_ms / steps
-    # one row-kernel launch per step when split == 1 (the plans of every
-    # workload here); with split > 1 a step also holds the merge kernel, so
-    # this is the duration of both
-    avg_launch_ms = ms_per_step
-
     read_rows = int(info["read_rows"])
-    rows_per_s = read_rows / (ms_per_step * 1e-3)
-    alg_bytes = algorithmic_bytes(info, case.vocab)
-    achieved_gbs = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
-
-    result = {
-        "metric": METRIC,
-        "value": rows_per_s,
-        "unit": "rows/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded draws with the workload's shapes and distributions)",
-        "config": {"workload": case.name, "batch": case.batch, "vocab": case.vocab,
-                   "levels": args.levels, "max_top_n": int(np.max(case.top_n)),
-                   "temperature": args.temperature if args.temperature is not None else 1.0,
-                   "top_k": args.top_k,
-                   "out_rows": int(info["out_rows"]), "read_rows": read_rows,
-                   "split": int(info["split"]), "waves": int(info["waves"]),
-                   "logits_copies_cycled": n_copies},
-        "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "row_kernel",
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "avg_launch_us": avg_launch_ms * 1e3,
-                     "p10_group_us": float(np.percentile(group_ms, 10)) * 1e3,
-                     "p90_group_us": float(np.percentile(group_ms, 90)) * 1e3},
-    }
-
-    if not args.no_e2e:
-        # host plan + descriptor upload over PCIe + launch, every step
-        e2e_steps = min(steps, 50)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(e2e_steps):
-            p2 = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits,
-                        levels=args.levels)
-            if args.split:
-                p2.set_split(args.split)
-            if args.waves:
-                p2.set_waves(args.waves)
-            if args.temperature is not None:
-                p2.set_temperature(args.temperature)
-            if args.top_k:
-                p2.set_top_k(args.top_k)
-            src = copies[i % n_copies]
-            p2.compute(src if case.has_logits else None, None if case.has_logits else src,
-                       case.tokens, case.sampled, lp, ids, ws, stream)
-            p2.close()
-        torch.cuda.synchronize()
-        e2e_ms = (time.perf_counter() - t0) * 1e3 / e2e_steps
-        result["e2e_host_inputs"] = {"ms_per_step": e2e_ms, "rows_per_s": read_rows / (e2e_ms * 1e-3),
-                                     "note": "plan + descriptor upload from host + launch per step"}
-
-    # host result assembly (lp_assemble_ragged) on this step's outputs, after
-    # their copy back: the per-request dicts of the page's compute_top
+    read_bytes = read_rows * 4 * case.vocab
+    alg = algorithmic_bytes(info, case.vocab)
+    n_copies = max(1, math.ceil(ROTATE_BYTES / max(read_bytes, 1)))
+    copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+    with torch.cuda.stream(stream):
+        lp, ids, ws = R.alloc_outputs(plan, dev, torch)
     torch.cuda.synchronize()
+    plan.stage(case.tokens, case.sampled, ws, stream)     # descriptors resident in HBM
+
+    def srcs(c):
+        return (c, None) if case.has_logits else (None, c)
+
+    launch = [plan.launcher(*srcs(c), lp, ids, ws, stream) for c in copies]
+    for i in range(warmup):
+        launch[i % n_copies]()
     t0 = time.perf_counter()
-    lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
-    t1 = time.perf_counter()
-    reps = 0
-    while True:
-        plan.assemble(lp_h, ids_h)
-        reps += 1
-        if time.perf_counter() - t1 > 0.2:
-            break
-    asm_ms = (time.perf_counter() - t1) * 1e3 / reps
-    result["host_assembly"] = {"ms": asm_ms, "rows_per_s": int(info["out_rows"]) / (asm_ms * 1e-3),
-                               "copy_back_ms": (t1 - t0) * 1e3,
-                               "note": "lp_assemble_ragged on the host, one thread; copy back "
-                                       "of the (R, C) outputs timed separately"}
-
-    if not args.no_probe and case.vocab % 4 == 0:
-        result["probe"] = bench_probe(copies, n_copies, read_rows, case.vocab, steps, stream, torch,
-                                      dev, R, alg_bytes, avg_launch_ms)
-
-    if args.shards:
-        result["shards"] = bench_shards(args, case, plan, info, copies, n_copies, torch, dev,
-                                        stream, ws)
-
-    if args.copy_probe_mb:
-        n = args.copy_probe_mb * (1 << 20) // 4
-        a = torch.ones(n, device=dev)
-        b = torch.empty_like(a)
+    ms_per_step = _grouped_ms(launch, n_copies, steps, stream, torch)
+    wall = time.perf_counter() - t0
+    per, _ = _timed_calls(launch, n_copies, steps, stream, torch)
+    st = _stats_us(per)
+    rec = {
+        "workload": case.name, "batch": case.batch, "vocab": case.vocab, "levels": args.levels,
+        "max_top_n": int(np.max(case.top_n)) if case.batch else 0,
+        "out_rows": int(info["out_rows"]), "read_rows": read_rows,
+        "split": int(info["split"]), "waves": int(info["waves"]), "depth": int(info["depth"]),
+        "direct_rows": int(info["direct_rows"]), "logits_copies_cycled": n_copies,
+        "algorithmic_bytes_per_launch": alg, "steps": steps, "ms_per_step": ms_per_step,
+        "host_wall_s": wall, "rows_per_s": read_rows / (ms_per_step * 1e-3),
+        "launch_with_event_pairs": st,
+        "gbs": alg / (ms_per_step * 1e-3) / 1e9,
+    }
+    rec["frac"] = rec["gbs"] / HBM_PEAK_GBS
+    if extras:
+        # lp_compute_ragged per step: host descriptors, PCIe upload, launch
+        comp = [plan.computer(*srcs(c), case.tokens, case.sampled, lp, ids, ws, stream)
+                for c in copies]
+        for i in range(3):
+            comp[i % n_copies]()
+        cper, _ = _timed_calls(comp, n_copies, steps, stream, torch)
+        cs = _stats_us(cper)
+        rec["compute_ragged"] = dict(cs, rows_per_s=read_rows / (cs["median_us"] * 1e-6),
+                                     gbs=alg / (cs["median_us"] * 1e-6) / 1e9,
+                                     note="lp_compute_ragged per step (host descriptor build, "
+                                          "PCIe upload, launch); event interval on the stream")
+        # leave the resident descriptors in place for the parity check
+        plan.stage(case.tokens, case.sampled, ws, stream)
+        launch[0]()
         torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    traffic = stored_traffic(case.name, info)
-    if traffic is not None:
-        result["roofline"]["traffic"] = traffic
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, base, ntl, cols=int(info["columns"]))
-
-    print(json.dumps(result), flush=True)
+    if probe and case.vocab % 4 == 0 and read_rows > 0:
+        rec["probe"] = bench_probe(copies, n_copies, read_rows, case.vocab, steps, stream, torch,
+                                   dev, R, ms_per_step * 1e3)
+    return rec, plan, info, base, lp, ids, ws, copies
 
 
-def bench_probe(copies, n_copies, rows, vocab, steps, stream, torch, dev, R, alg_bytes, kernel_ms):
+def bench_probe(copies, n_copies, rows, vocab, steps, stream, torch, dev, R, kernel_us):
     """The plain streaming read (lp_bench_stream_read: one workgroup per row,
     nontemporal 16-byte loads, a sum per row) over as many rows of the same
     width, cycling through the same copies: what the memory system gives a
@@ -304,18 +399,12 @@ def bench_probe(copies, n_copies, rows, vocab, steps, stream, torch, dev, R, alg
     launch = [R.binding.stream_read_launcher(c, rows, vocab, partial, stream) for c in copies]
     for i in range(3):
         launch[i % n_copies]()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(steps):
-        launch[i % n_copies]()
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / steps
+    us = _grouped_ms(launch, n_copies, steps, stream, torch) * 1e3
     gbs = rows * vocab * 4 / (us * 1e-6) / 1e9
     return {"us": us, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
-            "kernel_time_over_probe": kernel_ms * 1e3 / us,
-            "note": "plain read of the same number of rows and row width, same copies cycled"}
+            "kernel_time_over_probe": kernel_us / us,
+            "note": "plain read of the same number of rows and row width, same copies cycled, "
+                    "steps back to back between two events"}
 
 
 def bench_shards(args, case, plan, info, copies, n_copies, torch, dev, stream, ws):
@@ -361,6 +450,185 @@ def bench_shards(args, case, plan, info, copies, n_copies, torch, dev, stream, w
             "note": "one shard's record kernel (what each tensor-parallel rank runs on its "
                     "columns) and the merge over all shards' records, each averaged over "
                     f"{steps} back-to-back launches; shard copies rotated"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--split", type=int, default=None, help="force the plan's split")
+    ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8|16)")
+    ap.add_argument("--levels", type=int, default=3,
+                    help="heap depth: 2**levels output columns, top_n up to 2**levels - 1")
+    ap.add_argument("--top-n", type=int, default=None,
+                    help="replace every nonzero top_n of the workload with this value")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="also time the vocabulary-sharded path: this many equal shards, "
+                         "each reduced to records, then merged (all on this GPU)")
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="log_softmax(logits / T) for every request")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="top-k front end (TopK on logits, then Softmax) for every request")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the plain-read probe over the same rows (the practical ceiling)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode sub-record")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on every workload in full on the host, then exit")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many MiB "
+                         "(a known-size kernel for calibrating FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print the rows of rocprofv3 csv output directories")
+    ap.add_argument("--write-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/row_kernel_<workload>_{trace,counters}.txt from a "
+                         "kernel-trace run and FETCH_SIZE / WRITE_SIZE runs of this workload")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.write_profile:
+        write_profile(args.workload, *args.write_profile, split=args.split, waves=args.waves)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU per process; --gpus must be 1 "
+                                   "(rows shard across GPUs with no exchange, but the "
+                                   "multi-GPU path is not built)", "n_gpus": args.gpus}),
+              flush=True)
+        sys.exit(2)
+
+    import gen
+
+    if args.cpu_full:
+        cpu_full(list(gen.WORKLOADS))
+        return
+
+    case = gen.WORKLOADS[args.workload]()
+    if args.top_n is not None:
+        case.top_n = np.where(np.asarray(case.top_n) > 0, args.top_n, 0).astype(np.int32)
+    cols = 1 << args.levels if args.levels > 0 else 1
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before anything touches the GPU: the pool forks this process
+        cpu = cpu_baseline(case, cols)
+
+    import torch
+
+    import ragged_token_log_amd as R
+
+    R.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+
+    main_rec, plan, info, base, lp, ids, ws, copies = measure(
+        R, torch, dev, stream, case, args, steps, args.warmup, probe=not args.no_probe)
+    ms_per_step = main_rec["ms_per_step"]
+    read_rows = main_rec["read_rows"]
+    st = main_rec["launch_with_event_pairs"]
+    alg = main_rec["algorithmic_bytes_per_launch"]
+    achieved = main_rec["gbs"]
+
+    result = {
+        "metric": METRIC,
+        "value": read_rows / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded draws with the workload's shapes and distributions)",
+        "config": {k: main_rec[k] for k in ("workload", "batch", "vocab", "levels", "max_top_n",
+                                            "out_rows", "read_rows", "split", "waves", "depth",
+                                            "direct_rows", "logits_copies_cycled")},
+        "hbm_gbs": alg / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "row_kernel",
+                     "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_us": ms_per_step * 1e3,
+                     "median_launch_us_event_pairs": st["median_us"],
+                     "p10_launch_us_event_pairs": st["p10_us"],
+                     "p90_launch_us_event_pairs": st["p90_us"]},
+    }
+    result["config"]["temperature"] = args.temperature if args.temperature is not None else 1.0
+    result["config"]["top_k"] = args.top_k
+    for k in ("compute_ragged", "probe"):
+        if k in main_rec:
+            result[k] = main_rec[k]
+
+    # host result assembly (lp_assemble_ragged) on this step's outputs, after
+    # their copy back: the per-request dicts of the page's compute_top
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lp_h, ids_h = lp.cpu().numpy(), ids.cpu().numpy()
+    t1 = time.perf_counter()
+    reps = 0
+    while True:
+        plan.assemble(lp_h, ids_h)
+        reps += 1
+        if time.perf_counter() - t1 > 0.2:
+            break
+    asm_ms = (time.perf_counter() - t1) * 1e3 / reps
+    result["host_assembly"] = {"ms": asm_ms, "rows_per_s": int(info["out_rows"]) / (asm_ms * 1e-3),
+                               "copy_back_ms": (t1 - t0) * 1e3,
+                               "note": "lp_assemble_ragged on the host, one thread; copy back "
+                                       "of the (R, C) outputs timed separately"}
+
+    if args.shards:
+        result["shards"] = bench_shards(args, case, plan, info, copies, len(copies), torch, dev,
+                                        stream, ws)
+
+    traffic = stored_traffic(case.name, info)
+    if traffic is not None:
+        result["roofline"]["traffic"] = traffic
+
+    checks = []
+    if cpu is not None:
+        checks.append(cpu_check_timed_rows(case, base, lp, ids, cols))
+    del copies, base
+
+    if not args.no_decode and args.workload != SUB_WORKLOAD:
+        dcase = gen.WORKLOADS[SUB_WORKLOAD]()
+        if args.top_n is not None:
+            dcase.top_n = np.where(np.asarray(dcase.top_n) > 0, args.top_n, 0).astype(np.int32)
+        drec, dplan, dinfo, dbase, dlp, dids, _, dcopies = measure(
+            R, torch, dev, stream, dcase, args, DEFAULT_STEPS[SUB_WORKLOAD], args.warmup,
+            probe=not args.no_probe)
+        dtraffic = stored_traffic(dcase.name, dinfo)
+        drec["traffic"] = dtraffic
+        result["decode"] = drec
+        if cpu is not None:
+            checks.append(cpu_check_timed_rows(dcase, dbase, dlp, dids, cols))
+        del dcopies, dbase
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if cpu is not None:
+        cpu["timed_rows_check"] = checks
+        result["cpu_baseline"] = cpu
+        result["parity_rows_checked"] = sum(c["rows_checked"] for c in checks)
+        result["mismatches"] = sum(c["mismatches"] for c in checks)
+
+    print(json.dumps(result), flush=True)
+    if result.get("mismatches"):
+        sys.exit(1)
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "ragged_token_log_amd", "csrc", "logprob_kernels.hip")
@@ -466,7 +734,7 @@ def write_profile(workload, trace_dir, fetch_dir, write_dir, split=None, waves=N
     with open(os.path.join(PROFILES, f"row_kernel_{workload}_trace.txt"), "w") as f:
         f.write(f"rocprofv3 kernel trace: {workload}\n")
         f.write(f"command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace "
-                f"-- python bench.py --workload {workload} --no-cpu-baseline --no-e2e{flags}\n")
+                f"-- python bench.py --workload {workload} --no-cpu-baseline --no-decode{flags}\n")
         f.write(f"shape: {shape_text(info)}\n")
         f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
         f.write(f"algorithmic_bytes_per_launch: {alg}\n")
@@ -490,7 +758,7 @@ def write_profile(workload, trace_dir, fetch_dir, write_dir, split=None, waves=N
         for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
             f.write(f"command_{d}: rocprofv3 --pmc {c} --output-format csv -d <dir> -o {d} -- python "
                     f"bench.py --workload {workload} --steps 5 --warmup 1 --no-cpu-baseline "
-                    f"--no-e2e --copy-probe-mb 256{flags}\n")
+                    f"--no-decode --no-probe --copy-probe-mb 256{flags}\n")
         f.write(f"shape: {shape_text(info)}\n")
         f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
         f.write(f"kernel: {kname}\n")

@@ -155,7 +155,20 @@ WORKLOADS = {
 def request_logits_host(case: Case, n: int) -> np.ndarray:
     """Rows of request n (its full range, or its one next-token row)."""
     r0, r1 = case.request_rows(n)
-    rows = r1 - r0
+    return _draw_rows(case, n, r0, r1 - r0)
+
+
+def request_rows_sample(case: Case, n: int, k: int) -> np.ndarray:
+    """The first min(k, rows of request n) rows of request n's draw, without
+    drawing the rest: for the normal distributions these are exactly the
+    first rows of ``request_logits_host``; for the tie workload they are rows
+    of the same distribution from the same seed (its draw interleaves two
+    arrays, so a prefix is a different draw)."""
+    r0, r1 = case.request_rows(n)
+    return _draw_rows(case, n, r0, min(int(k), r1 - r0))
+
+
+def _draw_rows(case: Case, n: int, r0: int, rows: int) -> np.ndarray:
     rng = np.random.default_rng(_request_seq(case.seed, n))
     d = case.dist
     if d["kind"] == "normal":

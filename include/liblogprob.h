@@ -151,8 +151,8 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
  * §output 从 forward() 到响应对象的完整路径 applies before the softmax whose
  * result the logprobs reuse.  The ranking stays on the raw logits (for T > 0
  * it is the same order).  LP_ERR_TEMPERATURE, with the plan unchanged, if
- * some T_n lies outside [2^-126, 2^120] (or is NaN): inside it T_n, 1/T_n
- * and log2(e)/T_n are normal fp32 numbers, and two logits further apart
+ * some T_n lies outside [2^-126, 2^120] (or is NaN): inside it T_n and
+ * log2(e)/T_n are normal fp32 numbers, and two logits further apart
  * than the fp32 range (whose difference the kernels take as -inf) differ by
  * more than 256 after the division.
  * Applies to descriptors built after the call.
@@ -178,10 +178,11 @@ lp_status lp_plan_set_top_k(lp_plan *plan, const int32_t *batch_top_k);
 /*
  * Host-side row descriptors, for inspection (no HIP call).  Writes R rows of
  * 4 uint32 to desc_out: {logits row read, chosen token, top_n | k << 16 (k the top-k front
- * end; 0 on rows of top_n 0), 1/temperature bits}, in output
+ * end; 0 on rows of top_n 0), temperature bits}, in output
  * row order.  tokens: host, T uint32 (may be NULL when no request echoes);
  * sampled_tokens: host, B uint32.  LP_ERR_TOKEN_RANGE if an id >= V.  The
- * fourth word holds the fp32 bits of the row's 1 / temperature.
+ * fourth word holds the fp32 bits of the row's temperature (the kernels
+ * divide by it in fp64 when they write a log-probability).
  */
 lp_status lp_plan_descriptors(const lp_plan *plan, const uint32_t *tokens,
                               const uint32_t *sampled_tokens, uint32_t *desc_out);

@@ -134,11 +134,15 @@ def _ints(a, dtype, lo, hi, code, what):
 
 
 def _u32(a, n=None, what="tokens"):
+    """A 1-D uint32 copy of the host id array ``a`` (None stays None); with
+    ``n`` given it must hold exactly n entries, because the library reads
+    that many (LP_ERR_SHAPE otherwise)."""
     if a is None:
         return None
+    ndim = np.ndim(a)   # before the copy, which makes a scalar 1-D
     arr = _ints(a, np.uint32, 0, 0xFFFFFFFF, 7, what)
-    if n is not None and arr.shape[0] != n:
-        raise LogprobError(3, "array length")
+    if n is not None and (ndim != 1 or arr.shape[0] != n):
+        raise LogprobError(3, f"{what} must be 1-D with {n} entries, got shape {arr.shape}")
     return arr
 
 
@@ -193,6 +197,14 @@ class Plan:
         self.out_rows = int(rows.value)
         self.input_row_offsets = off
         self._columns = None
+
+    def _token_arrays(self, tokens, sampled_tokens):
+        """The host id arrays as the library reads them: tokens (T =
+        input_row_offsets[-1] entries, or None when no request echoes) and
+        sampled_tokens (batch entries)."""
+        tok = _u32(tokens, int(self.input_row_offsets[-1]), "tokens")
+        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
+        return tok, smp
 
     # ---------------------------------------------------------------- facts
     @property
@@ -255,10 +267,9 @@ class Plan:
 
     def descriptors(self, tokens, sampled_tokens) -> np.ndarray:
         """(R, 4) uint32, as the device reads them: logits row read, chosen
-        token, top_n | k << 16 (k the top-k front end), fp32 bits of
-        1 / temperature."""
-        tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
+        token, top_n | k << 16 (k the top-k front end), fp32 bits of the
+        temperature."""
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
         out = np.zeros((self.out_rows, 4), dtype=np.uint32)
         _check(self._lib.lp_plan_descriptors(self._h, _ptr(tok, ctypes.c_uint32),
                                              _ptr(smp, ctypes.c_uint32),
@@ -284,8 +295,7 @@ class Plan:
 
     # ---------------------------------------------------------------- device work
     def stage(self, tokens, sampled_tokens, workspace, stream=None):
-        tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
         _check(self._lib.lp_stage_ragged(self._h, _ptr(tok, ctypes.c_uint32),
                                          _ptr(smp, ctypes.c_uint32), _dev_ptr(workspace),
                                          _nbytes(workspace), _stream_ptr(stream)),
@@ -313,10 +323,28 @@ class Plan:
                 _check(st, "lp_launch_ragged")
         return launch
 
+    def computer(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
+                 out_token_ids, workspace, stream=None):
+        """A zero-argument callable doing lp_compute_ragged (descriptor build
+        and upload, then the launch) with these buffers, its arguments
+        checked and converted once; it keeps the host id arrays alive."""
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
+        fn = self._lib.lp_compute_ragged
+        args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _ptr(tok), _ptr(smp),
+                _dev_ptr(out_logprobs), _dev_ptr(out_token_ids), _dev_ptr(workspace),
+                ctypes.c_uint64(_nbytes(workspace)), _stream_ptr(stream))
+        keep = (tok, smp)
+
+        def compute():
+            st = fn(*args)
+            if st != 0:
+                _check(st, "lp_compute_ragged")
+            return keep
+        return compute
+
     def compute(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
                 out_token_ids, workspace, stream=None):
-        tok = _u32(tokens) if tokens is not None else None
-        smp = _u32(sampled_tokens, self.batch, "sampled_tokens")
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
         _check(self._lib.lp_compute_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
                                            _ptr(tok, ctypes.c_uint32), _ptr(smp, ctypes.c_uint32),
                                            _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
@@ -495,7 +523,11 @@ def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, 
     device = next_token_logits.device
     if stream is None:
         stream = torch.cuda.current_stream(device)
-    lp, ids, ws = alloc_outputs(plan, device, torch)
+    # Allocated on the launch stream: the caching allocator hands a freed
+    # block (the workspace, dropped on return) only to later work on that
+    # same stream, which runs after these kernels.
+    with torch.cuda.stream(stream):
+        lp, ids, ws = alloc_outputs(plan, device, torch)
     plan.compute(logits, next_token_logits, tokens, sampled_tokens, lp, ids, ws, stream)
     return lp, ids
 

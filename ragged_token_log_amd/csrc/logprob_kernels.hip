@@ -50,7 +50,7 @@ namespace dev {
 constexpr int kWave = 64;
 constexpr int kU = 4;                // float4 loads per lane per chunk
 constexpr int kChunkF4 = kWave * kU; // float4 per wave-chunk (1024 elements)
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2eF64 = 1.4426950408889634;   // log2(e)
 
 // ------------------------------------------------------------------ order keys
 
@@ -113,6 +113,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The exponent scale log2(e) / temperature of every sum e^((x - m) /
+// temperature) = 2^((x - m) * scale), rounded once from fp64.  The row and
+// merge kernels both take it from here, so partial sums scaled in one and
+// combined in the other agree.
+__device__ __forceinline__ float exp2_scale(float temp) {
+    return float(kLog2eF64 / double(temp));
+}
 
 // Orders this wave's LDS accesses around an LDS counter: the workgroup-scope
 // fences restricted to LDS wait only for outstanding LDS operations, never
@@ -335,10 +343,12 @@ struct RowArgs {
 // S = sum of e^((x - M) / temperature): the subtraction comes first, so a
 // large common offset of the row costs no accuracy, and it is done in fp64,
 // so logits at opposite ends of the fp32 range still give the finite value
-// that the division by a large temperature brings back into range (a few
-// lanes per row: the cost is nil).
-__device__ __forceinline__ float logprob(float x, float M, float inv_temp, float ln_s) {
-    return float((double(x) - double(M)) * double(inv_temp) - double(ln_s));
+// that the division by a large temperature brings back into range.  The
+// division itself is in fp64 too: (x - M) is exact there, so the quotient
+// carries no more than fp64 rounding, and the one rounding to fp32 at the
+// end is the only one of size (a few lanes per row: the cost is nil).
+__device__ __forceinline__ float logprob(float x, float M, float temp, float ln_s) {
+    return float((double(x) - double(M)) / double(temp) - double(ln_s));
 }
 
 // One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK
@@ -362,7 +372,7 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 template <int kK>
 __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint64_t o, int lane,
                                           uint64_t key, uint32_t top_word, float M, float S,
-                                          float inv_temp, float x_chosen, uint32_t chosen) {
+                                          float temp, float c, float x_chosen, uint32_t chosen) {
     constexpr uint64_t kC = uint64_t(kK) + 1;
     uint32_t listed = top_word & 0xFFFFu;
     const uint32_t keep = top_word >> 16;
@@ -370,17 +380,17 @@ __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint6
     if (keep != 0) {
         const bool kept = uint32_t(lane) < keep && key != 0;
         const float ms = (M == -INFINITY) ? 0.0f : M;
-        S = wave_sum_f32(kept ? fast_exp2((key_value(key) - ms) * (kLog2e * inv_temp)) : 0.0f);
+        S = wave_sum_f32(kept ? fast_exp2((key_value(key) - ms) * c) : 0.0f);
         chosen_kept = __ballot(kept && key_id(key) == chosen) != 0;
         if (keep < listed) listed = keep;
     }
     const float ln_s = logf(S);
     if (lane < kK) {
         const bool valid = uint32_t(lane) < listed && key != 0;
-        out_lp[o * kC + lane] = valid ? logprob(key_value(key), M, inv_temp, ln_s) : -INFINITY;
+        out_lp[o * kC + lane] = valid ? logprob(key_value(key), M, temp, ln_s) : -INFINITY;
         out_id[o * kC + lane] = valid ? key_id(key) : kPadId;
     } else if (lane == kK) {
-        out_lp[o * kC + lane] = chosen_kept ? logprob(x_chosen, M, inv_temp, ln_s) : -INFINITY;
+        out_lp[o * kC + lane] = chosen_kept ? logprob(x_chosen, M, temp, ln_s) : -INFINITY;
         out_id[o * kC + lane] = chosen;
     }
 }
@@ -460,9 +470,9 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
     const uint32_t ntr = (v1 - a0) & 3u;
 
-    // the row's 1 / temperature; sums are of e^((x - m) / temperature)
-    const float inv_temp = __uint_as_float(d.inv_temp_bits);
-    const float c = kLog2e * inv_temp;
+    // the row's temperature; sums are of e^((x - m) / temperature)
+    const float temp = __uint_as_float(d.temp_bits);
+    const float c = exp2_scale(temp);
     float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^((x - m) / temperature)
     uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
@@ -616,11 +626,15 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         // largest of the 64 values bounds it.
         float cm0 = -INFINITY;
         if (ch < nchunks) cm0 = lse_chunk(xb[0]);
-        s_lmax[wave * kWave + lane] = cm0;
+        // relaxed workgroup-scope atomics: other waves read these words
+        // with no barrier in between (each read sees -inf or a lane max)
+        __hip_atomic_store(&s_lmax[wave * kWave + lane], cm0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         float cmx = cm0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i)
-            if (i != wave) cmx = fmaxf(cmx, s_lmax[i * kWave + lane]);
+            if (i != wave)
+                cmx = fmaxf(cmx, __hip_atomic_load(&s_lmax[i * kWave + lane], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP));
         T = bound_from_lane_values(cmx, need);
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     wave_lse(M, S, c);
 
     if (!a.records) {
-        write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, inv_temp, x_chosen, d.chosen);
+        write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, temp, c, x_chosen, d.chosen);
     } else {
         uint64_t *rec = a.rec + uint64_t(o) * a.rec_row_stride + uint64_t(seg) * a.rec_seg_stride;
         if (lane == 0) {
@@ -812,8 +826,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     const uint64_t own = __ballot(owner);
     const float x_chosen = own != 0 ? readlane_f32(xc, __builtin_ctzll(own)) : __uint_as_float(0x7FC00000u);
-    const float inv_temp = __uint_as_float(d.inv_temp_bits);
-    wave_lse(m, s, kLog2e * inv_temp);
+    const float temp = __uint_as_float(d.temp_bits);
+    const float c = exp2_scale(temp);
+    wave_lse(m, s, c);
     const uint32_t nkeys = a.nseg * uint32_t(kK);
     // this wave's LDS: the records' keys (record r's slot p at r * kK + p)
     // and the kK best, placed by rank
@@ -876,7 +891,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         uint32_t found;
         top = wave_select<kK, kPer>(e, lane, &found);
     }
-    write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m, s, inv_temp, x_chosen, d.chosen);
+    write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, m, s, temp, c, x_chosen, d.chosen);
 }
 
 // Plans that read no row (every top_n is 0): all R * columns entries padding.

@@ -45,7 +45,7 @@ struct RowDesc {
     uint32_t chosen;    // token whose log-probability goes in the last column
     uint32_t top_n;     // low 16 bits: top_n (0 => padding only, logits not read);
                         // high 16 bits: the top-k front end's k (0 = none)
-    uint32_t inv_temp_bits;  // fp32 bits of 1 / temperature of the row's request
+    uint32_t temp_bits; // fp32 bits of the temperature of the row's request
 };
 static_assert(sizeof(RowDesc) == 16, "RowDesc is one 16-byte load");
 
@@ -72,7 +72,7 @@ struct lp_plan {
     std::vector<uint32_t> out_off;   // B+1
     std::vector<uint8_t> echo;       // B
     std::vector<int32_t> top_n;      // B
-    std::vector<float> inv_temp;     // B: 1 / temperature (1 unless set)
+    std::vector<float> temp;         // B: temperature (1 unless set)
     std::vector<uint32_t> top_k;     // B: top-k front end (0 = none unless set)
     uint64_t out_rows = 0;
     uint64_t read_rows = 0;

@@ -173,8 +173,8 @@ lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
             d.top_n = static_cast<uint32_t>(p.top_n[n]);
             if (d.top_n > 0) d.top_n |= p.top_k[n] << 16;
             uint32_t bits;
-            std::memcpy(&bits, &p.inv_temp[n], 4);
-            d.inv_temp_bits = bits;
+            std::memcpy(&bits, &p.temp[n], 4);
+            d.temp_bits = bits;
             out[o] = d;
         }
     }
@@ -229,7 +229,7 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         p->in_off.assign(input_row_offsets, input_row_offsets + batch + 1);
         p->echo.resize(batch);
         p->top_n.resize(batch);
-        p->inv_temp.assign(batch, 1.0f);
+        p->temp.assign(batch, 1.0f);
         p->top_k.assign(batch, 0u);
         p->out_off.resize(size_t(batch) + 1);
         uint64_t acc = 0, read = 0;
@@ -318,18 +318,18 @@ lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth) {
 lp_status lp_plan_set_temperature(lp_plan *plan, const float *batch_temperature) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (batch_temperature == nullptr) {
-        plan->inv_temp.assign(plan->batch, 1.0f);
+        plan->temp.assign(plan->batch, 1.0f);
         return LP_OK;
     }
     for (uint32_t n = 0; n < plan->batch; ++n) {
         const float t = batch_temperature[n];
-        // within [2^-126, 2^120]: T, 1/T and the kernels' exponent scale
+        // within [2^-126, 2^120]: T and the kernels' exponent scale
         // log2(e)/T are normal fp32 numbers, and a logit difference that
         // overflows fp32 (taken as -inf by the kernels) has a weight below
         // e^-256 after the division.  NaN fails both compares.
         if (!(t >= 0x1p-126f && t <= 0x1p120f)) return LP_ERR_TEMPERATURE;
     }
-    for (uint32_t n = 0; n < plan->batch; ++n) plan->inv_temp[n] = 1.0f / batch_temperature[n];
+    for (uint32_t n = 0; n < plan->batch; ++n) plan->temp[n] = batch_temperature[n];
     return LP_OK;
 }
 

@@ -45,9 +45,9 @@ int main(void) {
     CHECK(desc[4] == 1 && desc[5] == 6);
     CHECK(desc[8] == 2 && desc[9] == 9);
     CHECK(desc[12 + 2] == 0);
-    float inv_t;
-    memcpy(&inv_t, &desc[3], 4);
-    CHECK(inv_t == 1.0f);
+    float temp_word;
+    memcpy(&temp_word, &desc[3], 4);
+    CHECK(temp_word == 1.0f);
 
     /* temperature and top-k front end in the descriptors */
     const float temps[2] = {0.5f, 2.0f};
@@ -55,8 +55,8 @@ int main(void) {
     const int32_t ks[2] = {1, 0};
     CHECK(lp_plan_set_top_k(plan, ks) == LP_OK);
     CHECK(lp_plan_descriptors(plan, tokens, sampled, desc) == LP_OK);
-    memcpy(&inv_t, &desc[3], 4);
-    CHECK(inv_t == 2.0f && desc[2] == (2u | (1u << 16)));
+    memcpy(&temp_word, &desc[3], 4);
+    CHECK(temp_word == 0.5f && desc[2] == (2u | (1u << 16)));
     const int32_t bad_k[2] = {8, 0};
     CHECK(lp_plan_set_top_k(plan, bad_k) == LP_ERR_TOP_K);
     const float bad_t[2] = {0.0f, 1.0f};

@@ -314,16 +314,16 @@ def test_temperature_in_descriptors_and_errors():
     sampled = np.array([4, 5], np.uint32)
     plan.set_temperature([0.5, 2.0])
     desc = plan.descriptors(tokens, sampled)
-    inv = desc[:, 3].view(np.float32)
-    assert inv.tolist() == [2.0, 2.0, 0.5]           # rows of request 0, then request 1
+    temp = desc[:, 3].view(np.float32)
+    assert temp.tolist() == [0.5, 0.5, 2.0]          # rows of request 0, then request 1
     for bad in ([0.0, 1.0], [-1.0, 1.0], [np.inf, 1.0], [np.nan, 1.0], [1e-45, 1.0],
                 [2.0 ** -127, 1.0], [1.0, 3.5e-39], [1.0, 2.0 ** 121], [3.0e38, 1.0]):
         _expect("LP_ERR_TEMPERATURE", lambda b=bad: plan.set_temperature(b))
-    assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [2.0, 2.0, 0.5]
+    assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [0.5, 0.5, 2.0]
     # both ends of the accepted range [2^-126, 2^120]
     plan.set_temperature([2.0 ** -126, 2.0 ** 120])
-    inv = plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist()
-    assert inv == [2.0 ** 126, 2.0 ** 126, 2.0 ** -120]
+    temp = plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist()
+    assert temp == [2.0 ** -126, 2.0 ** -126, 2.0 ** 120]
     plan.set_temperature(None)
     assert plan.descriptors(tokens, sampled)[:, 3].view(np.float32).tolist() == [1.0] * 3
 
@@ -387,3 +387,19 @@ def test_out_of_range_integers_are_rejected_not_wrapped():
     # whole numbers in range still pass, whatever their dtype
     d = plan.descriptors(np.array([0, 3], np.int64), np.array([2.0]))
     assert d[:, :2].tolist() == [[0, 3], [1, 2]]
+
+
+def test_token_arrays_must_match_the_batch():
+    """The library reads input_row_offsets[-1] tokens and batch sampled
+    tokens; a shorter, longer or 2-D array is refused before any call reads
+    it (descriptors, staging and compute share the check)."""
+    plan = R.Plan([0, 64], [1], [3], 2 ** 32 - 1, True)
+    good = np.arange(64, dtype=np.uint32)
+    assert plan.descriptors(good, [1]).shape == (64, 4)
+    for bad in (np.array([0, 1, 2], np.uint32), np.arange(65, dtype=np.uint32),
+                np.arange(64, dtype=np.uint32).reshape(8, 8)):
+        _expect("LP_ERR_SHAPE", lambda b=bad: plan.descriptors(b, [1]))
+        _expect("LP_ERR_SHAPE", lambda b=bad: plan.stage(b, [1], None))
+        _expect("LP_ERR_SHAPE", lambda b=bad: plan.compute(None, None, b, [1], None, None, None))
+    for bad in ([], [1, 2], np.array([[1]], np.uint32), 5):
+        _expect("LP_ERR_SHAPE", lambda b=bad: plan.descriptors(good, b))

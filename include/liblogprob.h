@@ -231,6 +231,32 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits,
                             uint64_t workspace_bytes, void *stream);
 
 /*
+ * lp_compute_ragged_noalloc -- lp_compute_ragged for callers that cannot
+ * allocate memory (code that must not call hipMalloc or a caching allocator,
+ * tight serving loops): the same kernels and results, with no workspace
+ * argument and no allocation of any kind, device or pinned host.
+ *
+ * The workspace is a fixed device array of 4 MiB inside the library, one per
+ * GPU (each GPU holds it until the process ends), and the descriptors are
+ * built in a fixed host array of the same size.  LP_ERR_WORKSPACE, before
+ * any HIP call, if the plan's workspace_bytes exceeds 4 MiB (at the default
+ * levels, about 262000 output rows without a split).  Other arguments as for
+ * lp_compute_ragged; `stream` a hipStream_t (NULL = default stream).
+ *
+ * Because the host array is not pinned, the descriptor copy is synchronous:
+ * the call returns after the stream has finished its earlier work and the
+ * copy, then enqueues the kernels and does not wait for them.  Calls are
+ * serialised by a lock while they build and copy.  Every call on one GPU
+ * shares that GPU's array and leaves its last contents there: calls whose
+ * kernels overlap on one GPU (on different streams) race; calls on one
+ * stream are ordered.
+ */
+lp_status lp_compute_ragged_noalloc(const lp_plan *plan, const float *logits,
+                                    const float *next_token_logits, const uint32_t *tokens,
+                                    const uint32_t *sampled_tokens, float *out_logprobs,
+                                    uint32_t *out_token_ids, void *stream);
+
+/*
  * lp_assemble_ragged -- host-side result assembly of rows copied back from
  * the device ([MAX] §compute_top 的结果组装; no HIP call).
  *

@@ -28,7 +28,8 @@ EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
     "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_set_top_k", "lp_plan_descriptors",
     "lp_assemble_ragged",
-    "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_shard_records",
+    "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_compute_ragged_noalloc",
+    "lp_shard_records",
     "lp_merge_shards", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
 )
@@ -91,6 +92,7 @@ def load():
     lib.lp_stage_ragged.argtypes = [vp, vp, vp, vp, u64, vp]
     lib.lp_launch_ragged.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp]
     lib.lp_compute_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
+    lib.lp_compute_ragged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lp_shard_records.argtypes = [vp, u32, u32, vp, vp, vp, vp, u64, vp]
     lib.lp_merge_shards.argtypes = [vp, u32, vp, vp, vp, vp, u64, vp]
     lib.lp_plan_destroy.argtypes = [vp]
@@ -104,7 +106,8 @@ def load():
                  "lp_plan_set_top_k",
                  "lp_plan_descriptors", "lp_assemble_ragged",
                  "lp_stage_ragged", "lp_launch_ragged", "lp_shard_records", "lp_merge_shards",
-                 "lp_compute_ragged", "lp_bench_stream_read", "lp_last_hip_error"):
+                 "lp_compute_ragged", "lp_compute_ragged_noalloc", "lp_bench_stream_read",
+                 "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -350,6 +353,20 @@ class Plan:
                                            _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
                                            _dev_ptr(workspace), _nbytes(workspace),
                                            _stream_ptr(stream)), "lp_compute_ragged")
+
+    def compute_noalloc(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
+                        out_token_ids, stream=None):
+        """lp_compute_ragged_noalloc: the same computation with the library's
+        fixed device workspace (at most 4 MiB of workspace; no allocation).
+        Returns after the descriptor copy; the kernels run on ``stream``."""
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
+        _check(self._lib.lp_compute_ragged_noalloc(self._h, _dev_ptr(logits),
+                                                   _dev_ptr(next_token_logits),
+                                                   _ptr(tok, ctypes.c_uint32),
+                                                   _ptr(smp, ctypes.c_uint32),
+                                                   _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
+                                                   _stream_ptr(stream)),
+               "lp_compute_ragged_noalloc")
 
     def shard_records(self, vocab_begin: int, shard_logits, shard_next_token_logits, records,
                       workspace, stream=None):

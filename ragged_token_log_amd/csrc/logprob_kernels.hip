@@ -1103,6 +1103,45 @@ static lp_status check_workspace(const lp_plan *plan, const void *ws, uint64_t w
     return LP_OK;
 }
 
+// ------------------------------------------------------------------ no-allocation path
+//
+// For callers that cannot allocate: the workspace (descriptors, then split
+// records) lives in a fixed device array of kNoAllocScratchBytes, `scratch`
+// below, one copy per GPU the library runs on; the descriptors are built in a
+// fixed host array of the same size and copied from there.  In host code the
+// array's name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, asked once per device with that device current, and is
+// what the kernels and the copy receive.
+constexpr uint64_t kNoAllocScratchBytes = 4ull << 20;
+constexpr int kMaxDevices = 64;
+
+static std::mutex g_noalloc_mutex;                 // guards both arrays below
+static void *g_scratch_dev[kMaxDevices] = {};      // device address of `scratch`, per device
+alignas(256) static RowDesc g_noalloc_desc[kNoAllocScratchBytes / sizeof(RowDesc)];
+
+}  // namespace lp
+
+// The no-allocation path's device workspace (see above).  Nothing in it must
+// start at zero: every descriptor is copied in before the kernels read it, and
+// every split record is written by its row kernel before the merge reads it.
+static __device__ __align__(256) unsigned char scratch[lp::kNoAllocScratchBytes];
+
+namespace lp {
+
+// The device address of `scratch` on `device` (the current device), asked
+// once per device.  Called with g_noalloc_mutex held.
+static lp_status scratch_address(int device, void **out) {
+    if (device < 0 || device >= kMaxDevices) return LP_ERR_UNSUPPORTED;
+    if (g_scratch_dev[device] == nullptr) {
+        void *p = nullptr;
+        LP_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return LP_ERR_HIP;
+        g_scratch_dev[device] = p;
+    }
+    *out = g_scratch_dev[device];
+    return LP_OK;
+}
+
 }  // namespace lp
 
 extern "C" {
@@ -1190,6 +1229,35 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const floa
     if (st != LP_OK) return st;
     return lp_launch_ragged(plan, logits, next_token_logits, out_logprobs, out_token_ids,
                             workspace, workspace_bytes, stream);
+}
+
+lp_status lp_compute_ragged_noalloc(const lp_plan *plan, const float *logits,
+                                    const float *next_token_logits, const uint32_t *tokens,
+                                    const uint32_t *sampled_tokens, float *out_logprobs,
+                                    uint32_t *out_token_ids, void *stream) {
+    if (plan == nullptr) return LP_ERR_NULL_ARG;
+    if (plan->workspace_bytes > lp::kNoAllocScratchBytes) return LP_ERR_WORKSPACE;
+    if (plan->out_rows == 0) return LP_OK;
+    if (out_logprobs == nullptr || out_token_ids == nullptr) return LP_ERR_NULL_ARG;
+    if ((plan->has_logits ? logits : next_token_logits) == nullptr) return LP_ERR_NULL_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int device = 0;
+    LP_HIP_TRY(hipGetDevice(&device));
+    void *ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(lp::g_noalloc_mutex);
+        lp_status st = lp::scratch_address(device, &ws);
+        if (st != LP_OK) return st;
+        st = lp::build_descriptors(*plan, tokens, sampled_tokens, lp::g_noalloc_desc);
+        if (st != LP_OK) return st;
+        // the host array is not pinned: the copy is synchronous, and the
+        // stream is drained before the array may be refilled
+        LP_HIP_TRY(hipMemcpyWithStream(ws, lp::g_noalloc_desc, plan->out_rows * sizeof(lp::RowDesc),
+                                       hipMemcpyHostToDevice, s));
+        LP_HIP_TRY(hipStreamSynchronize(s));
+    }
+    return lp_launch_ragged(plan, logits, next_token_logits, out_logprobs, out_token_ids, ws,
+                            lp::kNoAllocScratchBytes, stream);
 }
 
 lp_status lp_shard_records(const lp_plan *plan, uint32_t vocab_begin, uint32_t shard_vocab,

@@ -403,3 +403,13 @@ def test_token_arrays_must_match_the_batch():
         _expect("LP_ERR_SHAPE", lambda b=bad: plan.compute(None, None, b, [1], None, None, None))
     for bad in ([], [1, 2], np.array([[1]], np.uint32), 5):
         _expect("LP_ERR_SHAPE", lambda b=bad: plan.descriptors(good, b))
+
+
+def test_noalloc_refuses_plans_beyond_its_workspace_before_any_hip_call():
+    """The no-allocation entry point's workspace is 4 MiB: a plan asking for
+    more is refused before any HIP call (so this runs without a GPU)."""
+    n = 300_000
+    plan = R.Plan(np.array([0, n], np.uint32), [1], [7], 32, True)
+    assert plan.workspace_bytes > 4 << 20
+    _expect("LP_ERR_WORKSPACE", lambda: plan.compute_noalloc(None, None, np.zeros(n, np.uint32),
+                                                             [0], None, None))

@@ -89,6 +89,7 @@ typedef struct lp_plan_info {
                                  and every top_n > 0): the kernel then addresses rows
                                  without waiting for their descriptors */
     uint32_t record_words;    /* 8-byte words of one partial record: 2^levels + 1 */
+    uint32_t deterministic;   /* 1 if lp_plan_set_deterministic(plan, 1) is in effect */
 } lp_plan_info;
 
 /*
@@ -142,6 +143,23 @@ lp_status lp_plan_set_waves(lp_plan *plan, uint32_t waves);
 /* Overrides the chunks in flight per wave (1 or 2); LP_ERR_UNSUPPORTED
  * otherwise.  Results are identical for either value. */
 lp_status lp_plan_set_depth(lp_plan *plan, uint32_t depth);
+
+/*
+ * Reproducibility of the log-probability values (ids, offsets and padding
+ * are exact in every mode).  By default (0), a plan that reads fewer than
+ * 1024 rows hands the chunks of a row past each wave's first ones to
+ * whichever wave of the workgroup frees a buffer first, so that the waves
+ * finish together; the fp32 rounding of the row's sum then depends on
+ * timing, and two runs may differ in the last bits of a log-probability
+ * (about 1e-6 here, well inside the 1e-5 bar against the float64
+ * definition).  Plans reading more rows use a fixed assignment and repeat
+ * bit for bit.  Nonzero fixes the assignment for every plan: the same inputs
+ * and plan shape give bit-identical outputs on every run, at some cost in
+ * speed on small batches (decode, 256 rows of 128256: about 0.8 us per
+ * launch).  Applies to launches after the call; LP_ERR_NULL_ARG for a NULL
+ * plan.
+ */
+lp_status lp_plan_set_deterministic(lp_plan *plan, int deterministic);
 
 /*
  * Per-request temperature (host, B floats; NULL restores 1 for all).  The

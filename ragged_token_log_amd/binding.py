@@ -26,7 +26,8 @@ STATUS_NAMES = {
 # every symbol include/liblogprob.h declares
 EXPORTED = (
     "lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split", "lp_plan_set_waves",
-    "lp_plan_set_depth", "lp_plan_set_temperature", "lp_plan_set_top_k", "lp_plan_descriptors",
+    "lp_plan_set_depth", "lp_plan_set_deterministic", "lp_plan_set_temperature",
+    "lp_plan_set_top_k", "lp_plan_descriptors",
     "lp_assemble_ragged",
     "lp_stage_ragged", "lp_launch_ragged", "lp_compute_ragged", "lp_compute_ragged_noalloc",
     "lp_shard_records",
@@ -60,6 +61,7 @@ class PlanInfo(ctypes.Structure):
         ("waves", ctypes.c_uint32), ("depth", ctypes.c_uint32),
         ("workspace_bytes", ctypes.c_uint64),
         ("direct_rows", ctypes.c_uint32), ("record_words", ctypes.c_uint32),
+        ("deterministic", ctypes.c_uint32),
     ]
 
 
@@ -85,6 +87,7 @@ def load():
     lib.lp_plan_set_split.argtypes = [vp, u32]
     lib.lp_plan_set_waves.argtypes = [vp, u32]
     lib.lp_plan_set_depth.argtypes = [vp, u32]
+    lib.lp_plan_set_deterministic.argtypes = [vp, ctypes.c_int]
     lib.lp_plan_set_temperature.argtypes = [vp, vp]
     lib.lp_plan_set_top_k.argtypes = [vp, vp]
     lib.lp_plan_descriptors.argtypes = [vp, vp, vp, vp]
@@ -102,7 +105,8 @@ def load():
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u32, u32, vp, vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
-                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_temperature",
+                 "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_deterministic",
+                 "lp_plan_set_temperature",
                  "lp_plan_set_top_k",
                  "lp_plan_descriptors", "lp_assemble_ragged",
                  "lp_stage_ragged", "lp_launch_ragged", "lp_shard_records", "lp_merge_shards",
@@ -238,6 +242,14 @@ class Plan:
 
     def set_depth(self, depth: int):
         _check(self._lib.lp_plan_set_depth(self._h, int(depth)), "lp_plan_set_depth")
+
+    def set_deterministic(self, deterministic: bool = True):
+        """Bit-reproducible log-probabilities (a fixed chunk assignment) when
+        true; by default the chunks go to whichever wave is free, which is
+        faster and may change the last bits of a value between runs (ids,
+        offsets and padding are exact either way)."""
+        _check(self._lib.lp_plan_set_deterministic(self._h, 1 if deterministic else 0),
+               "lp_plan_set_deterministic")
 
     def set_temperature(self, temperature):
         """Per-request temperatures (a scalar for all, a length-batch
@@ -467,7 +479,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
                                      sampled_tokens, batch_top_n, batch_echo, *,
                                      split: int | None = None, waves: int | None = None,
                                      depth: int | None = None, stream=None,
-                                     levels: int = LEVELS, temperature=None, top_k=None):
+                                     levels: int = LEVELS, temperature=None, top_k=None,
+                                     deterministic: bool = False):
     """Ragged batched token log-probabilities on the GPU.
 
     Arguments follow the MAX page's ``compute_log_probabilities_ragged``
@@ -485,6 +498,8 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     ``top_k`` (a scalar or one per request, 0 or None = none, at most C - 1)
     adds the FlashInfer page's TopK-then-Softmax front end: the k best tokens
     are kept and the log-probabilities renormalised over them.
+    ``deterministic`` makes the log-probability values bit-reproducible from
+    run to run (lp_plan_set_deterministic); ids and offsets always are.
 
     Returns ``(logprobs (R, C) float32, token_ids (R, C) uint32,
     output_row_offsets (batch+1,) uint32 numpy)``, the tensors on the GPU.
@@ -492,7 +507,7 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
     import torch
 
     plan = _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo,
-                         levels, temperature, top_k, torch)
+                         levels, temperature, top_k, torch, deterministic)
     try:
         lp, ids = _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves,
                        depth, stream, torch)
@@ -503,7 +518,7 @@ def compute_log_probabilities_ragged(input_row_offsets, logits, next_token_logit
 
 
 def _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo, levels,
-                  temperature, top_k, torch) -> Plan:
+                  temperature, top_k, torch, deterministic=False) -> Plan:
     """Checks the device tensors (2-D fp32 contiguous on one GPU, matching
     rows and vocabulary) and plans the batch with its options."""
     off = np.asarray(input_row_offsets)
@@ -523,6 +538,8 @@ def _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, bat
             plan.set_temperature(temperature)
         if top_k is not None:
             plan.set_top_k(top_k)
+        if deterministic:
+            plan.set_deterministic(True)
     except BaseException:
         plan.close()
         raise
@@ -551,7 +568,7 @@ def _run(plan, logits, next_token_logits, tokens, sampled_tokens, split, waves, 
 
 def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, tokens, sampled_tokens,
                              batch_top_n, batch_echo, *, levels: int = LEVELS, temperature=None,
-                             top_k=None, stream=None):
+                             top_k=None, stream=None, deterministic: bool = False):
     """The whole call of the MAX page's ``compute_log_probabilities_ragged``:
     the device computation, the copy back, and the host assembly
     (lp_assemble_ragged).  Returns one entry per request: None when its
@@ -560,7 +577,7 @@ def log_probabilities_ragged(input_row_offsets, logits, next_token_logits, token
     import torch
 
     plan = _checked_plan(input_row_offsets, logits, next_token_logits, batch_top_n, batch_echo,
-                         levels, temperature, top_k, torch)
+                         levels, temperature, top_k, torch, deterministic)
     try:
         if stream is None:
             stream = torch.cuda.current_stream(next_token_logits.device)

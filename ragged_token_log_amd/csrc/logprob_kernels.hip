@@ -272,6 +272,17 @@ __device__ __forceinline__ float strict_value(uint64_t T) {
     return hi >= 0x007FFFFFu ? key_value(uint64_t(hi + 1u) << 32) : -INFINITY;
 }
 
+// The larger of two logits.  Logits hold no NaN, so the IEEE maximum (which
+// propagates NaN and orders -0 below +0, neither of which changes a max
+// used as an exponent offset or as a superset test) serves; on gfx950 it is
+// v_maximum3_f32, which needs no quieting of its inputs, where fmaxf costs
+// a canonicalising max per loaded operand.
+__device__ __forceinline__ float max_nan_free(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float group_max(const f32x4 &v) {
+    return max_nan_free(max_nan_free(v.x, v.y), max_nan_free(v.z, v.w));
+}
+
 __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
@@ -279,15 +290,16 @@ __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
 // A bound from one real element per lane (or -inf for none): if `need`
 // lanes hold values >= t (counting lanes that tie), no element below t can be
 // in the top `need`, so the bound may be just under the smallest key of value
-// t.  t is the need-th largest of the 64 lane values, found bit by bit from
-// the top on their order-mapped high words: a bit stays set when at least
-// `need` lanes are at or above the prefix with it, 32 compare-and-count steps
-// for any count.  A -inf t excludes nothing.
+// t.  t is the need-th largest of the 64 lane values cut to the top 16 bits
+// of its order-mapped high word (sign, exponent and 7 mantissa bits: within
+// 1/128 of it), found bit by bit from the top: a bit stays set when at least
+// `need` lanes are at or above the prefix with it, 16 compare-and-count
+// steps for any count.  A -inf t excludes nothing.
 __device__ __forceinline__ uint64_t bound_from_lane_values(float v, uint32_t need) {
     const uint32_t u = uint32_t(order_key(v, kPadId) >> 32);
     uint32_t t = 0;
 #pragma unroll
-    for (int b = 31; b >= 0; --b) {
+    for (int b = 31; b >= 16; --b) {
         const uint32_t trial = t | (1u << b);
         if (uint32_t(__popcll(__ballot(u >= trial))) >= need) t = trial;
     }
@@ -405,6 +417,34 @@ __device__ __forceinline__ RowDesc load_desc_uniform(const RowDesc *desc, uint32
                    uint32_t(__builtin_amdgcn_readfirstlane(int(v.w)))};
 }
 
+// The descriptor of a workgroup's row as one 16-byte vector load (every lane
+// loads the same 16 bytes; one request per wave).  Vector loads return in
+// issue order, so a descriptor loaded ahead of the row's first chunks has
+// arrived by the time those chunks have, and waiting for it never waits for
+// anything else; a scalar load would share its counter with the LDS
+// operations, and the first LDS wait would then stall on it.
+__device__ __forceinline__ uint4 load_desc_vector(const RowDesc *desc, uint32_t o, uint32_t rows) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<RowDesc *>(desc), 0, int(rows * uint32_t(sizeof(RowDesc))), kBufferWord3);
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o * uint32_t(sizeof(RowDesc)), 0, 0));
+}
+
+__device__ __forceinline__ RowDesc desc_uniform(const uint4 v) {
+    return RowDesc{uint32_t(__builtin_amdgcn_readfirstlane(int(v.x))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.y))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))),
+                   uint32_t(__builtin_amdgcn_readfirstlane(int(v.w)))};
+}
+
+// Keys a row needs exactly: its top_n, or with the top-k front end its k
+// (the kept keys all enter the renormalised sum; k >= the listed slots),
+// within [1, kK].
+template <int kK>
+__device__ __forceinline__ uint32_t keys_needed(uint32_t top_word) {
+    const uint32_t raw = (top_word >> 16) != 0 ? (top_word >> 16) : (top_word & 0xFFFFu);
+    return raw < 1u ? 1u : (raw > uint32_t(kK) ? uint32_t(kK) : raw);
+}
+
 template <int kK>
 __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, uint64_t o, int lane) {
     constexpr uint64_t kC = uint64_t(kK) + 1;
@@ -415,10 +455,16 @@ __device__ __forceinline__ void write_padding(float *out_lp, uint32_t *out_id, u
 }
 
 // kDirect: output row o reads logits row o and no row is padding-only, so
-// the row's address does not wait for its descriptor (whose chosen token and
-// top_n are needed only at the end).
+// the row's address does not wait for its descriptor: its loads go out
+// first, behind one vector load of the descriptor, whose fields are read
+// when the first chunk has arrived.
 // kK: ranked slots per row (2^levels - 1).
-template <int kK, int kWaves, int kDepth, bool kDirect>
+// kDyn: chunks past each wave's first kDepth are handed out one at a time as
+// buffers free up (the waves of a workgroup then finish together), so which
+// wave sums which chunk, and with it the fp32 rounding of the row's sum,
+// depends on timing; without it the assignment is fixed and results are
+// reproducible bit for bit.
+template <int kK, int kWaves, int kDepth, bool kDirect, bool kDyn>
 __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
     static_assert(kThreads >= kChunkF4, "one thread per float4 of the partial chunk");
@@ -430,6 +476,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ uint64_t s_pub[kWaves];
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
+    __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
@@ -439,14 +486,19 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kPubJ = (kK + kWaves - 1) / kWaves - 1;        // published slot
     constexpr int kPubM = (kK + kPubJ) / (kPubJ + 1);           // waves needed
     constexpr bool kPubBound = kK >= 31 && kPubM >= kWaves - 1;  // its min or second min
-    const RowDesc d = load_desc_uniform(a.desc, o);
-    // Keys the row needs exactly: its top_n, or with the top-k front end its
-    // k (the kept keys all enter the renormalised sum; k >= the listed
-    // slots).  The bound is the wave's need-th key: need real keys above a
-    // key exclude it.  Slots past `need` are written as padding, so keys
-    // there may be incomplete.
-    const uint32_t need_raw = (d.top_n >> 16) != 0 ? (d.top_n >> 16) : (d.top_n & 0xFFFFu);
-    const uint32_t need = need_raw < 1u ? 1u : (need_raw > uint32_t(kK) ? uint32_t(kK) : need_raw);
+    // The bound is the wave's need-th key (keys_needed): need real keys above
+    // a key exclude it.  Slots past `need` are written as padding, so keys
+    // there may be incomplete.  With direct rows the descriptor (and so
+    // need, the temperature and the chosen token) is read after the first
+    // chunk has arrived.
+    uint4 dv{};
+    RowDesc d{};
+    if constexpr (kDirect) {
+        dv = load_desc_vector(a.desc, o, a.out_rows);
+    } else {
+        d = load_desc_uniform(a.desc, o);
+    }
+    uint32_t need = keys_needed<kK>(d.top_n);
 
     if (!kDirect && d.top_n == 0) {  // padding-only row: no logits read (the merge kernel pads record rows)
         if (!a.records && wave == 0) write_padding<kK>(a.out_lp, a.out_id, o, lane);
@@ -470,9 +522,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t nchunks = nf4 / uint32_t(kChunkF4);
     const uint32_t ntr = (v1 - a0) & 3u;
 
-    // the row's temperature; sums are of e^((x - m) / temperature)
-    const float temp = __uint_as_float(d.temp_bits);
-    const float c = exp2_scale(temp);
+    // the row's temperature; sums are of e^((x - m) / temperature) (with
+    // direct rows both are set when the descriptor is read)
+    float temp = kDirect ? 1.0f : __uint_as_float(d.temp_bits);
+    float c = kDirect ? 0.0f : exp2_scale(temp);
     float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^((x - m) / temperature)
     uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
@@ -503,10 +556,11 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
 
     // LSE update for one chunk; returns the lane's chunk max
     auto lse_chunk = [&](const f32x4 (&x)[kU]) __attribute__((always_inline)) {
-        float cm = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
+        // 16 values in 8 three-input maxima, a float4 at a time as they arrive
+        float cm = max_nan_free(max_nan_free(x[0].x, x[0].y), max_nan_free(x[0].z, x[0].w));
 #pragma unroll
         for (int u = 1; u < kU; ++u)
-            cm = fmaxf(cm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+            cm = max_nan_free(max_nan_free(max_nan_free(cm, x[u].x), x[u].y), max_nan_free(x[u].z, x[u].w));
         const float mn = fmaxf(m, cm);
         const float ms = (mn == -INFINITY) ? 0.0f : mn;
         float acc[kU];
@@ -555,7 +609,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         uint32_t cols = 0;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const float gm = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
+            const float gm = group_max(x[u]);
             if (__ballot(gm >= tv) == 0) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -604,10 +658,16 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const bool e1_ok = uint32_t(tid) < nh + ntr;
     const uint32_t e1 = uint32_t(tid) < nh ? v0 + uint32_t(tid) : a0 + 4u * nf4 + (uint32_t(tid) - nh);
     const float xr1 = row[e1_ok ? e1 : 0u];
-    // the chosen token's logit, from the segment that holds it
-    const uint32_t chosen_local = d.chosen - gid;
-    const bool owns_chosen = d.chosen >= gid && chosen_local >= v0 && chosen_local < v1;
-    const float x_chosen = row[(owns_chosen && lane == kK) ? chosen_local : 0u];
+    // the chosen token's logit, from the segment that holds it (with direct
+    // rows, once the descriptor is read, below)
+    bool owns_chosen = false;
+    float x_chosen = 0.0f;
+    auto load_chosen = [&]() __attribute__((always_inline)) {
+        const uint32_t chosen_local = d.chosen - gid;
+        owns_chosen = d.chosen >= gid && chosen_local >= v0 && chosen_local < v1;
+        x_chosen = row[(owns_chosen && lane == kK) ? chosen_local : 0u];
+    };
+    if constexpr (!kDirect) load_chosen();
     // LDS set-up (before any data can have arrived, so the barrier costs only
     // the spread of the waves' start)
     s_lmax[tid] = -INFINITY;
@@ -615,17 +675,57 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (tid == 0) {
         s_T = 0;
         s_done = 0;
+        s_next = uint32_t(kDepth * kWaves);
     }
     __syncthreads();
 
     {
-        // First chunk: the wave publishes its lanes' chunk maxima and seeds T
-        // from, per lane position, the max over the maxima the waves have
-        // published so far (its own at least); ones not yet written read
-        // -inf.  These are distinct elements of the row, so the kK-th
-        // largest of the 64 values bounds it.
+        // First chunk.  With direct rows it is copied aside and its buffer
+        // refilled at once, so that loads stay in flight while the wave
+        // computes the seed and ranks the chunk's candidates (decode, 256
+        // rows of 128256: 25.4 -> 25.0 us).  Rows found through their
+        // descriptors refill after the chunk, as in the loop (the early
+        // refill cost 1.3-1.5 us on 520 rows of 32000, one chunk deep).
+        // The wave publishes its lanes' chunk maxima and seeds T from, per
+        // lane position, the max over the maxima the waves have published so
+        // far (its own at least); ones not yet written read -inf.  These are
+        // distinct elements of the row, so the need-th largest of the 64
+        // values bounds it.
+        constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
+        // With kDyn each wave takes its next chunk index from an LDS counter
+        // one step ahead of the refill that needs it, so the atomic's
+        // latency hides under a chunk.  cb[b] is the chunk buffer b holds.
+        uint32_t cb[kDepth];
+#pragma unroll
+        for (int dd = 0; dd < kDepth; ++dd) cb[dd] = uint32_t(wave + dd * kWaves);
+        auto grab = [&]() __attribute__((always_inline)) {
+            uint32_t v = 0;
+            if (kDyn && lane == 0)
+                v = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return v;   // lane 0's value, read with readfirstlane when used
+        };
+        uint32_t gv = grab();
+        // refills buffer b with the next chunk: the grabbed one, or the one
+        // kAhead past what it held
+        auto refill_next = [&](f32x4 (&x)[kU], uint32_t &held) __attribute__((always_inline)) {
+            held = kDyn ? uint32_t(__builtin_amdgcn_readfirstlane(int(gv))) : held + kAhead;
+            refill(x, held);
+            if constexpr (kDyn) gv = grab();
+        };
+        f32x4 x0[kU];
+        if constexpr (kDirect) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) x0[u] = xb[0][u];
+            refill_next(xb[0], cb[0]);
+            d = desc_uniform(dv);
+            need = keys_needed<kK>(d.top_n);
+            temp = __uint_as_float(d.temp_bits);
+            c = exp2_scale(temp);
+            load_chosen();
+        }
+        f32x4 (&first)[kU] = kDirect ? x0 : xb[0];
         float cm0 = -INFINITY;
-        if (ch < nchunks) cm0 = lse_chunk(xb[0]);
+        if (ch < nchunks) cm0 = lse_chunk(first);
         // relaxed workgroup-scope atomics: other waves read these words
         // with no barrier in between (each read sees -inf or a lane max)
         __hip_atomic_store(&s_lmax[wave * kWave + lane], cm0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -633,36 +733,34 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < kWaves; ++i)
             if (i != wave)
-                cmx = fmaxf(cmx, __hip_atomic_load(&s_lmax[i * kWave + lane], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP));
+                cmx = max_nan_free(cmx, __hip_atomic_load(&s_lmax[i * kWave + lane], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_WORKGROUP));
         T = bound_from_lane_values(cmx, need);
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (ch < nchunks) topk_chunk(xb[0], ch, cm0);
-        constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
-        refill(xb[0], ch + kAhead);
-        ch += kWaves;
+        if (ch < nchunks) topk_chunk(first, ch, cm0);
+        if constexpr (!kDirect) refill_next(xb[0], cb[0]);
         // The remaining chunks of this wave go in whole rounds of kDepth steps
-        // (buffer d % kDepth holds chunk ch on the d-th step of a round); in
-        // the last round, steps past the end skip their chunk and their
-        // refill reads nothing.  The loop has one exit, at its bottom, and no
-        // buffer is read after it: an exit from the middle, or a use after
-        // the loop, would add paths on which buffers are copied between
-        // registers or every wait for loads in flight must be stricter.  The
-        // shared bound is read before each chunk's arithmetic, so that its
-        // latency hides there.
-        const uint32_t mine = nchunks > uint32_t(wave) ? (nchunks - uint32_t(wave) + kWaves - 1) / kWaves : 0u;
-        const uint32_t rounds = mine > 1 ? (mine - 1 + kDepth - 1) / uint32_t(kDepth) : 0u;
-        for (uint32_t r = 0; r < rounds; ++r) {
+        // (buffer d % kDepth on the d-th step of a round).  Buffers are
+        // processed in the order they were filled, so the chunk indices they
+        // hold increase in that order: once the next one is past the end,
+        // every later one is too, and the wave is done; within the last
+        // round, steps past the end skip their chunk and their refill reads
+        // nothing.  The loop has one exit, at its bottom, and no buffer is
+        // read after it: an exit from the middle, or a use after the loop,
+        // would add paths on which buffers are copied between registers or
+        // every wait for loads in flight must be stricter.  The shared bound
+        // is read before each chunk's arithmetic, so that its latency hides
+        // there.
+        while (cb[1 % kDepth] < nchunks) {
 #pragma unroll
             for (int dd = 1; dd <= kDepth; ++dd) {
-                if (ch < nchunks) {
+                if (cb[dd % kDepth] < nchunks) {
                     const uint64_t shared = lds_load_relaxed(&s_T);
                     const float cm = lse_chunk(xb[dd % kDepth]);
                     T = umax64(T, uniform64(shared));
-                    topk_chunk(xb[dd % kDepth], ch, cm);
+                    topk_chunk(xb[dd % kDepth], cb[dd % kDepth], cm);
                 }
-                refill(xb[dd % kDepth], ch + kAhead);
-                ch += kWaves;
+                refill_next(xb[dd % kDepth], cb[dd % kDepth]);
             }
         }
     }
@@ -1025,9 +1123,15 @@ static void staging_release(StagingSlot *sl) {
 }
 
 template <int kK, int kWaves, int kDepth>
-static void launch_shape(bool direct, dim3 grid, hipStream_t s, const dev::RowArgs &ra) {
-    if (direct) hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, true>), grid, dim3(kWaves * 64), 0, s, ra);
-    else hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, false>), grid, dim3(kWaves * 64), 0, s, ra);
+static void launch_shape(bool direct, bool dyn, dim3 grid, hipStream_t s, const dev::RowArgs &ra) {
+    const dim3 block(kWaves * 64);
+    if (direct) {
+        if (dyn) hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, true, true>), grid, block, 0, s, ra);
+        else hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, true, false>), grid, block, 0, s, ra);
+    } else {
+        if (dyn) hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, false, true>), grid, block, 0, s, ra);
+        else hipLaunchKernelGGL((dev::row_kernel<kK, kWaves, kDepth, false, false>), grid, block, 0, s, ra);
+    }
 }
 
 // What one call enqueues: the row kernel (rows or records), the merge
@@ -1039,16 +1143,16 @@ static void launch_k(const lp_plan &p, Launch what, dim3 grid, hipStream_t s,
                      const dev::RowArgs &ra, const dev::MergeArgs &ma, uint32_t waves,
                      uint32_t depth) {
     if (what != Launch::kMerge) {
-        const bool deep = depth == 2, direct = p.direct_rows != 0;
+        const bool deep = depth == 2, direct = p.direct_rows != 0, dyn = p.dynamic_chunks != 0;
         if (waves == 16) {
-            if (deep) launch_shape<kK, 16, 2>(direct, grid, s, ra);
-            else launch_shape<kK, 16, 1>(direct, grid, s, ra);
+            if (deep) launch_shape<kK, 16, 2>(direct, dyn, grid, s, ra);
+            else launch_shape<kK, 16, 1>(direct, dyn, grid, s, ra);
         } else if (waves == 8) {
-            if (deep) launch_shape<kK, 8, 2>(direct, grid, s, ra);
-            else launch_shape<kK, 8, 1>(direct, grid, s, ra);
+            if (deep) launch_shape<kK, 8, 2>(direct, dyn, grid, s, ra);
+            else launch_shape<kK, 8, 1>(direct, dyn, grid, s, ra);
         } else {
-            if (deep) launch_shape<kK, 4, 2>(direct, grid, s, ra);
-            else launch_shape<kK, 4, 1>(direct, grid, s, ra);
+            if (deep) launch_shape<kK, 4, 2>(direct, dyn, grid, s, ra);
+            else launch_shape<kK, 4, 1>(direct, dyn, grid, s, ra);
         }
     }
     if (what == Launch::kMerge || what == Launch::kRecordsThenMerge) {

@@ -80,6 +80,8 @@ struct lp_plan {
     uint32_t waves = 4;              // waves per workgroup: 4, 8 or 16
     uint32_t depth = 2;              // chunks in flight per wave: 1 or 2
     bool shape_set = false;          // waves or depth set by the caller
+    uint32_t deterministic = 0;      // 1: the caller asked for bit-reproducible sums
+    uint32_t dynamic_chunks = 0;     // 1: chunks go to whichever wave is free (see the plan)
     uint32_t direct_rows = 0;        // 1: output row o reads logits row o (all top_n > 0)
     uint64_t desc_bytes = 0;         // R * 16, rounded to 256
     uint64_t partial_bytes = 0;      // R * split * 8 (slots + 2) when split > 1

@@ -28,10 +28,10 @@ class DeviceRows:
 
 
 def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None,
-                waves=None, depth=None, levels=3):
+                waves=None, depth=None, levels=3, deterministic=False):
     lp, ids, out_off = R.compute_log_probabilities_ragged(
         offsets, logits, ntl, tokens, sampled, top_n, echo, split=split, waves=waves, depth=depth,
-        levels=levels)
+        levels=levels, deterministic=deterministic)
     torch.cuda.synchronize()
     return lp.cpu().numpy(), ids.cpu().numpy(), out_off
 

@@ -413,3 +413,12 @@ def test_noalloc_refuses_plans_beyond_its_workspace_before_any_hip_call():
     assert plan.workspace_bytes > 4 << 20
     _expect("LP_ERR_WORKSPACE", lambda: plan.compute_noalloc(None, None, np.zeros(n, np.uint32),
                                                              [0], None, None))
+
+
+def test_deterministic_flag_round_trips():
+    plan = R.Plan([0, 3, 5], [1, 0], [3, 2], 100, True)
+    assert plan.info()["deterministic"] == 0
+    plan.set_deterministic(True)
+    assert plan.info()["deterministic"] == 1
+    plan.set_deterministic(False)
+    assert plan.info()["deterministic"] == 0

@@ -678,18 +678,34 @@ def test_staging_pool_two_threads(R):
     assert not errors, errors[0]
 
 
-def test_deterministic_and_split_independent(R):
+@pytest.mark.parametrize("direct", [False, True])
+def test_deterministic_and_split_independent(R, direct):
+    """With lp_plan_set_deterministic the outputs repeat bit for bit; by
+    default the ids repeat exactly and the values within a few fp32 ulps
+    (the chunks' assignment to waves follows timing).  Ids never depend on
+    the split or shape, values only at that level."""
     c = gen.ragged_echo_mix(seed=9, batch=6, lmin=30, lmax=90)
+    if direct:
+        c.echo[:] = True
+        c.top_n = np.maximum(c.top_n, 1).astype(np.int32)
     logits = _dev(gen.host_logits(c))
     ntl = logits.index_select(0, torch.from_numpy(c.offsets[1:].astype(np.int64) - 1).cuda())
     args = (c.offsets, logits, ntl, c.tokens, c.sampled, c.top_n, c.echo)
-    a = run_library(R, torch, *args)
-    b = run_library(R, torch, *args)
-    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    for s, w, dp in ((None, None, None), (1, 8, 2), (1, 4, 1), (3, 16, 2)):
+        a = run_library(R, torch, *args, split=s, waves=w, depth=dp, deterministic=True)
+        b = run_library(R, torch, *args, split=s, waves=w, depth=dp, deterministic=True)
+        assert np.array_equal(a[1], b[1]), (s, w, dp)
+        assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32)), (s, w, dp)
+        for _ in range(3):
+            f = run_library(R, torch, *args, split=s, waves=w, depth=dp)
+            assert np.array_equal(a[1], f[1]), (s, w, dp)
+            np.testing.assert_allclose(a[0], f[0], rtol=0, atol=2e-6)
+    a = run_library(R, torch, *args, deterministic=True)
     for s, w, dp in ((2, 4, 2), (4, 8, 1), (64, 4, 1), (1, 8, 2), (1, 16, 1), (5, 16, 2), (1, 8, 1)):
-        d = run_library(R, torch, *args, split=s, waves=w, depth=dp)
-        assert np.array_equal(a[1], d[1]), (s, w, dp)
-        np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
+        for det in (True, False):
+            d = run_library(R, torch, *args, split=s, waves=w, depth=dp, deterministic=det)
+            assert np.array_equal(a[1], d[1]), (s, w, dp, det)
+            np.testing.assert_allclose(a[0], d[0], rtol=0, atol=2e-6)
 
 
 @pytest.mark.parametrize("levels", [4, 5, 6])

@@ -199,6 +199,20 @@ __device__ __forceinline__ void wave_lse(float &m, float &s, float c) {
     s = S;
 }
 
+// The (m, s) pairs of lanes 0..kN-1 merged (kN = 4, 8 or 16; other lanes are
+// ignored): DPP steps within the first 4, 8 or 16 lanes, after which lane 0
+// holds the result; fewer steps than a whole-wave reduction.
+template <int kN>
+__device__ __forceinline__ void lanes_lse(float &m, float &s, float c) {
+    static_assert(kN == 4 || kN == 8 || kN == 16, "4, 8 or 16 lanes");
+    lse_dpp_step<kDppXor1>(m, s, c);
+    lse_dpp_step<kDppXor2>(m, s, c);
+    if constexpr (kN >= 8) lse_dpp_step<kDppHalfMirror>(m, s, c);
+    if constexpr (kN >= 16) lse_dpp_step<kDppMirror>(m, s, c);
+    m = readlane_f32(m, 0);
+    s = readlane_f32(s, 0);
+}
+
 // Best kK keys of up to kPer*64 keys held kPer per lane (0 = empty).
 // Returns, in lane r < kK, the r-th best key (0 if fewer exist); *count gets
 // how many were found.  Each round finds the largest high word across the
@@ -739,6 +753,30 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(first, ch, cm0);
         if constexpr (!kDirect) refill_next(xb[0], cb[0]);
+        // the partial chunk and the single elements, from the registers they
+        // were loaded into at the start: handled now, so that no wave has
+        // them left to do after its last chunk
+        {
+            const f32x4 x4 = rest4_ok ? xr4 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            const float x1 = e1_ok ? xr1 : -INFINITY;
+            const float cm = fmaxf(fmaxf(fmaxf(x4.x, x4.y), fmaxf(x4.z, x4.w)), x1);
+            const float mn = fmaxf(m, cm);
+            const float ms = (mn == -INFINITY) ? 0.0f : mn;
+            const float add = (fast_exp2((x4.x - ms) * c) + fast_exp2((x4.y - ms) * c)) +
+                              (fast_exp2((x4.z - ms) * c) + fast_exp2((x4.w - ms) * c)) +
+                              fast_exp2((x1 - ms) * c);
+            s = s * fast_exp2((m - ms) * c) + add;
+            m = mn;
+            T = umax64(T, uniform64(lds_load_relaxed(&s_T)));
+            const float tv = threshold_value(T);
+            if (__ballot(cm >= tv) != 0) {
+                const uint32_t id4 = gid + a0 + 4u * rest4;
+                const float tv4 = rest4_ok ? tv : INFINITY;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) column(f4_get(x4, q), id4 + uint32_t(q), tv4);
+                column(x1, gid + e1, e1_ok ? tv : INFINITY);
+            }
+        }
         // The remaining chunks of this wave go in whole rounds of kDepth steps
         // (buffer d % kDepth on the d-th step of a round).  Buffers are
         // processed in the order they were filled, so the chunk indices they
@@ -762,30 +800,6 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                 }
                 refill_next(xb[dd % kDepth], cb[dd % kDepth]);
             }
-        }
-    }
-
-    // the partial chunk and the single elements, from the registers they
-    // were loaded into at the start
-    {
-        const f32x4 x4 = rest4_ok ? xr4 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        const float x1 = e1_ok ? xr1 : -INFINITY;
-        const float cm = fmaxf(fmaxf(fmaxf(x4.x, x4.y), fmaxf(x4.z, x4.w)), x1);
-        const float mn = fmaxf(m, cm);
-        const float ms = (mn == -INFINITY) ? 0.0f : mn;
-        const float add = (fast_exp2((x4.x - ms) * c) + fast_exp2((x4.y - ms) * c)) +
-                          (fast_exp2((x4.z - ms) * c) + fast_exp2((x4.w - ms) * c)) +
-                          fast_exp2((x1 - ms) * c);
-        s = s * fast_exp2((m - ms) * c) + add;
-        m = mn;
-        T = umax64(T, uniform64(lds_load_relaxed(&s_T)));
-        const float tv = threshold_value(T);
-        if (__ballot(cm >= tv) != 0) {
-            const uint32_t id4 = gid + a0 + 4u * rest4;
-            const float tv4 = rest4_ok ? tv : INFINITY;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) column(f4_get(x4, q), id4 + uint32_t(q), tv4);
-            column(x1, gid + e1, e1_ok ? tv : INFINITY);
         }
     }
 
@@ -863,7 +877,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         M = s_m[lane];
         S = s_s[lane];
     }
-    wave_lse(M, S, c);
+    lanes_lse<kWaves>(M, S, c);
 
     if (!a.records) {
         write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, temp, c, x_chosen, d.chosen);

@@ -483,6 +483,9 @@ def main():
                          "(a known-size kernel for calibrating FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print the rows of rocprofv3 csv output directories")
+    ap.add_argument("--write-counter-table", nargs="+", metavar="ARG",
+                    help="NAME DIR [DIR ...]: write profiles/NAME.txt, the per-dispatch mean of "
+                         "every counter in these rocprofv3 --pmc runs of this workload, per kernel")
     ap.add_argument("--write-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/row_kernel_<workload>_{trace,counters}.txt from a "
                          "kernel-trace run and FETCH_SIZE / WRITE_SIZE runs of this workload")
@@ -492,6 +495,9 @@ def main():
         return
     if args.write_profile:
         write_profile(args.workload, *args.write_profile, split=args.split, waves=args.waves)
+        return
+    if args.write_counter_table:
+        write_counter_table(args.workload, args.write_counter_table[0], args.write_counter_table[1:])
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU per process; --gpus must be 1 "
@@ -772,6 +778,35 @@ def write_profile(workload, trace_dir, fetch_dir, write_dir, split=None, waves=N
         f.write(f"algorithmic_bytes_per_launch: {alg}\n")
         f.write(f"traffic_over_algorithmic: {traffic / alg:.4f}\n")
     print(f"wrote profiles for {workload}: traffic/algorithmic = {traffic / alg:.4f}")
+
+
+def write_counter_table(workload, name, dirs):
+    """profiles/<name>.txt: for each rocprofv3 --pmc output directory (one
+    run each, of `bench.py --workload <workload> --no-cpu-baseline
+    --no-decode --steps 50`), the per-dispatch mean of every counter, for
+    the log-probability kernels and the plain-read probe."""
+    rows = {}
+    cmds = []
+    for d in dirs:
+        names = set()
+        for r in _kernel_rows(d, "counter_collection.csv"):
+            k = r["Kernel_Name"]
+            if not any(t in k for t in ("row_kernel", "merge_kernel", "stream_read_kernel")):
+                continue
+            names.add(r["Counter_Name"])
+            rows.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        cmds.append(f"rocprofv3 --pmc {' '.join(sorted(names))} --output-format csv -d <dir> -o <name> "
+                    f"-- python bench.py --workload {workload} --no-cpu-baseline --no-decode --steps 50")
+    with open(os.path.join(PROFILES, f"{name}.txt"), "w") as f:
+        f.write(f"rocprofv3 counters: {workload} (per-dispatch mean over the run's dispatches)\n")
+        for c in cmds:
+            f.write(f"command: {c}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+        for k, cs in sorted(rows.items()):
+            f.write(f"kernel: {k}\n")
+            for c, v in sorted(cs.items()):
+                f.write(f"  {c}: {sum(v) / len(v):.1f}  (dispatches={len(v)})\n")
+    print(f"wrote profiles/{name}.txt")
 
 
 def summarize(dirs):

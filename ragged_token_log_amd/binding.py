@@ -326,29 +326,34 @@ class Plan:
     def launcher(self, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
                  stream=None):
         """A zero-argument callable doing lp_launch_ragged with these buffers,
-        its ctypes arguments converted once (for tight launch loops)."""
+        its ctypes arguments converted once (for tight launch loops).  It
+        holds references to the tensors, so their memory cannot go back to
+        the caching allocator while the callable exists."""
         fn = self._lib.lp_launch_ragged
         args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _dev_ptr(out_logprobs),
                 _dev_ptr(out_token_ids), _dev_ptr(workspace), ctypes.c_uint64(_nbytes(workspace)),
                 _stream_ptr(stream))
+        keep = (logits, next_token_logits, out_logprobs, out_token_ids, workspace, self)
 
         def launch():
             st = fn(*args)
             if st != 0:
                 _check(st, "lp_launch_ragged")
+            return keep
         return launch
 
     def computer(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
                  out_token_ids, workspace, stream=None):
         """A zero-argument callable doing lp_compute_ragged (descriptor build
         and upload, then the launch) with these buffers, its arguments
-        checked and converted once; it keeps the host id arrays alive."""
+        checked and converted once; it keeps the host id arrays and the
+        tensors alive."""
         tok, smp = self._token_arrays(tokens, sampled_tokens)
         fn = self._lib.lp_compute_ragged
         args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _ptr(tok), _ptr(smp),
                 _dev_ptr(out_logprobs), _dev_ptr(out_token_ids), _dev_ptr(workspace),
                 ctypes.c_uint64(_nbytes(workspace)), _stream_ptr(stream))
-        keep = (tok, smp)
+        keep = (tok, smp, logits, next_token_logits, out_logprobs, out_token_ids, workspace, self)
 
         def compute():
             st = fn(*args)
@@ -430,9 +435,11 @@ def stream_read_launcher(x, rows: int, row_len: int, partial, stream=None):
     lib = load()
     args = (_dev_ptr(x), ctypes.c_uint32(rows), ctypes.c_uint32(row_len), _dev_ptr(partial),
             _stream_ptr(stream))
+    keep = (x, partial)
 
     def launch():
         _check(lib.lp_bench_stream_read(*args), "lp_bench_stream_read")
+        return keep
     return launch
 
 

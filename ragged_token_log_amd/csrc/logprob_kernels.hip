@@ -246,6 +246,28 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
 // with at most one key per lane it searches from 7 slots up.
 constexpr int kRankMergeMinK = 15;
 
+// Fewest slots for which a chunk's candidates may be merged into the wave's
+// list in bulk (gathered, then placed by rank) rather than one key at a
+// time, and for which the end ranks the waves' lists on every wave of the
+// workgroup.  From 31 slots the list spans rows of 16 lanes and one
+// insertion costs two lane permutes and about 300 cycles.  Bulk merging
+// pays where chunks bring many keys: always at 63 slots, and at 31 on rows
+// short enough that a wave has at most kBulkMaxChunksPerWave chunks of them
+// (most of its chunks come while its bound is still low).  Same box, 31
+// slots: 520 rows of 32000, 27.4 -> 26.3 us; 256 rows of 128256, 31.0 ->
+// 32.5 us had it been used there.
+constexpr int kBulkMinK = 31;
+constexpr int kBulkAlwaysK = 63;
+constexpr uint32_t kBulkMaxChunksPerWave = 8;
+constexpr int kParallelEndMinK = 31;
+// Gathered keys that a wave inserts one at a time rather than merging: a
+// merge costs about as much as three or four single insertions.
+constexpr uint32_t kBulkFewKeys = 3;
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
 // The number of keys above `key` in a list of kK keys sorted in descending
 // order (0 for empty slots), kK = 2^L - 1: a branchless binary search of L
 // probes.
@@ -491,6 +513,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_done;
     __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
+    constexpr bool kBulk = kK >= kBulkMinK;
+    constexpr bool kParallelEnd = kK >= kParallelEndMinK;
+    __shared__ uint64_t s_cand[kBulk ? kWaves * kWave : 1];   // per wave: a chunk's candidates
+    __shared__ uint64_t s_new[kBulk ? kWaves * kK : 1];       // per wave: the merged list
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
@@ -605,6 +631,48 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         }
     };
 
+    const bool use_bulk =
+        kBulk && (kK >= kBulkAlwaysK || nchunks <= kBulkMaxChunksPerWave * uint32_t(kWaves));
+
+    // Large K: merges the n keys a wave has gathered in its s_cand slots (keys
+    // above T, distinct, unsorted) into its sorted list.  A list key's new
+    // position is its old one plus the gathered keys above it, counted with
+    // broadcast reads; a gathered key's is the gathered keys above it plus
+    // the list keys above it, found by binary search.  The keys are distinct,
+    // so the positions are too; the first kK are kept, and T rises to the
+    // need-th.  About one insertion's cost, whatever n (<= 64).
+    auto bulk_merge = [&](uint32_t n) __attribute__((always_inline)) {
+        uint64_t *cand = s_cand + wave * kWave;
+        uint64_t *sl = s_keys + wave * kK;   // this wave's slots, free until the end
+        uint64_t *nl = s_new + wave * kK;
+        if (lane < kK) {
+            sl[lane] = list;
+            nl[lane] = 0ull;
+        }
+        lds_release();
+        lds_acquire();
+        const uint64_t mine = uint32_t(lane) < n ? cand[lane] : 0ull;
+        uint32_t above_l = 0, above_c = 0;
+#pragma unroll 4
+        for (uint32_t k = 0; k < n; ++k) {
+            const uint64_t b = cand[k];   // a broadcast read
+            above_l += b > list ? 1u : 0u;
+            above_c += b > mine ? 1u : 0u;
+        }
+        if (lane < kK && list != 0) {
+            const uint32_t r = uint32_t(lane) + above_l;
+            if (r < uint32_t(kK)) nl[r] = list;
+        }
+        if (mine != 0) {
+            const uint32_t r = above_c + count_above<kK>(sl, mine);
+            if (r < uint32_t(kK)) nl[r] = mine;
+        }
+        lds_release();
+        lds_acquire();
+        list = lane < kK ? nl[lane] : 0ull;
+        T = umax64(T, readlane_u64(list, int(need) - 1));
+    };
+
     // The filter value for chunk ch against the bound as it stands.
     auto chunk_tv = [&](uint32_t ch) __attribute__((always_inline)) {
         const uint32_t first = gid + a0 + ch * uint32_t(kChunkF4 * 4);
@@ -633,10 +701,49 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                                                   __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
         const uint32_t lane_id = gid + a0 + ch * uint32_t(kChunkF4 * 4) + 4u * uint32_t(lane);
-        while (cols != 0) {
-            const uint32_t j = uint32_t(__builtin_ctz(cols));
-            cols &= cols - 1;
-            column(xv[j], lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u), tv);
+        if (use_bulk) {
+            // gather the keys above T column by column into this wave's
+            // s_cand slots (ballot and lane prefix), merging first whenever a
+            // column would overflow the 64 slots
+            uint64_t *cand = s_cand + wave * kWave;
+            uint32_t n = 0;
+            while (cols != 0) {
+                const uint32_t j = uint32_t(__builtin_ctz(cols));
+                cols &= cols - 1;
+                const float v = xv[j];
+                const bool pass = v >= tv;
+                const uint64_t key = order_key(v, lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u));
+                uint64_t mask = __ballot(pass && key > T);
+                if (mask == 0) continue;
+                if (n + uint32_t(__popcll(mask)) > uint32_t(kWave)) {
+                    bulk_merge(n);
+                    n = 0;
+                    mask = __ballot(pass && key > T);
+                    if (mask == 0) continue;
+                }
+                if (pass && key > T) cand[n + lanes_below(mask)] = key;
+                n += uint32_t(__popcll(mask));
+            }
+            if (n > kBulkFewKeys) {
+                bulk_merge(n);
+            } else if (n != 0) {
+                // few keys (long rows once the list is full): one at a time
+                lds_release();
+                lds_acquire();
+                for (uint32_t k = 0; k < n; ++k) {
+                    const uint64_t key = uniform64(cand[k]);
+                    if (key > T) {
+                        list = list_insert<kK>(list, key, lane);
+                        T = umax64(T, readlane_u64(list, int(need) - 1));
+                    }
+                }
+            }
+        } else {
+            while (cols != 0) {
+                const uint32_t j = uint32_t(__builtin_ctz(cols));
+                cols &= cols - 1;
+                column(xv[j], lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u), tv);
+            }
         }
         if constexpr (kPubBound) {
             // A bound from every wave's (kPubJ+1)-th key: kPubM of them at or
@@ -812,29 +919,18 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         s_m[wave] = m;
         s_s[wave] = s;
     }
-    lds_release();
-    if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
-    lds_acquire();
-
     constexpr int kN = kWaves * kK;
     constexpr int kPer = (kN + kWave - 1) / kWave;
     uint64_t top;
-    // The waves' lists are sorted: from 7 slots up (with one key per lane,
-    // or from 15 with more) a binary search ranks each key in fewer LDS
-    // round trips than counting; below, counting; 7 slots over more keys
-    // than lanes take kK wave-wide rounds.
-    constexpr bool kSearch = kK >= kRankMergeMinK || (kK >= 7 && kPer == 1);
-    if constexpr (kSearch) {
-        // a key's rank is the number of keys above it in all the lists
-        // together (in its own list, its position, the keys being distinct),
-        // each list binary-searched in log2(kK + 1) probes; the best kK go
-        // to their rank
-        if (lane < kK) s_top[lane] = 0ull;
-        lds_release();
-#pragma unroll 1
-        for (int i = 0; i < kPer; ++i) {
-            const int idx = lane + kWave * i;
-            const uint64_t key = idx < kN ? s_keys[idx] : 0ull;
+    if constexpr (kParallelEnd) {
+        // Large K: every wave ranks its share of the waves' kN (< threads)
+        // keys, one per thread, each a binary search in every list; wave 0
+        // then writes the row.  Ranking on one wave took kPer rounds of
+        // log2(kK + 1) dependent probes (6.5 us at 63 slots).
+        if (wave == 0 && lane < kK) s_top[lane] = 0ull;
+        __syncthreads();
+        if (tid < kN) {
+            const uint64_t key = s_keys[tid];
             if (key != 0) {
                 uint32_t rank = 0;
 #pragma unroll
@@ -842,35 +938,67 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                 if (rank < uint32_t(kK)) s_top[rank] = key;
             }
         }
-        lds_release();
-        lds_acquire();
-        top = lane < kK ? s_top[lane] : 0ull;
-    } else if constexpr (kPer == 1) {
-        // at most one key per lane: each key's rank is the number of keys
-        // above it (the keys are distinct but for empty slots, 0), counted
-        // with broadcast reads and independent compares rather than kK
-        // rounds of wave-wide maxima; the best kK go to their rank
-        // (lanes exchange values through s_top: the fences keep the
-        // compiler from forwarding a lane's own store to its read-back)
-        if (lane < kK) s_top[lane] = 0ull;
-        const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
-        uint32_t rank = 0;
-#pragma unroll 8
-        for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
-        lds_release();
-        if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
-        lds_release();
-        lds_acquire();
+        __syncthreads();
+        if (wave != 0) return;
         top = lane < kK ? s_top[lane] : 0ull;
     } else {
-        uint64_t e[kPer];
+        lds_release();
+        if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
+        lds_acquire();
+
+        // The waves' lists are sorted: from 7 slots up (with one key per lane,
+        // or from 15 with more) a binary search ranks each key in fewer LDS
+        // round trips than counting; below, counting; 7 slots over more keys
+        // than lanes take kK wave-wide rounds.
+        constexpr bool kSearch = kK >= kRankMergeMinK || (kK >= 7 && kPer == 1);
+        if constexpr (kSearch) {
+            // a key's rank is the number of keys above it in all the lists
+            // together (in its own list, its position, the keys being distinct),
+            // each list binary-searched in log2(kK + 1) probes; the best kK go
+            // to their rank
+            if (lane < kK) s_top[lane] = 0ull;
+            lds_release();
+#pragma unroll 1
+            for (int i = 0; i < kPer; ++i) {
+                const int idx = lane + kWave * i;
+                const uint64_t key = idx < kN ? s_keys[idx] : 0ull;
+                if (key != 0) {
+                    uint32_t rank = 0;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const uint32_t idx = uint32_t(lane + kWave * i);
-            e[i] = idx < uint32_t(kN) ? s_keys[idx] : 0ull;
+                    for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
+                    if (rank < uint32_t(kK)) s_top[rank] = key;
+                }
+            }
+            lds_release();
+            lds_acquire();
+            top = lane < kK ? s_top[lane] : 0ull;
+        } else if constexpr (kPer == 1) {
+            // at most one key per lane: each key's rank is the number of keys
+            // above it (the keys are distinct but for empty slots, 0), counted
+            // with broadcast reads and independent compares rather than kK
+            // rounds of wave-wide maxima; the best kK go to their rank
+            // (lanes exchange values through s_top: the fences keep the
+            // compiler from forwarding a lane's own store to its read-back)
+            if (lane < kK) s_top[lane] = 0ull;
+            const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
+            uint32_t rank = 0;
+#pragma unroll 8
+            for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
+            lds_release();
+            if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
+            lds_release();
+            lds_acquire();
+            top = lane < kK ? s_top[lane] : 0ull;
+        } else {
+            uint64_t e[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t idx = uint32_t(lane + kWave * i);
+                e[i] = idx < uint32_t(kN) ? s_keys[idx] : 0ull;
+            }
+            uint32_t found;
+            top = wave_select<kK, kPer>(e, lane, &found);
         }
-        uint32_t found;
-        top = wave_select<kK, kPer>(e, lane, &found);
     }
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {

@@ -874,3 +874,25 @@ def test_calls_on_streams_other_than_the_current_one(R):
     torch.cuda.synchronize()
     for i, (lp, ids, off) in enumerate(outs):
         assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), off, ref, f"stream call {i}")
+
+
+def test_launcher_holds_its_buffers(R):
+    """A launcher keeps the tensors it was made from: with every other
+    reference dropped and the caching allocator handing out blocks of the
+    same sizes (filled with garbage), its launches still read the staged
+    descriptors and write outputs that match the oracle."""
+    c = gen.ragged_echo_mix(seed=33, batch=5, lmin=20, lmax=80, vocab=12007)
+    logits = gen.host_logits(c)
+    ntl = gen.next_token_rows(c, logits)
+    ref = oracle(c.offsets, logits, ntl, c.tokens, c.sampled, c.top_n, c.echo)
+    plan = R.Plan(c.offsets, c.echo, c.top_n, c.vocab, True)
+    lp, ids, ws = R.alloc_outputs(plan, torch.device("cuda"), torch)
+    plan.stage(c.tokens, c.sampled, ws, torch.cuda.current_stream())
+    launch = plan.launcher(_dev(logits), None, lp, ids, ws)
+    shapes = [(t.shape, t.dtype) for t in (lp, ids, ws)]
+    del lp, ids, ws
+    churn = [torch.full(sh, 7, dtype=dt, device="cuda") for sh, dt in shapes for _ in range(3)]
+    held = launch()
+    torch.cuda.synchronize()
+    del churn
+    assert_parity(held[2].cpu().numpy(), held[3].cpu().numpy(), plan.out_off, ref, "launcher buffers")

@@ -40,6 +40,7 @@
 #include <memory>
 #include <mutex>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "lp_internal.h"
@@ -102,6 +103,23 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
 }
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) { return readlane_u64(v, 0); }
+
+// The minimum over the first kN (<= 16) lanes' values, all lanes of the
+// first row of 16 taking part (lanes kN..15 must hold ~0).
+template <int kN>
+__device__ __forceinline__ uint64_t first_lanes_min_u64(uint64_t v) {
+    static_assert(kN >= 2 && kN <= 16, "within one row");
+    auto step = [&](auto ctrl) __attribute__((always_inline)) {
+        constexpr int kCtrl = decltype(ctrl)::value;
+        const uint64_t o = (uint64_t(dpp_u32<kCtrl>(uint32_t(v >> 32))) << 32) | dpp_u32<kCtrl>(uint32_t(v));
+        v = o < v ? o : v;
+    };
+    step(std::integral_constant<int, kDppXor1>{});
+    if constexpr (kN > 2) step(std::integral_constant<int, kDppXor2>{});
+    if constexpr (kN > 4) step(std::integral_constant<int, kDppHalfMirror>{});
+    if constexpr (kN > 8) step(std::integral_constant<int, kDppMirror>{});
+    return readlane_u64(v, 0);
+}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<kDppXor1>(v));
@@ -260,6 +278,7 @@ constexpr int kBulkMinK = 31;
 constexpr int kBulkAlwaysK = 63;
 constexpr uint32_t kBulkMaxChunksPerWave = 8;
 constexpr int kParallelEndMinK = 31;
+constexpr int kSeedAllMinK = 31;
 // Gathered keys that a wave inserts one at a time rather than merging: a
 // merge costs about as much as three or four single insertions.
 constexpr uint32_t kBulkFewKeys = 3;
@@ -323,21 +342,27 @@ __device__ __forceinline__ float f4_get(const f32x4 &v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// A bound from one real element per lane (or -inf for none): if `need`
-// lanes hold values >= t (counting lanes that tie), no element below t can be
-// in the top `need`, so the bound may be just under the smallest key of value
-// t.  t is the need-th largest of the 64 lane values cut to the top 16 bits
-// of its order-mapped high word (sign, exponent and 7 mantissa bits: within
-// 1/128 of it), found bit by bit from the top: a bit stays set when at least
-// `need` lanes are at or above the prefix with it, 16 compare-and-count
-// steps for any count.  A -inf t excludes nothing.
-__device__ __forceinline__ uint64_t bound_from_lane_values(float v, uint32_t need) {
-    const uint32_t u = uint32_t(order_key(v, kPadId) >> 32);
+// The high word of a value's order key: larger values map to larger words.
+__device__ __forceinline__ uint32_t order_value(float v) { return uint32_t(order_key(v, kPadId) >> 32); }
+
+// A bound from kN distinct real elements per lane, given as order values (0
+// for none): if `need` of them are >= t (counting ties), no element below t
+// can be in the top `need`, so the bound may be just under the smallest key
+// of value t.  t is the need-th largest of the values cut to their top 16
+// bits (sign, exponent and 7 mantissa bits: within 1/128 of it), found bit
+// by bit from the top: a bit stays set when at least `need` values are at or
+// above the prefix with it, 16 compare-and-count steps for any count.  A
+// -inf t excludes nothing.
+template <int kN>
+__device__ __forceinline__ uint64_t bound_from_lane_values(const uint32_t (&u)[kN], uint32_t need) {
     uint32_t t = 0;
 #pragma unroll
     for (int b = 31; b >= 16; --b) {
         const uint32_t trial = t | (1u << b);
-        if (uint32_t(__popcll(__ballot(u >= trial))) >= need) t = trial;
+        uint32_t n = 0;
+#pragma unroll
+        for (int i = 0; i < kN; ++i) n += uint32_t(__popcll(__ballot(u[i] >= trial)));
+        if (n >= need) t = trial;
     }
     return t > 0 ? (uint64_t(t) << 32) - 1 : 0ull;  // low word 0: smallest key of value t
 }
@@ -505,7 +530,13 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     constexpr int kThreads = kWaves * kWave;
     static_assert(kThreads >= kChunkF4, "one thread per float4 of the partial chunk");
     static_assert(kK >= 1 && kK < kWave, "one lane per column");
-    __shared__ float s_lmax[kThreads];
+    // The seed's per-position maxima over the waves' first chunks, as order
+    // values: with 31 or more slots 4 per lane (one per float4 group) once
+    // every wave has added its own, else one per lane from whichever waves
+    // have added theirs.
+    constexpr bool kSeedAll = kK >= kSeedAllMinK;
+    constexpr int kSeedN = kSeedAll ? kU : 1;
+    __shared__ uint32_t s_lmax[kSeedN * kWave];
     __shared__ uint64_t s_keys[kWaves * kK];
     __shared__ uint64_t s_top[kK];
     __shared__ uint64_t s_T;
@@ -525,7 +556,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     const uint32_t seg = blockIdx.x - o * a.split;
     constexpr int kPubJ = (kK + kWaves - 1) / kWaves - 1;        // published slot
     constexpr int kPubM = (kK + kPubJ) / (kPubJ + 1);           // waves needed
-    constexpr bool kPubBound = kK >= 31 && kPubM >= kWaves - 1;  // its min or second min
+    constexpr bool kPubBound = kK >= 31 && kPubM >= kWaves;       // their minimum
     // The bound is the wave's need-th key (keys_needed): need real keys above
     // a key exclude it.  Slots past `need` are written as padding, so keys
     // there may be incomplete.  With direct rows the descriptor (and so
@@ -751,17 +782,15 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
             // (the waves' shares are disjoint, and a published key only
             // grows, so stale reads are weaker, never wrong).  Tighter than
             // the largest K-th key of one wave; it pays only for large K.
+            // lane w < kWaves reads wave w's key, and a DPP minimum over
+            // those lanes gives the bound (8 LDS reads in a row cost about
+            // as much as one insertion)
+            static_assert(kPubM == kWaves, "every wave's key is needed");
             const uint64_t mine = readlane_u64(list, kPubJ);
             if (lane == 0) __hip_atomic_store(&s_pub[wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            uint64_t lo1 = ~0ull, lo2 = ~0ull;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const uint64_t v = w == wave ? mine : __hip_atomic_load(&s_pub[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                lo2 = v < lo1 ? lo1 : (v < lo2 ? v : lo2);
-                lo1 = v < lo1 ? v : lo1;
-            }
-            const uint64_t b = uniform64(kPubM == kWaves ? lo1 : lo2);
-            T = umax64(T, b);
+            uint64_t v = ~0ull;
+            if (lane < kWaves) v = lane == wave ? mine : lds_load_relaxed(&s_pub[lane]);
+            T = umax64(T, first_lanes_min_u64<kWaves>(v));
         }
         if (T != T0 && lane == 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
@@ -791,7 +820,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if constexpr (!kDirect) load_chosen();
     // LDS set-up (before any data can have arrived, so the barrier costs only
     // the spread of the waves' start)
-    s_lmax[tid] = -INFINITY;
+    if (tid < kSeedN * kWave) s_lmax[tid] = 0u;
     if (tid < kWaves) s_pub[tid] = 0;
     if (tid == 0) {
         s_T = 0;
@@ -847,16 +876,28 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         f32x4 (&first)[kU] = kDirect ? x0 : xb[0];
         float cm0 = -INFINITY;
         if (ch < nchunks) cm0 = lse_chunk(first);
-        // relaxed workgroup-scope atomics: other waves read these words
-        // with no barrier in between (each read sees -inf or a lane max)
-        __hip_atomic_store(&s_lmax[wave * kWave + lane], cm0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        float cmx = cm0;
+        if constexpr (kSeedAll) {
+            // per (float4 group, lane) the largest of the waves' group
+            // maxima: 256 distinct elements, each the largest of 4 * kWaves
+            uint32_t ux[kU];
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i)
-            if (i != wave)
-                cmx = max_nan_free(cmx, __hip_atomic_load(&s_lmax[i * kWave + lane], __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_WORKGROUP));
-        T = bound_from_lane_values(cmx, need);
+            for (int u = 0; u < kU; ++u) {
+                ux[u] = ch < nchunks ? order_value(group_max(first[u])) : 0u;
+                __hip_atomic_fetch_max(&s_lmax[u * kWave + lane], ux[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kU; ++u) ux[u] = s_lmax[u * kWave + lane];
+            T = bound_from_lane_values<kU>(ux, need);
+        } else {
+            // per lane the largest chunk maximum of the waves that have added
+            // theirs (this one's at least); a relaxed atomic, since other
+            // waves add theirs with no barrier in between
+            const uint32_t u0 = order_value(cm0);
+            const uint32_t prev = __hip_atomic_fetch_max(&s_lmax[lane], u0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t ux[1] = {prev > u0 ? prev : u0};
+            T = bound_from_lane_values<1>(ux, need);
+        }
         if (lane == 0 && T != 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (ch < nchunks) topk_chunk(first, ch, cm0);
         if constexpr (!kDirect) refill_next(xb[0], cb[0]);

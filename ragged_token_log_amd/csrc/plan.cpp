@@ -35,7 +35,8 @@ void size_workspace(lp_plan &p) {
 constexpr uint64_t kManyRows = 1024;
 constexpr uint64_t kCUs = 256;
 constexpr uint64_t kSplitBelow = 129;   // at most 128 rows: segments (two per row or more)
-constexpr uint64_t kSplitBelowManySlots = 128;
+constexpr uint64_t kLargeKMaxSplit = 4;        // 31+ slots: segments per row at most
+constexpr uint32_t kLargeKMinSegment = 8000;   // 31+ slots: shortest segment of a short row
 constexpr uint32_t kVeryShortRow = 20480;
 constexpr uint32_t kShortRow = 65536;
 constexpr uint32_t kMinSegment = 32768;
@@ -76,15 +77,39 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
     const bool many = read_rows >= kManyRows || read_rows == 0;
 
     if (slots >= 31) {
-        // Levels 5 and 6: every wave of every segment pays ~K ln(n / K)
-        // insertions, so fewer waves pay.  1024 rows or more: 4 waves (16-68
-        // % ahead of 8 or 16).  Fewer: 8 waves two deep, whole rows, except
-        // 31 slots over fewer than 128 rows longer than kShortRow, which gain
-        // from segments (8 rows of 128256: 21 against 29 us whole; of 256000:
-        // 25 against 31 us for 7 segments of 16 waves).
-        *waves = many ? 4 : 8;
-        if (!many && slots == 31 && read_rows < kSplitBelowManySlots && vocab > kShortRow)
-            *split = few_rows_split(read_rows, vocab, slots, min_split);
+        // Levels 5 and 6, timed on decode batches of 16-2048 rows at V =
+        // 32000 to 256000.  1024 rows or more: 4 waves two deep (within 2 %
+        // of the fastest shape).  257-1023 rows: 8 waves one deep (520 rows
+        // of 32000: 24.8 against 31.4 us two deep).  129-256: 16 waves one
+        // deep (256 rows of 128256 at levels 6: 32.2 against 36.8 us for 8
+        // two deep).  At most 128: 16 waves one deep, up to 4 segments a row
+        // (16 rows of 151936 at levels 6: 23.3 against 37.3 us whole; 8
+        // segments lose to 4 from 63 slots and win by at most 2 % at 31);
+        // rows of at most kShortRow are cut only up to 64 rows, in segments
+        // of at least kLargeKMinSegment over 8 waves (16 rows of 32000: 13.1
+        // against 14.0 us whole).  The seed waits for every wave, so more
+        // waves give it more data, and the merge of 4 records stays short.
+        if (many) {
+            *waves = 4;
+            return;
+        }
+        *depth = 1;
+        if (read_rows > kCUs || vocab <= kVeryShortRow) {
+            *waves = 8;
+            return;
+        }
+        *waves = 16;
+        if (read_rows >= kSplitBelow) return;
+        uint64_t s = kCUs / read_rows;
+        if (s > kLargeKMaxSplit) s = kLargeKMaxSplit;
+        if (vocab <= kShortRow) {
+            const uint64_t by_vocab = vocab / kLargeKMinSegment;
+            s = s < kLargeKMaxSplit ? 1 : (by_vocab < s ? by_vocab : s);
+            if (s > 1) *waves = 8;
+        }
+        if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
+        if (s < 1) s = 1;
+        *split = s < min_split ? min_split : static_cast<uint32_t>(s);
         return;
     }
     if (many) {

@@ -193,16 +193,23 @@ def test_few_rows_shape(rows, vocab, shape):
 
 @pytest.mark.parametrize("levels,rows,vocab,shape", [
     (5, 2048, 32000, (1, 4, 2)), (6, 2048, 128256, (1, 4, 2)), (5, 1024, 256000, (1, 4, 2)),
-    (5, 512, 128256, (1, 8, 2)), (6, 32, 256000, (1, 8, 2)), (6, 96, 151936, (1, 8, 2)),
-    (5, 32, 256000, (8, 8, 2)), (5, 64, 151936, (4, 8, 2)), (5, 32, 128256, (8, 8, 2)),
-    (5, 96, 70001, (2, 8, 2)), (5, 32, 65536, (1, 8, 2)),
-    (5, 128, 256000, (1, 8, 2)), (4, 32, 151936, (8, 8, 2)), (4, 80, 128256, (3, 8, 2)),
+    (5, 512, 128256, (1, 8, 1)), (6, 520, 32000, (1, 8, 1)), (6, 300, 16000, (1, 8, 1)),
+    (6, 200, 16000, (1, 8, 1)), (5, 256, 128256, (1, 16, 1)), (6, 129, 32000, (1, 16, 1)),
+    (6, 32, 256000, (4, 16, 1)), (6, 96, 151936, (2, 16, 1)), (6, 16, 151936, (4, 16, 1)),
+    (5, 32, 256000, (4, 16, 1)), (5, 64, 151936, (4, 16, 1)), (5, 32, 128256, (4, 16, 1)),
+    (5, 96, 70001, (2, 16, 1)), (5, 80, 128256, (3, 16, 1)), (5, 128, 256000, (2, 16, 1)),
+    (5, 32, 65536, (4, 8, 1)), (6, 16, 32000, (4, 8, 1)), (6, 64, 32000, (4, 8, 1)),
+    (6, 64, 24000, (3, 8, 1)), (6, 65, 32000, (1, 16, 1)), (5, 128, 32000, (1, 16, 1)),
+    (6, 8, 1 << 29, (4, 16, 1)), (6, 200, 1 << 29, (2, 16, 1)),
+    (4, 32, 151936, (8, 8, 2)), (4, 80, 128256, (3, 8, 2)),
     (4, 96, 128256, (2, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
 def test_shape_by_ranked_slots(levels, rows, vocab, shape):
-    """With 31 or more ranked slots every wave's insertions weigh more: 4
-    waves for many rows, 8 two deep for fewer, segments only for 31 slots
-    over few long rows; 15 slots keep the segments of 7 but take 8 waves two
-    deep from three segments a row."""
+    """With 31 or more ranked slots: 4 waves two deep for many rows, 8 one
+    deep above one row per compute unit, 16 one deep below, with up to 4
+    segments a row at most 128 rows (short rows only up to 64 rows, then
+    over 8 waves); 15 slots keep the segments of 7 but take 8 waves two deep
+    from three segments a row.  A row beyond the streamed range is always
+    cut."""
     plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool),
                   np.full(rows, (1 << levels) - 1), vocab, False, levels=levels)
     info = plan.info()

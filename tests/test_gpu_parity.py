@@ -784,12 +784,13 @@ def test_default_split_pairs(R):
     assert_parity(*got, ref, "default split pairs")
 
 
-@pytest.mark.parametrize("levels,shape", [(3, (8, 16, 1)), (4, (8, 8, 2)), (5, (8, 8, 2))])
+@pytest.mark.parametrize("levels,shape", [(3, (8, 16, 1)), (4, (8, 8, 2)), (5, (4, 16, 1)),
+                                          (6, (4, 16, 1))])
 def test_default_segments_of_long_rows(R, levels, shape):
     """8 next-token rows of 128256 entries: the default plan cuts each row
-    into 8 segments of at least 16000 entries (8 waves two deep from 15
-    ranked slots up) and merges the records; every row matches the oracle,
-    special rows included."""
+    into 8 segments of at least 16000 entries (8 waves two deep at 15 ranked
+    slots), or 4 from 31 slots up, and merges the records; every row matches
+    the oracle, special rows included."""
     vocab, rows = 128256, 8
     rng = np.random.default_rng(80 + levels)
     ntl_np = _special_rows(rng, rows, vocab)

@@ -264,20 +264,19 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
 // with at most one key per lane it searches from 7 slots up.
 constexpr int kRankMergeMinK = 15;
 
-// Fewest slots for which a chunk's candidates may be merged into the wave's
+// Fewest slots for which a chunk's candidates are merged into the wave's
 // list in bulk (gathered, then placed by rank) rather than one key at a
-// time, and for which the end ranks the waves' lists on every wave of the
-// workgroup.  From 31 slots the list spans rows of 16 lanes and one
-// insertion costs two lane permutes and about 300 cycles.  Bulk merging
-// pays where chunks bring many keys: always at 63 slots, and at 31 on rows
-// short enough that a wave has at most kBulkMaxChunksPerWave chunks of them
-// (most of its chunks come while its bound is still low).  Same box, 31
-// slots: 520 rows of 32000, 27.4 -> 26.3 us; 256 rows of 128256, 31.0 ->
-// 32.5 us had it been used there.
-constexpr int kBulkMinK = 31;
-constexpr int kBulkAlwaysK = 63;
-constexpr uint32_t kBulkMaxChunksPerWave = 8;
+// time.  At 63 slots the list spans four rows of 16 lanes and a chunk still
+// brings several keys once the seed has set the bound; at 31 the seed
+// leaves so few that single insertions cost less (decode, 256 rows of
+// 128256: 28.3 us with bulk merging, 27.5 without).
+constexpr int kBulkMinK = 63;
+// Fewest slots for which the end ranks the waves' lists on every wave of the
+// workgroup, one key per thread, rather than on the last wave to arrive
+// (which took 6.5 us at 63 slots).
 constexpr int kParallelEndMinK = 31;
+// Fewest slots for which the first chunk's seed waits for every wave's
+// first chunk (a barrier) and ranks 4 maxima per lane instead of 1.
 constexpr int kSeedAllMinK = 31;
 // Gathered keys that a wave inserts one at a time rather than merging: a
 // merge costs about as much as three or four single insertions.
@@ -662,9 +661,6 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         }
     };
 
-    const bool use_bulk =
-        kBulk && (kK >= kBulkAlwaysK || nchunks <= kBulkMaxChunksPerWave * uint32_t(kWaves));
-
     // Large K: merges the n keys a wave has gathered in its s_cand slots (keys
     // above T, distinct, unsorted) into its sorted list.  A list key's new
     // position is its old one plus the gathered keys above it, counted with
@@ -732,7 +728,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                                                   __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
         const uint32_t lane_id = gid + a0 + ch * uint32_t(kChunkF4 * 4) + 4u * uint32_t(lane);
-        if (use_bulk) {
+        if constexpr (kBulk) {
             // gather the keys above T column by column into this wave's
             // s_cand slots (ballot and lane prefix), merging first whenever a
             // column would overflow the 64 slots

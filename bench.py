@@ -593,7 +593,7 @@ def main():
         result["shards"] = bench_shards(args, case, plan, info, copies, len(copies), torch, dev,
                                         stream, ws)
 
-    traffic = stored_traffic(case.name, info)
+    traffic = stored_traffic(case.name, info, algorithmic_bytes(info, case.vocab))
     if traffic is not None:
         result["roofline"]["traffic"] = traffic
 
@@ -609,7 +609,7 @@ def main():
         drec, dplan, dinfo, dbase, dlp, dids, _, dcopies = measure(
             R, torch, dev, stream, dcase, args, DEFAULT_STEPS[SUB_WORKLOAD], args.warmup,
             probe=not args.no_probe)
-        dtraffic = stored_traffic(dcase.name, dinfo)
+        dtraffic = stored_traffic(dcase.name, dinfo, algorithmic_bytes(dinfo, dcase.vocab))
         drec["traffic"] = dtraffic
         result["decode"] = drec
         if cpu is not None:
@@ -662,10 +662,11 @@ def shape_text(info):
             f"direct_rows={info['direct_rows']}")
 
 
-def stored_traffic(workload, info):
+def stored_traffic(workload, info, alg):
     """HBM bytes per launch of the row kernel from the committed counter
-    summary for this workload, if it was taken on the current kernel source
-    and the same kernel shape; else None."""
+    summary for this workload, if it was taken on the current kernel source,
+    the same kernel shape and the same algorithmic bytes (rows, width and
+    columns: another --levels moves other bytes); else None."""
     path = os.path.join(PROFILES, f"row_kernel_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -678,6 +679,8 @@ def stored_traffic(workload, info):
     if vals.get("kernel_source_sha256") != kernel_source_hash():
         return None
     if vals.get("shape") != shape_text(info):
+        return None
+    if vals.get("algorithmic_bytes_per_launch") != str(int(alg)):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])

@@ -874,11 +874,17 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         if (ch < nchunks) cm0 = lse_chunk(first);
         if constexpr (kSeedAll) {
             // per (float4 group, lane) the largest of the waves' group
-            // maxima: 256 distinct elements, each the largest of 4 * kWaves
+            // maxima over all the chunks they hold (kDepth each): 256
+            // distinct elements, each the largest of 4 * kWaves * kDepth
+            // (two deep, levels 6: ragged mix 30.9 -> 27.9 us, decode 36.5
+            // -> 34.4 us against the first chunk alone)
             uint32_t ux[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 ux[u] = ch < nchunks ? order_value(group_max(first[u])) : 0u;
+#pragma unroll
+                for (int dd = 1; dd < kDepth; ++dd)
+                    if (cb[dd] < nchunks) ux[u] = max(ux[u], order_value(group_max(xb[dd][u])));
                 __hip_atomic_fetch_max(&s_lmax[u * kWave + lane], ux[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             __syncthreads();

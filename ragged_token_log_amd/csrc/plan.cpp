@@ -67,8 +67,8 @@ static uint32_t few_rows_split(uint64_t read_rows, uint32_t vocab, uint32_t slot
     return static_cast<uint32_t>(s);
 }
 
-static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, uint32_t *waves,
-                           uint32_t *depth, uint32_t *split) {
+static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, bool direct,
+                           uint32_t *waves, uint32_t *depth, uint32_t *split) {
     // fewest segments that keep each within kMaxSegment (1 for any real vocabulary)
     uint32_t min_split = 1;
     while (segment_length(vocab, min_split) > kMaxSegment) ++min_split;
@@ -95,7 +95,14 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, u
         }
         *depth = 1;
         if (read_rows > kCUs || vocab <= kVeryShortRow) {
+            // Two deep, the seed sees twice the row.  Rows found through
+            // their descriptors then hold 74 VGPRs, and three workgroups of
+            // 8 waves fit a CU (520 rows of 32000 at levels 6: 27.9 against
+            // 29.2 us one deep); direct rows also hold the first chunk's
+            // copy, 90 VGPRs, and fit two, so past 512 rows workgroups wait
+            // (33.8 against 30.3 us one deep).
             *waves = 8;
+            if (!direct && vocab > kVeryShortRow) *depth = 2;
             return;
         }
         *waves = 16;
@@ -179,7 +186,7 @@ void shard_shape(const lp_plan &p, uint32_t shard_vocab, uint32_t *waves, uint32
         return;
     }
     uint32_t split = 1;   // a shard is one segment of each row
-    choose_variant(p.read_rows, shard_vocab, p.slots, waves, depth, &split);
+    choose_variant(p.read_rows, shard_vocab, p.slots, p.direct_rows != 0, waves, depth, &split);
 }
 
 lp_status build_descriptors(const lp_plan &p, const uint32_t *tokens,
@@ -297,7 +304,8 @@ lp_status lp_plan_ragged(uint32_t batch, uint32_t vocab, uint32_t levels,
         delete p;
         return LP_ERR_NOMEM;
     }
-    lp::choose_variant(p->read_rows, vocab, p->slots, &p->waves, &p->depth, &p->split);
+    lp::choose_variant(p->read_rows, vocab, p->slots, p->direct_rows != 0, &p->waves, &p->depth,
+                       &p->split);
     p->dynamic_chunks = lp::dynamic_chunks(*p);
     lp::size_workspace(*p);
 

@@ -216,6 +216,21 @@ def test_shape_by_ranked_slots(levels, rows, vocab, shape):
     assert (info["split"], info["waves"], info["depth"]) == shape
 
 
+@pytest.mark.parametrize("levels,rows,vocab,shape", [
+    (6, 520, 32000, (1, 8, 2)), (5, 300, 151936, (1, 8, 2)), (5, 600, 16000, (1, 8, 1)),
+    (6, 1024, 32000, (1, 4, 2)), (6, 200, 32000, (1, 16, 1))])
+def test_shape_by_ranked_slots_rows_through_descriptors(levels, rows, vocab, shape):
+    """Requests that read their last row only (no echo, full logits): above
+    one row per compute unit the rows are found through their descriptors,
+    the kernel holds no copy of its first chunk, and 8 waves go two deep."""
+    off = np.arange(0, 2 * rows + 1, 2, dtype=np.uint32)
+    plan = R.Plan(off, np.zeros(rows, bool), np.full(rows, (1 << levels) - 1), vocab, True,
+                  levels=levels)
+    info = plan.info()
+    assert info["direct_rows"] == 0 and info["read_rows"] == rows
+    assert (info["split"], info["waves"], info["depth"]) == shape
+
+
 def test_segments_stay_within_the_streamed_range():
     # one workgroup streams at most 2^28 elements of a row: a wider row is
     # always cut into segments, and a split leaving longer segments is refused

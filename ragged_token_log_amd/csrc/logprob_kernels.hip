@@ -275,12 +275,20 @@ constexpr int kBulkMinK = 63;
 // workgroup, one key per thread, rather than on the last wave to arrive
 // (which took 6.5 us at 63 slots).
 constexpr int kParallelEndMinK = 31;
-// Fewest slots for which the first chunk's seed waits for every wave's
-// first chunk (a barrier) and ranks 4 maxima per lane instead of 1.
+// Fewest slots for which the seed waits (a barrier) for the chunks every
+// wave holds at the start and ranks 4 maxima per lane instead of 1.
 constexpr int kSeedAllMinK = 31;
 // Gathered keys that a wave inserts one at a time rather than merging: a
 // merge costs about as much as three or four single insertions.
 constexpr uint32_t kBulkFewKeys = 3;
+// Keys a wave gathers before it merges them.  Once the seed has set the
+// bound a chunk brings a few keys, and a merge after every chunk cost more
+// than the keys an earlier rise of the bound would have stopped; merging
+// only when the 64 slots fill let the bound lag on long rows.  Same box at
+// 63 slots, merging after every chunk / at 16 keys / at 64: ragged mix
+// 27.9 / 25.9 / 25.2 us, decode 32.1 / 30.7 / 32.1 us, tie workload 596 /
+// 596 / 600 us.
+constexpr uint32_t kBulkMergeAt = 16;
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
@@ -599,6 +607,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     float m = -INFINITY, s = 0.0f;  // this lane's running max and sum of e^((x - m) / temperature)
     uint64_t list = 0;              // lane i < kK: the wave's (i+1)-th best key so far
     uint64_t T = 0;                 // wave-uniform bound (see above)
+    uint32_t pending = 0;           // large K: keys in this wave's s_cand slots, not yet merged
 
     // The full chunks are read through a buffer resource whose range ends at
     // the last of them: a load past the end returns zeros without touching
@@ -661,13 +670,32 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         }
     };
 
+    // A bound from every wave's (kPubJ+1)-th key: kPubM of them at or above x
+    // mean kPubM * (kPubJ + 1) >= kK real keys at or above x (the waves'
+    // shares are disjoint, and a published key only grows, so stale reads
+    // are weaker, never wrong).  Tighter than the largest K-th key of one
+    // wave; it pays only for large K.  Lane w < kWaves reads wave w's key,
+    // and a DPP minimum over those lanes gives the bound (8 LDS reads in a
+    // row cost about as much as one insertion).
+    auto publish_bound = [&]() __attribute__((always_inline)) {
+        if constexpr (kPubBound) {
+            static_assert(kPubM == kWaves, "every wave's key is needed");
+            const uint64_t mine = readlane_u64(list, kPubJ);
+            if (lane == 0) __hip_atomic_store(&s_pub[wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            uint64_t v = ~0ull;
+            if (lane < kWaves) v = lane == wave ? mine : lds_load_relaxed(&s_pub[lane]);
+            T = umax64(T, first_lanes_min_u64<kWaves>(v));
+        }
+    };
+
     // Large K: merges the n keys a wave has gathered in its s_cand slots (keys
     // above T, distinct, unsorted) into its sorted list.  A list key's new
     // position is its old one plus the gathered keys above it, counted with
     // broadcast reads; a gathered key's is the gathered keys above it plus
     // the list keys above it, found by binary search.  The keys are distinct,
     // so the positions are too; the first kK are kept, and T rises to the
-    // need-th.  About one insertion's cost, whatever n (<= 64).
+    // need-th, then the published bound is refreshed.  About one insertion's
+    // cost, whatever n (<= 64).
     auto bulk_merge = [&](uint32_t n) __attribute__((always_inline)) {
         uint64_t *cand = s_cand + wave * kWave;
         uint64_t *sl = s_keys + wave * kK;   // this wave's slots, free until the end
@@ -698,6 +726,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         lds_acquire();
         list = lane < kK ? nl[lane] : 0ull;
         T = umax64(T, readlane_u64(list, int(need) - 1));
+        publish_bound();
     };
 
     // The filter value for chunk ch against the bound as it stands.
@@ -731,9 +760,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         if constexpr (kBulk) {
             // gather the keys above T column by column into this wave's
             // s_cand slots (ballot and lane prefix), merging first whenever a
-            // column would overflow the 64 slots
+            // column would overflow the 64 slots; the slots are merged once
+            // they hold kBulkMergeAt keys and after the wave's last chunk,
+            // not after every chunk
             uint64_t *cand = s_cand + wave * kWave;
-            uint32_t n = 0;
             while (cols != 0) {
                 const uint32_t j = uint32_t(__builtin_ctz(cols));
                 cols &= cols - 1;
@@ -742,28 +772,18 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                 const uint64_t key = order_key(v, lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u));
                 uint64_t mask = __ballot(pass && key > T);
                 if (mask == 0) continue;
-                if (n + uint32_t(__popcll(mask)) > uint32_t(kWave)) {
-                    bulk_merge(n);
-                    n = 0;
+                if (pending + uint32_t(__popcll(mask)) > uint32_t(kWave)) {
+                    bulk_merge(pending);
+                    pending = 0;
                     mask = __ballot(pass && key > T);
                     if (mask == 0) continue;
                 }
-                if (pass && key > T) cand[n + lanes_below(mask)] = key;
-                n += uint32_t(__popcll(mask));
+                if (pass && key > T) cand[pending + lanes_below(mask)] = key;
+                pending += uint32_t(__popcll(mask));
             }
-            if (n > kBulkFewKeys) {
-                bulk_merge(n);
-            } else if (n != 0) {
-                // few keys (long rows once the list is full): one at a time
-                lds_release();
-                lds_acquire();
-                for (uint32_t k = 0; k < n; ++k) {
-                    const uint64_t key = uniform64(cand[k]);
-                    if (key > T) {
-                        list = list_insert<kK>(list, key, lane);
-                        T = umax64(T, readlane_u64(list, int(need) - 1));
-                    }
-                }
+            if (pending >= kBulkMergeAt) {
+                bulk_merge(pending);
+                pending = 0;
             }
         } else {
             while (cols != 0) {
@@ -771,22 +791,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                 cols &= cols - 1;
                 column(xv[j], lane_id + 4u * uint32_t(kWave) * (j >> 2) + (j & 3u), tv);
             }
-        }
-        if constexpr (kPubBound) {
-            // A bound from every wave's (kPubJ+1)-th key: kPubM of them at or
-            // above x mean kPubM * (kPubJ + 1) >= kK real keys at or above x
-            // (the waves' shares are disjoint, and a published key only
-            // grows, so stale reads are weaker, never wrong).  Tighter than
-            // the largest K-th key of one wave; it pays only for large K.
-            // lane w < kWaves reads wave w's key, and a DPP minimum over
-            // those lanes gives the bound (8 LDS reads in a row cost about
-            // as much as one insertion)
-            static_assert(kPubM == kWaves, "every wave's key is needed");
-            const uint64_t mine = readlane_u64(list, kPubJ);
-            if (lane == 0) __hip_atomic_store(&s_pub[wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            uint64_t v = ~0ull;
-            if (lane < kWaves) v = lane == wave ? mine : lds_load_relaxed(&s_pub[lane]);
-            T = umax64(T, first_lanes_min_u64<kWaves>(v));
+            publish_bound();
         }
         if (T != T0 && lane == 0) __hip_atomic_fetch_max(&s_T, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
@@ -949,6 +954,23 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
                     topk_chunk(xb[dd % kDepth], cb[dd % kDepth], cm);
                 }
                 refill_next(xb[dd % kDepth], cb[dd % kDepth]);
+            }
+        }
+    }
+    if constexpr (kBulk) {
+        // the keys still pending: merged, or a few inserted one at a time
+        if (pending > kBulkFewKeys) {
+            bulk_merge(pending);
+        } else if (pending != 0) {
+            lds_release();
+            lds_acquire();
+            const uint64_t *cand = s_cand + wave * kWave;
+            for (uint32_t k = 0; k < pending; ++k) {
+                const uint64_t key = uniform64(cand[k]);
+                if (key > T) {
+                    list = list_insert<kK>(list, key, lane);
+                    T = umax64(T, readlane_u64(list, int(need) - 1));
+                }
             }
         }
     }

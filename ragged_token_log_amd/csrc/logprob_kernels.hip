@@ -153,13 +153,6 @@ __device__ __forceinline__ uint64_t lds_load_relaxed(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Lane 0 adds 1 to an LDS counter; every lane gets the previous value.
-__device__ __forceinline__ uint32_t lds_arrive(uint32_t *counter, int lane) {
-    uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return readlane_u32(prev, 0);
-}
-
 // Logits are read exactly once: nontemporal 16-byte loads (the `nt` form of
 // buffer_load_dwordx4) stream them without displacing reusable cache lines;
 // on gfx950 they sustain ~13% more HBM bandwidth than plain loads here.
@@ -259,11 +252,6 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t (&e)[kPer], int lane, u
     return mine;
 }
 
-// Fewest slots for which the end of the row kernel ranks the waves' sorted
-// lists by binary search when they hold more keys than a wave has lanes;
-// with at most one key per lane it searches from 7 slots up.
-constexpr int kRankMergeMinK = 15;
-
 // Fewest slots for which a chunk's candidates are merged into the wave's
 // list in bulk (gathered, then placed by rank) rather than one key at a
 // time.  At 63 slots the list spans four rows of 16 lanes and a chunk still
@@ -271,10 +259,6 @@ constexpr int kRankMergeMinK = 15;
 // leaves so few that single insertions cost less (decode, 256 rows of
 // 128256: 28.3 us with bulk merging, 27.5 without).
 constexpr int kBulkMinK = 63;
-// Fewest slots for which the end ranks the waves' lists on every wave of the
-// workgroup, one key per thread, rather than on the last wave to arrive
-// (which took 6.5 us at 63 slots).
-constexpr int kParallelEndMinK = 31;
 // Fewest slots for which the seed waits (a barrier) for the chunks every
 // wave holds at the start and ranks 4 maxima per lane instead of 1.
 constexpr int kSeedAllMinK = 31;
@@ -549,10 +533,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ uint64_t s_T;
     __shared__ uint64_t s_pub[kWaves];
     __shared__ float s_m[kWaves], s_s[kWaves];
-    __shared__ uint32_t s_done;
     __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
     constexpr bool kBulk = kK >= kBulkMinK;
-    constexpr bool kParallelEnd = kK >= kParallelEndMinK;
     __shared__ uint64_t s_cand[kBulk ? kWaves * kWave : 1];   // per wave: a chunk's candidates
     __shared__ uint64_t s_new[kBulk ? kWaves * kK : 1];       // per wave: the merged list
 
@@ -825,7 +807,6 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     if (tid < kWaves) s_pub[tid] = 0;
     if (tid == 0) {
         s_T = 0;
-        s_done = 0;
         s_next = uint32_t(kDepth * kWaves);
     }
     __syncthreads();
@@ -837,11 +818,9 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         // rows of 128256: 25.4 -> 25.0 us).  Rows found through their
         // descriptors refill after the chunk, as in the loop (the early
         // refill cost 1.3-1.5 us on 520 rows of 32000, one chunk deep).
-        // The wave publishes its lanes' chunk maxima and seeds T from, per
-        // lane position, the max over the maxima the waves have published so
-        // far (its own at least); ones not yet written read -inf.  These are
-        // distinct elements of the row, so the need-th largest of the 64
-        // values bounds it.
+        // The seed: distinct elements of the row bound it (the need-th
+        // largest of any of them is at most the row's need-th), here the
+        // per-position maxima of the waves' first chunks (see below).
         constexpr uint32_t kAhead = uint32_t(kDepth * kWaves);
         // With kDyn each wave takes its next chunk index from an LDS counter
         // one step ahead of the refill that needs it, so the atomic's
@@ -975,9 +954,16 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         }
     }
 
-    // per wave: its list and (m, s) across lanes into LDS; the last wave of
-    // the workgroup to get here merges them and writes the row (or the
-    // segment's record)
+    // per wave: its list and (m, s) across lanes into LDS; then every wave
+    // ranks its share of the waves' kN (<= threads) keys, one per thread: a
+    // key's rank is the number of keys above it in all the lists together
+    // (in its own list, its position; the keys are distinct), each list
+    // binary-searched in log2(kK + 1) probes, and the best kK go to their
+    // rank.  Wave 0 then writes the row (or the segment's record).  The
+    // last wave to arrive used to rank them all alone: kPer rounds of
+    // searches (6.5 us at 63 slots), or at 7 slots counting or kK wave-wide
+    // maxima; with every wave ranking, decode at 7 slots went 24.5 -> 23.7
+    // us and the 4-row batch (16 waves) 9.0 -> 8.5 us, same box.
     if (lane < kK) s_keys[wave * kK + lane] = list;
     wave_lse(m, s, c);
     if (lane == 0) {
@@ -985,86 +971,21 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         s_s[wave] = s;
     }
     constexpr int kN = kWaves * kK;
-    constexpr int kPer = (kN + kWave - 1) / kWave;
-    uint64_t top;
-    if constexpr (kParallelEnd) {
-        // Large K: every wave ranks its share of the waves' kN (< threads)
-        // keys, one per thread, each a binary search in every list; wave 0
-        // then writes the row.  Ranking on one wave took kPer rounds of
-        // log2(kK + 1) dependent probes (6.5 us at 63 slots).
-        if (wave == 0 && lane < kK) s_top[lane] = 0ull;
-        __syncthreads();
-        if (tid < kN) {
-            const uint64_t key = s_keys[tid];
-            if (key != 0) {
-                uint32_t rank = 0;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
-                if (rank < uint32_t(kK)) s_top[rank] = key;
-            }
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        top = lane < kK ? s_top[lane] : 0ull;
-    } else {
-        lds_release();
-        if (lds_arrive(&s_done, lane) != uint32_t(kWaves - 1)) return;
-        lds_acquire();
-
-        // The waves' lists are sorted: from 7 slots up (with one key per lane,
-        // or from 15 with more) a binary search ranks each key in fewer LDS
-        // round trips than counting; below, counting; 7 slots over more keys
-        // than lanes take kK wave-wide rounds.
-        constexpr bool kSearch = kK >= kRankMergeMinK || (kK >= 7 && kPer == 1);
-        if constexpr (kSearch) {
-            // a key's rank is the number of keys above it in all the lists
-            // together (in its own list, its position, the keys being distinct),
-            // each list binary-searched in log2(kK + 1) probes; the best kK go
-            // to their rank
-            if (lane < kK) s_top[lane] = 0ull;
-            lds_release();
-#pragma unroll 1
-            for (int i = 0; i < kPer; ++i) {
-                const int idx = lane + kWave * i;
-                const uint64_t key = idx < kN ? s_keys[idx] : 0ull;
-                if (key != 0) {
-                    uint32_t rank = 0;
-#pragma unroll
-                    for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
-                    if (rank < uint32_t(kK)) s_top[rank] = key;
-                }
-            }
-            lds_release();
-            lds_acquire();
-            top = lane < kK ? s_top[lane] : 0ull;
-        } else if constexpr (kPer == 1) {
-            // at most one key per lane: each key's rank is the number of keys
-            // above it (the keys are distinct but for empty slots, 0), counted
-            // with broadcast reads and independent compares rather than kK
-            // rounds of wave-wide maxima; the best kK go to their rank
-            // (lanes exchange values through s_top: the fences keep the
-            // compiler from forwarding a lane's own store to its read-back)
-            if (lane < kK) s_top[lane] = 0ull;
-            const uint64_t mine = lane < kN ? s_keys[lane] : 0ull;
+    static_assert(kN <= kThreads, "one key per thread");
+    if (wave == 0 && lane < kK) s_top[lane] = 0ull;
+    __syncthreads();
+    if (tid < kN) {
+        const uint64_t key = s_keys[tid];
+        if (key != 0) {
             uint32_t rank = 0;
-#pragma unroll 8
-            for (int j = 0; j < kN; ++j) rank += s_keys[j] > mine ? 1u : 0u;   // s_keys[j]: a broadcast read
-            lds_release();
-            if (mine != 0 && rank < uint32_t(kK)) s_top[rank] = mine;
-            lds_release();
-            lds_acquire();
-            top = lane < kK ? s_top[lane] : 0ull;
-        } else {
-            uint64_t e[kPer];
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const uint32_t idx = uint32_t(lane + kWave * i);
-                e[i] = idx < uint32_t(kN) ? s_keys[idx] : 0ull;
-            }
-            uint32_t found;
-            top = wave_select<kK, kPer>(e, lane, &found);
+            for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
+            if (rank < uint32_t(kK)) s_top[rank] = key;
         }
     }
+    __syncthreads();
+    if (wave != 0) return;
+    const uint64_t top = lane < kK ? s_top[lane] : 0ull;
     float M = -INFINITY, S = 0.0f;
     if (lane < kWaves) {
         M = s_m[lane];

@@ -36,12 +36,12 @@ constexpr uint64_t kManyRows = 1024;
 constexpr uint64_t kCUs = 256;
 constexpr uint64_t kSplitBelow = 129;   // at most 128 rows: segments (two per row or more)
 constexpr uint64_t kLargeKMaxSplit = 4;        // 31+ slots: segments per row at most
-constexpr uint32_t kLargeKMinSegment = 8000;   // 31+ slots: shortest segment of a short row
 constexpr uint32_t kVeryShortRow = 20480;
 constexpr uint32_t kShortRow = 65536;
 constexpr uint32_t kMinSegment = 32768;
 constexpr uint32_t kMinLongSegment = 16000;   // rows longer than kShortRow
 constexpr uint32_t kMaxLongSplit = 8;
+constexpr uint32_t kMinWideSegment = 24576;   // up to 7 slots: 16 waves from this long
 
 // Segments per row for a batch too small to fill the chip: as many as keep
 // the workgroups within one per compute unit (floor, not ceil: a few compute
@@ -82,13 +82,11 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, b
         // of the fastest shape).  257-1023 rows: 8 waves one deep (520 rows
         // of 32000: 24.8 against 31.4 us two deep).  129-256: 16 waves one
         // deep (256 rows of 128256 at levels 6: 32.2 against 36.8 us for 8
-        // two deep).  At most 128: 16 waves one deep, up to 4 segments a row
-        // (16 rows of 151936 at levels 6: 23.3 against 37.3 us whole; 8
-        // segments lose to 4 from 63 slots and win by at most 2 % at 31);
-        // rows of at most kShortRow are cut only up to 64 rows, in segments
-        // of at least kLargeKMinSegment over 8 waves (16 rows of 32000: 13.1
-        // against 14.0 us whole).  The seed waits for every wave, so more
-        // waves give it more data, and the merge of 4 records stays short.
+        // two deep).  At most 128 long rows: 16 waves one deep, up to 4
+        // segments a row (16 rows of 151936 at levels 6: 23.3 against 37.3
+        // us whole; 8 segments lose to 4 from 63 slots and win by at most 2
+        // % at 31).  The seed waits for every wave, so more waves give it
+        // more data, and the merge of 4 records stays short.
         if (many) {
             *waves = 4;
             return;
@@ -105,15 +103,19 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, b
             if (!direct && vocab > kVeryShortRow) *depth = 2;
             return;
         }
+        if (vocab <= kShortRow) {
+            // short rows: 8 waves two deep, whole rows (the seed sees two
+            // chunks a wave; 4-64 rows of 32000: 12.6-13.6 against
+            // 12.8-13.9 us in 4 segments at levels 5, 15.4-16.0 against
+            // 15.7-16.9 at levels 6)
+            *waves = 8;
+            *depth = 2;
+            return;
+        }
         *waves = 16;
         if (read_rows >= kSplitBelow) return;
         uint64_t s = kCUs / read_rows;
         if (s > kLargeKMaxSplit) s = kLargeKMaxSplit;
-        if (vocab <= kShortRow) {
-            const uint64_t by_vocab = vocab / kLargeKMinSegment;
-            s = s < kLargeKMaxSplit ? 1 : (by_vocab < s ? by_vocab : s);
-            if (s > 1) *waves = 8;
-        }
         if (s > max_split_for_slots(slots)) s = max_split_for_slots(slots);
         if (s < 1) s = 1;
         *split = s < min_split ? min_split : static_cast<uint32_t>(s);
@@ -147,25 +149,27 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, b
         *depth = 1;
         return;
     }
+    // One chunk deep from here.  Since every wave ranks at the end (the
+    // last wave no longer ranks the workgroup's keys alone), 16 waves gain
+    // where 8 two deep used to win.
+    *depth = 1;
     if (read_rows >= kSplitBelow) {
-        // one row per compute unit at most (129-256 rows): 16 waves one chunk
-        // deep on short rows (3-10 % ahead of two deep), 8 waves two deep on
-        // long ones (1-4 %); two segments a row would leave more workgroups
-        // than compute units (25 against 20 us at 144 rows of 128256)
-        *waves = vocab <= kShortRow ? 16 : 8;
-        *depth = vocab <= kShortRow ? 1 : 2;
+        // one row per compute unit at most (129-256 rows): 16 waves (decode,
+        // 256 rows of 128256: 23.4 against 23.8 us for 8 waves two deep at
+        // levels 3, 24.8 against 26.1 at levels 4); two segments a row would
+        // leave more workgroups than compute units (25 against 20 us at 144
+        // rows of 128256)
+        *waves = 16;
         return;
     }
-    // fewer rows still (at most 128): segments, 16 waves one chunk deep (7-40
-    // % ahead of whole rows at 32-96 rows of 151936 or 256000); two segments
-    // a row from 112 rows up take 8 waves two deep (3-8 % ahead of 16 waves
-    // and of whole rows at 112 and 128 rows of 128256 to 256000), and so do
-    // three or more segments at 15 slots (8 rows of 128256 in 8 segments:
-    // 13.3 against 15.9 us; 16.1 against 17.1 us at 40 rows in 4)
+    // fewer rows still (at most 128): segments (7-40 % ahead of whole rows at
+    // 32-96 rows of 151936 or 256000) over 16 waves (at levels 4, 4-64 rows
+    // of 128256 and 256000: 5-17 % ahead of 8 waves two deep), or over 8
+    // waves at up to 7 slots when a segment is shorter than
+    // kMinWideSegment (4 and 16 rows of 128256 in 8 segments of 16032:
+    // 10.3 and 11.0 against 10.9 and 11.3 us)
     *split = few_rows_split(read_rows, vocab, slots, min_split);
-    const bool pairs = (*split == 2 && read_rows >= 112) || (*split > 2 && slots >= 15);
-    *waves = pairs ? 8 : 16;
-    *depth = pairs ? 2 : 1;
+    *waves = (slots <= 7 && segment_length(vocab, *split) < kMinWideSegment) ? 8 : 16;
 }
 
 // Chunks handed to whichever wave of a workgroup frees a buffer first

@@ -173,17 +173,18 @@ def test_many_rows_shape_by_row_length(vocab, waves, depth):
 
 @pytest.mark.parametrize("rows,vocab,shape", [
     (4, 32000, (1, 16, 1)), (32, 32000, (1, 16, 1)), (200, 32000, (1, 16, 1)),
-    (32, 8192, (1, 8, 1)), (200, 16000, (1, 8, 1)), (32, 24000, (1, 16, 1)),
-    (32, 128256, (8, 16, 1)), (32, 151936, (8, 16, 1)), (64, 151936, (4, 16, 1)),
-    (32, 256000, (8, 16, 1)), (8, 65536, (2, 16, 1)), (8, 65537, (4, 16, 1)),
-    (40, 128256, (6, 16, 1)), (8, 1 << 20, (32, 16, 1)), (8, 256000, (8, 16, 1)), (4, 294912, (9, 16, 1)), (96, 256000, (2, 16, 1)), (111, 151936, (2, 16, 1)),
-    (112, 151936, (2, 8, 2)), (127, 256000, (2, 8, 2)), (128, 128256, (2, 8, 2)),
-    (129, 128256, (1, 8, 2)), (128, 32000, (1, 16, 1)), (256, 128256, (1, 8, 2)), (256, 32000, (1, 16, 1)),
+    (32, 8192, (1, 8, 1)), (200, 16000, (1, 8, 1)), (32, 24000, (1, 8, 1)), (32, 24576, (1, 16, 1)),
+    (32, 128256, (8, 8, 1)), (32, 151936, (8, 8, 1)), (64, 151936, (4, 16, 1)),
+    (32, 256000, (8, 16, 1)), (8, 65536, (2, 16, 1)), (8, 65537, (4, 8, 1)),
+    (40, 128256, (6, 8, 1)), (8, 1 << 20, (32, 16, 1)), (8, 256000, (8, 16, 1)), (4, 294912, (9, 16, 1)), (96, 256000, (2, 16, 1)), (111, 151936, (2, 16, 1)),
+    (112, 151936, (2, 16, 1)), (127, 256000, (2, 16, 1)), (128, 128256, (2, 16, 1)),
+    (129, 128256, (1, 16, 1)), (128, 32000, (1, 16, 1)), (256, 128256, (1, 16, 1)), (256, 32000, (1, 16, 1)),
     (257, 128256, (1, 8, 1)), (600, 151936, (1, 8, 1))])
 def test_few_rows_shape(rows, vocab, shape):
     """Plans of at most 1023 read rows: (split, waves, depth) from the row
     count and the row length; long rows of small batches are cut into at
-    most one workgroup per compute unit."""
+    most one workgroup per compute unit, over 8 waves at 7 slots when a
+    segment holds fewer than 24576 entries, else 16."""
     plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool), np.full(rows, 7),
                   vocab, False)
     info = plan.info()
@@ -194,22 +195,21 @@ def test_few_rows_shape(rows, vocab, shape):
 @pytest.mark.parametrize("levels,rows,vocab,shape", [
     (5, 2048, 32000, (1, 4, 2)), (6, 2048, 128256, (1, 4, 2)), (5, 1024, 256000, (1, 4, 2)),
     (5, 512, 128256, (1, 8, 1)), (6, 520, 32000, (1, 8, 1)), (6, 300, 16000, (1, 8, 1)),
-    (6, 200, 16000, (1, 8, 1)), (5, 256, 128256, (1, 16, 1)), (6, 129, 32000, (1, 16, 1)),
+    (6, 200, 16000, (1, 8, 1)), (5, 256, 128256, (1, 16, 1)), (6, 129, 32000, (1, 8, 2)),
     (6, 32, 256000, (4, 16, 1)), (6, 96, 151936, (2, 16, 1)), (6, 16, 151936, (4, 16, 1)),
     (5, 32, 256000, (4, 16, 1)), (5, 64, 151936, (4, 16, 1)), (5, 32, 128256, (4, 16, 1)),
     (5, 96, 70001, (2, 16, 1)), (5, 80, 128256, (3, 16, 1)), (5, 128, 256000, (2, 16, 1)),
-    (5, 32, 65536, (4, 8, 1)), (6, 16, 32000, (4, 8, 1)), (6, 64, 32000, (4, 8, 1)),
-    (6, 64, 24000, (3, 8, 1)), (6, 65, 32000, (1, 16, 1)), (5, 128, 32000, (1, 16, 1)),
+    (5, 32, 65536, (1, 8, 2)), (6, 16, 32000, (1, 8, 2)), (6, 64, 32000, (1, 8, 2)),
+    (6, 64, 24000, (1, 8, 2)), (6, 65, 32000, (1, 8, 2)), (5, 128, 32000, (1, 8, 2)),
     (6, 8, 1 << 29, (4, 16, 1)), (6, 200, 1 << 29, (2, 16, 1)),
-    (4, 32, 151936, (8, 8, 2)), (4, 80, 128256, (3, 8, 2)),
+    (4, 32, 151936, (8, 16, 1)), (4, 80, 128256, (3, 16, 1)),
     (4, 96, 128256, (2, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
 def test_shape_by_ranked_slots(levels, rows, vocab, shape):
     """With 31 or more ranked slots: 4 waves two deep for many rows, 8 one
-    deep above one row per compute unit, 16 one deep below, with up to 4
-    segments a row at most 128 rows (short rows only up to 64 rows, then
-    over 8 waves); 15 slots keep the segments of 7 but take 8 waves two deep
-    from three segments a row.  A row beyond the streamed range is always
-    cut."""
+    deep above one row per compute unit, rows of at most 65536 entries over 8
+    waves two deep below, long rows over 16 waves one deep with up to 4
+    segments a row at most 128 rows; 15 slots keep the segments of 7 over 16
+    waves.  A row beyond the streamed range is always cut."""
     plan = R.Plan(np.arange(rows + 1, dtype=np.uint32), np.zeros(rows, bool),
                   np.full(rows, (1 << levels) - 1), vocab, False, levels=levels)
     info = plan.info()
@@ -218,7 +218,7 @@ def test_shape_by_ranked_slots(levels, rows, vocab, shape):
 
 @pytest.mark.parametrize("levels,rows,vocab,shape", [
     (6, 520, 32000, (1, 8, 2)), (5, 300, 151936, (1, 8, 2)), (5, 600, 16000, (1, 8, 1)),
-    (6, 1024, 32000, (1, 4, 2)), (6, 200, 32000, (1, 16, 1))])
+    (6, 1024, 32000, (1, 4, 2)), (6, 200, 32000, (1, 8, 2)), (6, 200, 128256, (1, 16, 1))])
 def test_shape_by_ranked_slots_rows_through_descriptors(levels, rows, vocab, shape):
     """Requests that read their last row only (no echo, full logits): above
     one row per compute unit the rows are found through their descriptors,

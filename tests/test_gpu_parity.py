@@ -762,9 +762,9 @@ def test_outputs_stay_in_bounds_and_plan_is_reusable(R):
     plan.close()
 
 
-def test_default_split_pairs(R):
+def test_default_split_in_two(R):
     """120 next-token rows of 70001 entries (segments hold at least 32768):
-    the default plan cuts each row in two (8 waves, two chunks deep) and
+    the default plan cuts each row in two (16 waves, one chunk deep) and
     merges the records; every row matches the oracle, special rows
     included."""
     vocab, rows = 70001, 120
@@ -778,19 +778,19 @@ def test_default_split_pairs(R):
     plan = R.Plan(off, echo, top_n, vocab, False)
     info = plan.info()
     plan.close()
-    assert (info["split"], info["waves"], info["depth"]) == (2, 8, 2)
+    assert (info["split"], info["waves"], info["depth"]) == (2, 16, 1)
     got = run_library(R, torch, off, None, _dev(ntl_np), tokens, sampled, top_n, echo)
     ref = oracle(off, None, ntl_np, tokens, sampled, top_n, echo)
-    assert_parity(*got, ref, "default split pairs")
+    assert_parity(*got, ref, "default split in two")
 
 
-@pytest.mark.parametrize("levels,shape", [(3, (8, 16, 1)), (4, (8, 8, 2)), (5, (4, 16, 1)),
+@pytest.mark.parametrize("levels,shape", [(3, (8, 8, 1)), (4, (8, 16, 1)), (5, (4, 16, 1)),
                                           (6, (4, 16, 1))])
 def test_default_segments_of_long_rows(R, levels, shape):
     """8 next-token rows of 128256 entries: the default plan cuts each row
-    into 8 segments of at least 16000 entries (8 waves two deep at 15 ranked
-    slots), or 4 from 31 slots up, and merges the records; every row matches
-    the oracle, special rows included."""
+    into 8 segments of at least 16000 entries (over 8 waves at 7 ranked
+    slots, 16 at 15), or 4 from 31 slots up, and merges the records; every
+    row matches the oracle, special rows included."""
     vocab, rows = 128256, 8
     rng = np.random.default_rng(80 + levels)
     ntl_np = _special_rows(rng, rows, vocab)

@@ -138,3 +138,38 @@ def check_all_rows_properties(torch, src, desc, lp_dev, ids_dev, vocab, chunk=25
         assert bool((ids64[r0:r1, 7][live] == ch[live]).all())
         assert bool(pad[r0:r1][~live].all())
         del x
+
+
+def special_rows(rng, n, vocab):
+    """Rows covering the degenerate cases: all-equal, +-0.0, -inf heavy, all
+    -inf, one finite entry, a boosted token, heavy ties."""
+    rows = []
+    kinds = ["normal", "equal", "zeros", "ninf_heavy", "all_ninf", "one_finite", "boost",
+             "ties", "ninf_prefix"]
+    for i in range(n):
+        k = kinds[i % len(kinds)]
+        if k == "normal":
+            x = rng.standard_normal(vocab).astype(np.float32) * 2
+        elif k == "equal":
+            x = np.full(vocab, -0.5, np.float32)
+        elif k == "zeros":
+            x = np.where(rng.random(vocab) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+            x[rng.random(vocab) < 0.2] = -1.0
+        elif k == "ninf_heavy":
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[rng.random(vocab) < 0.9] = -np.inf
+        elif k == "all_ninf":
+            x = np.full(vocab, -np.inf, np.float32)
+        elif k == "one_finite":
+            x = np.full(vocab, -np.inf, np.float32)
+            x[rng.integers(vocab)] = 3.0
+        elif k == "boost":
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[rng.integers(vocab)] += 30.0
+        elif k == "ties":
+            x = (rng.integers(-3, 4, vocab) * 0.5).astype(np.float32)
+        else:  # a long -inf run at the start, then values
+            x = rng.standard_normal(vocab).astype(np.float32)
+            x[: vocab * 3 // 4] = -np.inf
+        rows.append(x)
+    return np.stack(rows)

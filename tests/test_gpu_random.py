@@ -1,0 +1,86 @@
+"""Seeded random plans against the oracle (needs an MI355X).
+
+Each case draws a batch of requests (row counts, echo flags, top_n up to the
+heap depth's cap), a row width from tiny to past 128K entries, rows of the
+degenerate kinds the parity suite uses (ties, all -inf, +-0.0, a boosted
+token), and, for some cases, a forced kernel shape (waves, depth, segments)
+or the deterministic chunk order.  Ids and offsets must match the oracle bit
+for bit and logprobs within 1e-5.  The draws cover the paths a fixed grid can
+miss: large-K bulk merges with keys still pending at a wave's end, seeds over
+two chunks, segments of a few elements, rows shorter than one chunk.
+"""
+import numpy as np
+import pytest
+
+import oracle.logprob_oracle as LO
+from tests.gpu_helpers import assert_parity, log, oracle, run_library, special_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+N_CASES = 96
+
+
+@pytest.fixture(scope="module")
+def R():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_token_log_amd as lib
+    lib.load()
+    return lib
+
+
+def _draw_case(i):
+    rng = np.random.default_rng(9000 + i)
+    levels = int(rng.integers(0, 7))
+    cap = LO.max_top_n(levels)
+    kind = i % 4
+    if kind == 0:
+        vocab = int(rng.integers(1, 300))
+    elif kind == 1:
+        vocab = int(rng.integers(900, 9000))
+    elif kind == 2:
+        vocab = int(rng.integers(20000, 70000))
+    else:
+        vocab = int(rng.choice([128256, 131073, 151936]))
+    batch = int(rng.integers(1, 7))
+    lengths = rng.integers(1, 6 if vocab < 100000 else 3, batch)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    echo = rng.random(batch) < 0.5
+    top_n = rng.integers(0, cap + 1, batch) if cap > 0 else np.zeros(batch, int)
+    if cap > 0 and rng.random() < 0.7:
+        top_n[int(rng.integers(batch))] = cap
+    logits = special_rows(rng, int(off[-1]), vocab)
+    ntl = logits[off[1:].astype(np.int64) - 1]
+    tokens = rng.integers(0, vocab, int(off[-1])).astype(np.uint32)
+    sampled = rng.integers(0, vocab, batch).astype(np.uint32)
+    split = waves = depth = None
+    if rng.random() < 0.5:
+        waves = int(rng.choice([4, 8, 16]))
+        depth = int(rng.integers(1, 3))
+        most = min(64, 1024 // max(cap, 1))
+        split = int(rng.choice([s for s in (1, 2, 3, 4, 7) if s <= most]))
+    deterministic = bool(rng.random() < 0.25)
+    has_logits = bool(rng.random() < 0.6)
+    return dict(levels=levels, vocab=vocab, off=off, echo=echo, top_n=top_n, logits=logits,
+                ntl=ntl, tokens=tokens, sampled=sampled, split=split, waves=waves, depth=depth,
+                deterministic=deterministic, has_logits=has_logits)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_plan(R, i):
+    c = _draw_case(i)
+    echo = c["echo"] if c["has_logits"] else np.zeros_like(c["echo"])
+    log(f"random case {i}: levels={c['levels']} vocab={c['vocab']} rows={int(c['off'][-1])} "
+        f"logits={c['has_logits']} shape={(c['waves'], c['depth'], c['split'])} "
+        f"deterministic={c['deterministic']}")
+    logits = c["logits"] if c["has_logits"] else None
+    ref = oracle(c["off"], logits, c["ntl"], c["tokens"], c["sampled"], c["top_n"], echo,
+                 levels=c["levels"])
+    dl = torch.from_numpy(c["logits"]).cuda() if c["has_logits"] else None
+    dn = torch.from_numpy(np.ascontiguousarray(c["ntl"])).cuda()
+    got = run_library(R, torch, c["off"], dl, dn, c["tokens"], c["sampled"], c["top_n"], echo,
+                      c["split"], c["waves"], c["depth"], levels=c["levels"],
+                      deterministic=c["deterministic"])
+    assert_parity(*got, ref, f"random case {i}")

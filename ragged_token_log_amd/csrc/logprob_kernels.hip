@@ -24,13 +24,15 @@
 //    ties go to the lowest id and every merge uses one total order.
 //  * Each wave keeps its K best keys sorted across lanes 0..K-1 and filters
 //    its chunks against a bound T (its own K-th key, a workgroup maximum of
-//    such keys in LDS, and a seed from the first chunks' lane maxima).  A
-//    chunk whose lane maxima stay below T costs one compare; the few columns
-//    that beat it enter their keys one at a time.
-//  * The waves' lists and (m, s) pairs meet in LDS; the last wave to finish
-//    selects the K best and writes lp = (x - M) / T - ln S for them and for
-//    the chosen token, or, for segments and shards, a record of (M, S, K
-//    keys, chosen logit) that a second kernel (one wave per row) merges.
+//    such keys in LDS, and a seed from the first chunks' maxima; from 31
+//    slots also the waves' published keys).  A chunk whose lane maxima stay
+//    below T costs one compare; the few columns that beat it enter their
+//    keys one at a time, or at 63 slots are gathered and merged in bulk.
+//  * The waves' lists and (m, s) pairs meet in LDS; every wave ranks its
+//    share of the keys, and wave 0 writes lp = (x - M) / T - ln S for the K
+//    best and for the chosen token, or, for segments and shards, a record of
+//    (M, S, K keys, chosen logit) that a second kernel (one wave per row)
+//    merges.
 //
 // No MFMA: there is no contraction here.
 #include <hip/hip_runtime.h>
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
     constexpr bool kBulk = kK >= kBulkMinK;
-    __shared__ uint64_t s_cand[kBulk ? kWaves * kWave : 1];   // per wave: a chunk's candidates
+    __shared__ uint64_t s_cand[kBulk ? kWaves * kWave : 1];   // per wave: gathered keys not yet merged
     __shared__ uint64_t s_new[kBulk ? kWaves * kK : 1];       // per wave: the merged list
 
     const int tid = int(threadIdx.x);

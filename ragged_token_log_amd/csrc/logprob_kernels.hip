@@ -212,20 +212,6 @@ __device__ __forceinline__ void wave_lse(float &m, float &s, float c) {
     s = S;
 }
 
-// The (m, s) pairs of lanes 0..kN-1 merged (kN = 4, 8 or 16; other lanes are
-// ignored): DPP steps within the first 4, 8 or 16 lanes, after which lane 0
-// holds the result; fewer steps than a whole-wave reduction.
-template <int kN>
-__device__ __forceinline__ void lanes_lse(float &m, float &s, float c) {
-    static_assert(kN == 4 || kN == 8 || kN == 16, "4, 8 or 16 lanes");
-    lse_dpp_step<kDppXor1>(m, s, c);
-    lse_dpp_step<kDppXor2>(m, s, c);
-    if constexpr (kN >= 8) lse_dpp_step<kDppHalfMirror>(m, s, c);
-    if constexpr (kN >= 16) lse_dpp_step<kDppMirror>(m, s, c);
-    m = readlane_f32(m, 0);
-    s = readlane_f32(s, 0);
-}
-
 // Best kK keys of up to kPer*64 keys held kPer per lane (0 = empty).
 // Returns, in lane r < kK, the r-th best key (0 if fewer exist); *count gets
 // how many were found.  Each round finds the largest high word across the
@@ -426,6 +412,37 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     v += dpp_f32<kDppHalfMirror>(v);
     v += dpp_f32<kDppMirror>(v);
     return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = max_nan_free(v, dpp_f32<kDppXor1>(v));
+    v = max_nan_free(v, dpp_f32<kDppXor2>(v));
+    v = max_nan_free(v, dpp_f32<kDppHalfMirror>(v));
+    v = max_nan_free(v, dpp_f32<kDppMirror>(v));
+    return max_nan_free(max_nan_free(readlane_f32(v, 0), readlane_f32(v, 16)),
+                        max_nan_free(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+// The maximum and the sum over the first kN (4, 8 or 16) lanes, every lane
+// of the first row of 16 taking part (lanes kN..15 must hold -inf, or 0 for
+// the sum); the sum's order is fixed.
+template <int kN>
+__device__ __forceinline__ float first_lanes_max_f32(float v) {
+    static_assert(kN == 4 || kN == 8 || kN == 16, "4, 8 or 16 lanes");
+    v = max_nan_free(v, dpp_f32<kDppXor1>(v));
+    v = max_nan_free(v, dpp_f32<kDppXor2>(v));
+    if constexpr (kN >= 8) v = max_nan_free(v, dpp_f32<kDppHalfMirror>(v));
+    if constexpr (kN >= 16) v = max_nan_free(v, dpp_f32<kDppMirror>(v));
+    return readlane_f32(v, 0);
+}
+template <int kN>
+__device__ __forceinline__ float first_lanes_sum_f32(float v) {
+    static_assert(kN == 4 || kN == 8 || kN == 16, "4, 8 or 16 lanes");
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    if constexpr (kN >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if constexpr (kN >= 16) v += dpp_f32<kDppMirror>(v);
+    return readlane_f32(v, 0);
 }
 
 // Writes an output row from the row's best keys (lane i < kK holds the
@@ -966,16 +983,25 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // searches (6.5 us at 63 slots), or at 7 slots counting or kK wave-wide
     // maxima; with every wave ranking, decode at 7 slots went 24.5 -> 23.7
     // us and the 4-row batch (16 waves) 9.0 -> 8.5 us, same box.
+    //
+    // The workgroup's (M, S) comes from two plain reductions instead of
+    // pairwise (m, s) merges (two exponentials each): the wave maxima of m
+    // before the first barrier, then the workgroup maximum M, every lane's
+    // s scaled to it, and a wave sum.  The last wave's path after its last
+    // chunk loses a dozen dependent merge steps.
     if (lane < kK) s_keys[wave * kK + lane] = list;
-    wave_lse(m, s, c);
-    if (lane == 0) {
-        s_m[wave] = m;
-        s_s[wave] = s;
-    }
+    const float mw = wave_max_f32(m);
+    if (lane == 0) s_m[wave] = mw;
     constexpr int kN = kWaves * kK;
     static_assert(kN <= kThreads, "one key per thread");
     if (wave == 0 && lane < kK) s_top[lane] = 0ull;
     __syncthreads();
+    {
+        const float M = first_lanes_max_f32<kWaves>(lane < kWaves ? s_m[lane] : -INFINITY);
+        const float Ms = (M == -INFINITY) ? 0.0f : M;
+        const float sw = wave_sum_f32(s * fast_exp2((m - Ms) * c));   // lanes that saw no finite value: s = 0
+        if (lane == 0) s_s[wave] = sw;
+    }
     if (tid < kN) {
         const uint64_t key = s_keys[tid];
         if (key != 0) {
@@ -988,12 +1014,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __syncthreads();
     if (wave != 0) return;
     const uint64_t top = lane < kK ? s_top[lane] : 0ull;
-    float M = -INFINITY, S = 0.0f;
-    if (lane < kWaves) {
-        M = s_m[lane];
-        S = s_s[lane];
-    }
-    lanes_lse<kWaves>(M, S, c);
+    const float M = first_lanes_max_f32<kWaves>(lane < kWaves ? s_m[lane] : -INFINITY);
+    const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] : 0.0f);
 
     if (!a.records) {
         write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, temp, c, x_chosen, d.chosen);

@@ -144,8 +144,10 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, b
     if (read_rows > kCUs || vocab <= kVeryShortRow) {
         // more rows than compute units, or rows of at most 20K entries: 8
         // waves one chunk deep (2-8 % ahead of two deep at 320 rows, level
-        // at 512; 7-14 % ahead of 16 waves on rows of 8192 and 16000)
-        *waves = 8;
+        // at 512; 7-14 % ahead of 16 waves on rows of 8192 and 16000); with
+        // at most 3 slots and two rows or more per compute unit, 4 waves
+        // (520 rows of 32000 and 128256 at levels 1 and 2: 9-12 % ahead)
+        *waves = (slots <= 3 && read_rows >= 2 * kCUs) ? 4 : 8;
         *depth = 1;
         return;
     }

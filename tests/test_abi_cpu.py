@@ -203,7 +203,9 @@ def test_few_rows_shape(rows, vocab, shape):
     (6, 64, 24000, (1, 8, 2)), (6, 65, 32000, (1, 8, 2)), (5, 128, 32000, (1, 8, 2)),
     (6, 8, 1 << 29, (4, 16, 1)), (6, 200, 1 << 29, (2, 16, 1)),
     (4, 32, 151936, (8, 16, 1)), (4, 80, 128256, (3, 16, 1)),
-    (4, 96, 128256, (2, 16, 1)), (4, 2048, 128256, (1, 16, 1))])
+    (4, 96, 128256, (2, 16, 1)), (4, 2048, 128256, (1, 16, 1)),
+    (1, 520, 32000, (1, 4, 1)), (2, 800, 128256, (1, 4, 1)), (2, 511, 128256, (1, 8, 1)),
+    (1, 300, 16000, (1, 8, 1)), (3, 520, 32000, (1, 8, 1))])
 def test_shape_by_ranked_slots(levels, rows, vocab, shape):
     """With 31 or more ranked slots: 4 waves two deep for many rows, 8 one
     deep above one row per compute unit, rows of at most 65536 entries over 8

@@ -97,10 +97,12 @@ static void choose_variant(uint64_t read_rows, uint32_t vocab, uint32_t slots, b
             // their descriptors then hold 74 VGPRs, and three workgroups of
             // 8 waves fit a CU (520 rows of 32000 at levels 6: 27.9 against
             // 29.2 us one deep); direct rows also hold the first chunk's
-            // copy, 90 VGPRs, and fit two, so past 512 rows workgroups wait
-            // (33.8 against 30.3 us one deep).
+            // copy, 90 VGPRs, and fit two: two deep up to 512 rows (300 rows
+            // of 128256 at levels 6: 40.8 against 45.0 us), one deep past
+            // it, where workgroups would wait (520 rows of 32000: 33.8
+            // against 30.3 us two deep).
             *waves = 8;
-            if (!direct && vocab > kVeryShortRow) *depth = 2;
+            if (vocab > kVeryShortRow && (!direct || read_rows <= 2 * kCUs)) *depth = 2;
             return;
         }
         if (vocab <= kShortRow) {

@@ -194,7 +194,8 @@ def test_few_rows_shape(rows, vocab, shape):
 
 @pytest.mark.parametrize("levels,rows,vocab,shape", [
     (5, 2048, 32000, (1, 4, 2)), (6, 2048, 128256, (1, 4, 2)), (5, 1024, 256000, (1, 4, 2)),
-    (5, 512, 128256, (1, 8, 1)), (6, 520, 32000, (1, 8, 1)), (6, 300, 16000, (1, 8, 1)),
+    (5, 512, 128256, (1, 8, 2)), (5, 513, 128256, (1, 8, 1)), (6, 520, 32000, (1, 8, 1)),
+    (6, 300, 128256, (1, 8, 2)), (6, 300, 16000, (1, 8, 1)),
     (6, 200, 16000, (1, 8, 1)), (5, 256, 128256, (1, 16, 1)), (6, 129, 32000, (1, 8, 2)),
     (6, 32, 256000, (4, 16, 1)), (6, 96, 151936, (2, 16, 1)), (6, 16, 151936, (4, 16, 1)),
     (5, 32, 256000, (4, 16, 1)), (5, 64, 151936, (4, 16, 1)), (5, 32, 128256, (4, 16, 1)),

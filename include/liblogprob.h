@@ -241,7 +241,16 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
                            uint32_t *out_token_ids, void *workspace,
                            uint64_t workspace_bytes, void *stream);
 
-/* lp_compute_ragged = lp_stage_ragged followed by lp_launch_ragged. */
+/*
+ * lp_compute_ragged -- the descriptors of this call, then the kernels: the
+ * results of lp_stage_ragged followed by lp_launch_ragged, with the same
+ * arguments and errors.  For plans of at most 16384 output rows the kernels
+ * read the descriptors straight from the library's pinned host staging
+ * memory and no copy precedes them; the workspace then holds only split
+ * records, and its descriptor area is left unwritten (a later
+ * lp_launch_ragged on this workspace needs its own lp_stage_ragged).
+ * Larger plans stage into the workspace as lp_stage_ragged does.
+ */
 lp_status lp_compute_ragged(const lp_plan *plan, const float *logits,
                             const float *next_token_logits, const uint32_t *tokens,
                             const uint32_t *sampled_tokens, float *out_logprobs,

@@ -1274,6 +1274,17 @@ static void staging_release(StagingSlot *sl) {
     sl->busy = false;
 }
 
+// lp_compute_ragged lets the kernels read the descriptors of plans up to
+// this many output rows (256 KB) straight from the pinned staging slot.
+constexpr uint64_t kZeroCopyMaxRows = 16384;
+
+lp_status launch_checks(const lp_plan *plan, const float *logits, const float *next_token_logits,
+                        const float *out_logprobs, const uint32_t *out_token_ids,
+                        const void *workspace, uint64_t workspace_bytes);
+lp_status launch_rows(const lp_plan &p, const float *logits, const float *next_token_logits,
+                      float *out_logprobs, uint32_t *out_token_ids, void *workspace,
+                      const void *desc, hipStream_t s);
+
 template <int kK, int kWaves, int kDepth>
 static void launch_shape(bool direct, bool dyn, dim3 grid, hipStream_t s, const dev::RowArgs &ra) {
     const dim3 block(kWaves * 64);
@@ -1439,21 +1450,43 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
                            const float *next_token_logits, float *out_logprobs,
                            uint32_t *out_token_ids, void *workspace, uint64_t workspace_bytes,
                            void *stream) {
+    const lp_status st = lp::launch_checks(plan, logits, next_token_logits, out_logprobs,
+                                           out_token_ids, workspace, workspace_bytes);
+    if (st != LP_OK || plan->out_rows == 0) return st;
+    return lp::launch_rows(*plan, logits, next_token_logits, out_logprobs, out_token_ids,
+                           workspace, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace lp {
+
+// The argument checks of lp_launch_ragged (LP_OK for a plan with no rows).
+lp_status launch_checks(const lp_plan *plan, const float *logits, const float *next_token_logits,
+                        const float *out_logprobs, const uint32_t *out_token_ids,
+                        const void *workspace, uint64_t workspace_bytes) {
     if (plan == nullptr) return LP_ERR_NULL_ARG;
     if (plan->out_rows == 0) return LP_OK;
     if (out_logprobs == nullptr || out_token_ids == nullptr) return LP_ERR_NULL_ARG;
-    const float *src = plan->has_logits ? logits : next_token_logits;
-    if (src == nullptr) return LP_ERR_NULL_ARG;
-    lp_status st = lp::check_workspace(plan, workspace, workspace_bytes);
+    if ((plan->has_logits ? logits : next_token_logits) == nullptr) return LP_ERR_NULL_ARG;
+    const lp_status st = check_workspace(plan, workspace, workspace_bytes);
     if (st != LP_OK) return st;
-    const uint32_t waves = plan->waves;
-    const uint64_t blocks = plan->out_rows * plan->split;
-    if (blocks * waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
+    if (plan->out_rows * plan->split * plan->waves * 64ull >= (1ull << 32)) return LP_ERR_UNSUPPORTED;
+    return LP_OK;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// Enqueues the row kernel (and the merge kernel for split rows) of a
+// checked plan whose descriptors are at `desc` (device-readable: the
+// workspace, or pinned host memory) and whose records go to the workspace.
+lp_status launch_rows(const lp_plan &p, const float *logits, const float *next_token_logits,
+                      float *out_logprobs, uint32_t *out_token_ids, void *workspace,
+                      const void *desc, hipStream_t s) {
+    const lp_plan *plan = &p;
+    const float *src = plan->has_logits ? logits : next_token_logits;
+    const uint64_t blocks = plan->out_rows * plan->split;
     if (plan->read_rows == 0) return lp::launch_padding(*plan, out_logprobs, out_token_ids, s);
     const uint64_t words = plan->slots + 2;   // one record
-    lp::dev::RowArgs ra = lp::row_args(*plan, src, plan->vocab, 0, plan->split, workspace);
+    lp::dev::RowArgs ra = lp::row_args(*plan, src, plan->vocab, 0, plan->split, desc);
     ra.out_lp = out_logprobs;
     ra.out_id = out_token_ids;
     ra.records = plan->split > 1 ? 1u : 0u;
@@ -1477,14 +1510,53 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
     return LP_OK;
 }
 
+}  // namespace lp
+
+extern "C" {
+
 lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const float *next_token_logits,
                             const uint32_t *tokens, const uint32_t *sampled_tokens,
                             float *out_logprobs, uint32_t *out_token_ids, void *workspace,
                             uint64_t workspace_bytes, void *stream) {
-    lp_status st = lp_stage_ragged(plan, tokens, sampled_tokens, workspace, workspace_bytes, stream);
+    lp_status st = lp::launch_checks(plan, logits, next_token_logits, out_logprobs, out_token_ids,
+                                     workspace, workspace_bytes);
+    if (st != LP_OK || plan->out_rows == 0) return st;
+    if (plan->out_rows > lp::kZeroCopyMaxRows) {
+        st = lp_stage_ragged(plan, tokens, sampled_tokens, workspace, workspace_bytes, stream);
+        if (st != LP_OK) return st;
+        return lp::launch_rows(*plan, logits, next_token_logits, out_logprobs, out_token_ids,
+                               workspace, workspace, static_cast<hipStream_t>(stream));
+    }
+    // Small plans: the kernels read the descriptors from the pinned staging
+    // slot itself, and no copy precedes them (a 4 KB upload cost 5-8 us of
+    // the call on decode).  The slot is free again once the kernels that
+    // read it have run: its event is recorded after them.
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int device = 0;
+    LP_HIP_TRY(hipGetDevice(&device));
+    lp::StagingSlot *slot = nullptr;
+    st = lp::staging_acquire(plan->out_rows * sizeof(lp::RowDesc), device, &slot);
     if (st != LP_OK) return st;
-    return lp_launch_ragged(plan, logits, next_token_logits, out_logprobs, out_token_ids,
-                            workspace, workspace_bytes, stream);
+    st = lp::build_descriptors(*plan, tokens, sampled_tokens, static_cast<lp::RowDesc *>(slot->host));
+    void *desc = nullptr;
+    hipError_t e = hipSuccess;
+    if (st == LP_OK) e = hipHostGetDevicePointer(&desc, slot->host, 0);
+    if (st == LP_OK && e == hipSuccess)
+        st = lp::launch_rows(*plan, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
+                             desc, s);
+    if (st == LP_OK && e == hipSuccess) {
+        e = hipEventRecord(slot->done, s);
+        // kernels whose end no event marks may still read the slot: it
+        // stays taken for good rather than be refilled under them
+        if (e != hipSuccess) {
+            lp::g_last_hip_error = int(e);
+            return LP_ERR_HIP;
+        }
+    }
+    lp::staging_release(slot);
+    if (st != LP_OK) return st;
+    LP_HIP_TRY(e);
+    return LP_OK;
 }
 
 lp_status lp_compute_ragged_noalloc(const lp_plan *plan, const float *logits,

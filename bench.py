@@ -369,7 +369,9 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
     }
     rec["frac"] = rec["gbs"] / HBM_PEAK_GBS
     if extras:
-        # lp_compute_ragged per step: host descriptors, PCIe upload, launch
+        # lp_compute_ragged per step: host descriptors, their upload (or, up
+        # to 16384 rows, the kernels' reads of them in pinned host memory),
+        # the launch
         comp = [plan.computer(*srcs(c), case.tokens, case.sampled, lp, ids, ws, stream)
                 for c in copies]
         for i in range(3):
@@ -379,7 +381,8 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
         rec["compute_ragged"] = dict(cs, rows_per_s=read_rows / (cs["median_us"] * 1e-6),
                                      gbs=alg / (cs["median_us"] * 1e-6) / 1e9,
                                      note="lp_compute_ragged per step (host descriptor build, "
-                                          "PCIe upload, launch); event interval on the stream")
+                                          "upload or, up to 16384 rows, reads from pinned host "
+                                          "memory, launch); event interval on the stream")
         # leave the resident descriptors in place for the parity check
         plan.stage(case.tokens, case.sampled, ws, stream)
         launch[0]()

@@ -863,3 +863,38 @@ def test_launcher_holds_its_buffers(R):
     torch.cuda.synchronize()
     del churn
     assert_parity(held[2].cpu().numpy(), held[3].cpu().numpy(), plan.out_off, ref, "launcher buffers")
+
+
+@pytest.mark.parametrize("rows", [16384, 16385])
+def test_compute_descriptors_either_side_of_the_zero_copy_limit(R, rows):
+    """lp_compute_ragged lets the kernels read the descriptors of plans up to
+    16384 output rows from pinned host memory and stages larger plans into
+    the workspace: both sides of the limit match the oracle, and a staged
+    launch of the same plan (lp_stage_ragged, then lp_launch_ragged)
+    matches the compute call bit for bit."""
+    vocab = 1003
+    rng = np.random.default_rng(rows)
+    lengths = np.full(rows // 1 if rows % 2 else rows // 2, 1 if rows % 2 else 2)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    echo = np.ones(len(lengths), bool) if rows % 2 == 0 else np.zeros(len(lengths), bool)
+    top_n = rng.integers(1, 8, len(lengths))
+    logits = _special_rows(rng, int(off[-1]), vocab)
+    ntl = logits[off[1:].astype(np.int64) - 1]
+    tokens = rng.integers(0, vocab, int(off[-1])).astype(np.uint32)
+    sampled = rng.integers(0, vocab, len(lengths)).astype(np.uint32)
+    log(f"zero-copy limit: rows={rows}")
+    dl, dn = _dev(logits), _dev(ntl)
+    plan = R.Plan(off, echo, top_n, vocab, True)
+    assert plan.info()["out_rows"] == rows
+    lp, ids, ws = R.alloc_outputs(plan, torch.device("cuda"), torch)
+    plan.compute(dl, dn, tokens, sampled, lp, ids, ws)
+    lp2, ids2, _ = R.alloc_outputs(plan, torch.device("cuda"), torch)
+    plan.stage(tokens, sampled, ws)
+    plan.launch(dl, dn, lp2, ids2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    assert torch.equal(lp.view(torch.int32), lp2.view(torch.int32))
+    sample = sorted(set(rng.choice(rows, size=64, replace=False).tolist()) | {0, rows - 1})
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, rows=sample)
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, ref, f"rows={rows}", rows=sample)
+    plan.close()

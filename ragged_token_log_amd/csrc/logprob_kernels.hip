@@ -1218,6 +1218,11 @@ struct StagingSlot {
     bool busy = false;   // taken by a stage call that has not recorded its event yet
 };
 
+// Mapped, so the kernels of lp_compute_ragged can read a slot through its
+// device pointer, and coherent (fine-grained), so no GPU cache keeps a line
+// of a slot that the host refills for a later call.
+constexpr unsigned kStagingFlags = hipHostMallocMapped | hipHostMallocCoherent;
+
 static std::mutex g_staging_mutex;
 static std::vector<std::unique_ptr<StagingSlot>> g_staging;
 
@@ -1238,7 +1243,7 @@ static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) 
     }
     if (fit == nullptr && small != nullptr) {
         void *h = nullptr;
-        LP_HIP_TRY(hipHostMalloc(&h, bytes, hipHostMallocDefault));
+        LP_HIP_TRY(hipHostMalloc(&h, bytes, kStagingFlags));
         (void)hipHostFree(small->host);
         small->host = h;
         small->bytes = bytes;
@@ -1252,7 +1257,7 @@ static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) 
         } catch (...) {
             return LP_ERR_NOMEM;
         }
-        LP_HIP_TRY(hipHostMalloc(&sl->host, bytes, hipHostMallocDefault));
+        LP_HIP_TRY(hipHostMalloc(&sl->host, bytes, kStagingFlags));
         const hipError_t e = hipEventCreateWithFlags(&sl->done, hipEventDisableTiming);
         if (e != hipSuccess) {
             (void)hipHostFree(sl->host);

@@ -336,6 +336,42 @@ def _warm(calls, n_copies, steps, min_s, torch):
         torch.cuda.synchronize()
 
 
+PROBE_SHAPES = [(segs, threads, loads) for segs in (1, 2, 4) for threads in (256, 512, 1024)
+                for loads in (1, 2, 4, 8)]
+
+
+def probe_sweep(R, torch, dev, stream, case, args):
+    """The plain-read probe (lp_bench_stream_read_shape) in every launch
+    shape of PROBE_SHAPES over the workload's read rows, on the same cycled
+    copies as the bench: one JSON line per shape, then the fastest."""
+    import gen
+
+    base = gen.device_logits(case, dev, torch)
+    plan = make_plan(R, case, args)
+    rows = int(plan.info()["read_rows"])
+    plan.close()
+    read_bytes = rows * 4 * case.vocab
+    n_copies = max(1, math.ceil(ROTATE_BYTES / max(read_bytes, 1)))
+    copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+    steps = args.steps or DEFAULT_STEPS.get(case.name, 50)
+    best = None
+    for segs, threads, loads in PROBE_SHAPES:
+        partial = torch.empty(rows * segs, dtype=torch.float32, device=dev)
+        launch = [R.binding.stream_read_shape_launcher(c, rows, case.vocab, segs, threads, loads,
+                                                       partial, stream) for c in copies]
+        _warm(launch, n_copies, 3, SUB_WARM_S, torch)
+        us = _grouped_ms(launch, n_copies, steps, stream, torch) * 1e3
+        rec = {"workload": case.name, "rows": rows, "row_len": case.vocab, "segments": segs,
+               "threads": threads, "loads_per_thread": loads, "us": us,
+               "gbs": read_bytes / (us * 1e-6) / 1e9,
+               "frac": read_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+               "copies_cycled": n_copies, "steps": steps}
+        print(json.dumps(rec), flush=True)
+        if best is None or us < best["us"]:
+            best = rec
+    print(json.dumps({"probe_sweep_best": best, "shapes": len(PROBE_SHAPES)}), flush=True)
+
+
 def make_plan(R, case, args):
     plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits,
                   levels=args.levels)
@@ -496,6 +532,10 @@ def main():
                     help="log_softmax(logits / T) for every request")
     ap.add_argument("--top-k", type=int, default=0,
                     help="top-k front end (TopK on logits, then Softmax) for every request")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="time the plain-read probe in every launch shape (1, 2 or 4 workgroups "
+                         "per row; 256, 512 or 1024 threads; 1-8 loads in flight per thread) "
+                         "over the workload's read rows, print one JSON line per shape, exit")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the plain-read probe over the same rows (the practical ceiling)")
     ap.add_argument("--no-decode", action="store_true",
@@ -542,7 +582,7 @@ def main():
         case.top_n = np.where(np.asarray(case.top_n) > 0, args.top_n, 0).astype(np.int32)
     cols = 1 << args.levels if args.levels > 0 else 1
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.probe_sweep:
         # before anything touches the GPU: the pool forks this process
         cpu = cpu_baseline(case, cols)
 
@@ -555,6 +595,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+    if args.probe_sweep:
+        probe_sweep(R, torch, dev, stream, case, args)
+        return
 
     main_rec, plan, info, base, lp, ids, ws, copies = measure(
         R, torch, dev, stream, case, args, steps, args.warmup, probe=not args.no_probe,

@@ -371,6 +371,20 @@ int lp_last_hip_error(void);
 lp_status lp_bench_stream_read(const float *x, uint32_t rows, uint32_t row_len, float *partial_out,
                                void *stream);
 
+/*
+ * Measurement aid: the same plain read in another launch shape, to sweep
+ * what the memory system gives a row shape.  Each row is read by `segments`
+ * (1..64) workgroups of `threads` (256, 512 or 1024) threads, each taking one
+ * contiguous share of the row's float4s with `loads` (1, 2, 4 or 8)
+ * nontemporal 16-byte loads in flight per thread; workgroup row * segments +
+ * seg writes its share's sum to partial_out[rows * segments] (device).
+ * LP_ERR_UNSUPPORTED for a misaligned x or row_len, a shape outside those
+ * values, or rows * segments >= 2^31.
+ */
+lp_status lp_bench_stream_read_shape(const float *x, uint32_t rows, uint32_t row_len,
+                                     uint32_t segments, uint32_t threads, uint32_t loads,
+                                     float *partial_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

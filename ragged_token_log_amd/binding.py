@@ -33,6 +33,7 @@ EXPORTED = (
     "lp_shard_records",
     "lp_merge_shards", "lp_plan_destroy",
     "lp_status_string", "lp_last_hip_error", "lp_bench_stream_read",
+    "lp_bench_stream_read_shape",
 )
 
 LEVELS = 3          # default heap depth: 8 columns, top_n <= 7
@@ -104,6 +105,7 @@ def load():
     lib.lp_status_string.restype = ctypes.c_char_p
     lib.lp_last_hip_error.argtypes = []
     lib.lp_bench_stream_read.argtypes = [vp, u32, u32, vp, vp]
+    lib.lp_bench_stream_read_shape.argtypes = [vp, u32, u32, u32, u32, u32, vp, vp]
     for name in ("lp_plan_ragged", "lp_plan_get_info", "lp_plan_set_split",
                  "lp_plan_set_waves", "lp_plan_set_depth", "lp_plan_set_deterministic",
                  "lp_plan_set_temperature",
@@ -111,7 +113,7 @@ def load():
                  "lp_plan_descriptors", "lp_assemble_ragged",
                  "lp_stage_ragged", "lp_launch_ragged", "lp_shard_records", "lp_merge_shards",
                  "lp_compute_ragged", "lp_compute_ragged_noalloc", "lp_bench_stream_read",
-                 "lp_last_hip_error"):
+                 "lp_bench_stream_read_shape", "lp_last_hip_error"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -433,12 +435,34 @@ def stream_read_launcher(x, rows: int, row_len: int, partial, stream=None):
     """A zero-argument callable running the plain-read probe
     (lp_bench_stream_read) over ``rows`` rows of ``row_len`` floats of x."""
     lib = load()
+    if x.numel() < rows * row_len or partial.numel() < rows:
+        raise LogprobError(3, "x must hold rows * row_len floats and partial rows floats")
     args = (_dev_ptr(x), ctypes.c_uint32(rows), ctypes.c_uint32(row_len), _dev_ptr(partial),
             _stream_ptr(stream))
     keep = (x, partial)
 
     def launch():
         _check(lib.lp_bench_stream_read(*args), "lp_bench_stream_read")
+        return keep
+    return launch
+
+
+def stream_read_shape_launcher(x, rows: int, row_len: int, segments: int, threads: int,
+                               loads: int, partial, stream=None):
+    """A zero-argument callable running the plain-read probe in another launch
+    shape (lp_bench_stream_read_shape): ``segments`` workgroups of
+    ``threads`` per row, ``loads`` 16-byte loads in flight per thread;
+    ``partial`` holds rows * segments floats."""
+    lib = load()
+    if x.numel() < rows * row_len or partial.numel() < rows * segments:
+        raise LogprobError(3, "x must hold rows * row_len floats and partial rows * segments")
+    args = (_dev_ptr(x), ctypes.c_uint32(rows), ctypes.c_uint32(row_len),
+            ctypes.c_uint32(segments), ctypes.c_uint32(threads), ctypes.c_uint32(loads),
+            _dev_ptr(partial), _stream_ptr(stream))
+    keep = (x, partial)
+
+    def launch():
+        _check(lib.lp_bench_stream_read_shape(*args), "lp_bench_stream_read_shape")
         return keep
     return launch
 

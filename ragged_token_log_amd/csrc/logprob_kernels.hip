@@ -278,6 +278,31 @@ __device__ __forceinline__ uint32_t count_above(const uint64_t *list, uint64_t k
     return pos;
 }
 
+// The number of keys above `key` in kN lists of kK keys each, sorted in
+// descending order and stored one after another: the same binary search as
+// count_above in every list, taken a probe at a time across the lists, so
+// the kN reads of one probe go out together and the search costs
+// log2(kK + 1) LDS round trips, not that many per group of lists.
+template <int kK, int kN>
+__device__ __forceinline__ uint32_t count_above_lists(const uint64_t *lists, uint64_t key) {
+    uint32_t pos[kN];
+#pragma unroll
+    for (int w = 0; w < kN; ++w) pos[w] = 0;
+#pragma unroll
+    for (uint32_t step = (uint32_t(kK) + 1) / 2; step > 0; step >>= 1) {
+        uint64_t v[kN];
+#pragma unroll
+        for (int w = 0; w < kN; ++w) v[w] = lists[w * kK + pos[w] + step - 1];
+#pragma unroll
+        for (int w = 0; w < kN; ++w)
+            if (v[w] > key) pos[w] += step;
+    }
+    uint32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < kN; ++w) n += pos[w];
+    return n;
+}
+
 // ------------------------------------------------------------------ candidates
 //
 // Each wave keeps the K best keys it has seen (K = 2^levels - 1, 7 by
@@ -1006,8 +1031,17 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         const uint64_t key = s_keys[tid];
         if (key != 0) {
             uint32_t rank = 0;
+            if constexpr (kK <= 15 && kWaves >= 8) {
+                // all lists a probe at a time (decode, 256 rows of 128256:
+                // 23.03 -> 22.91 us; 520 rows of 32000: 15.75 -> 15.71 us)
+                rank = count_above_lists<kK, kWaves>(s_keys, key);
+            } else {
+                // longer searches, or four lists: list by list, which the
+                // compiler already overlaps four at a time (the interleaved
+                // form was 0.2-0.7 % slower at 31 and 63 slots)
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
+                for (int w = 0; w < kWaves; ++w) rank += count_above<kK>(s_keys + w * kK, key);
+            }
             if (rank < uint32_t(kK)) s_top[rank] = key;
         }
     }
@@ -1185,6 +1219,45 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const float *x, uint32
     if (threadIdx.x == 0) {
         float t = 0.0f;
         for (int k = 0; k < 8; ++k) t += red[k];
+        partial[blockIdx.x] = t;
+    }
+}
+
+// The same plain read in other shapes, for a sweep of what the memory system
+// gives this row shape: `segs` workgroups of kThreads per row, each reading
+// one contiguous share of the row's float4s with kLoads nontemporal 16-byte
+// loads in flight per thread, and writing its share's sum to
+// partial[row * segs + seg].  row_len is a multiple of 4.
+template <int kThreads, int kLoads>
+__global__ __launch_bounds__(kThreads) void stream_read_shape_kernel(const float *x, uint32_t row_len,
+                                                                     uint32_t segs, float *partial) {
+    __shared__ float red[kThreads / 64];
+    const uint32_t row = blockIdx.x / segs;
+    const uint32_t seg = blockIdx.x - row * segs;
+    const uint32_t n4 = row_len / 4;
+    const uint32_t per = (n4 + segs - 1) / segs;
+    const uint32_t b = seg * per < n4 ? seg * per : n4;
+    const uint32_t e = b + per < n4 ? b + per : n4;
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(x + uint64_t(row) * row_len);
+    float acc = 0.0f;
+    uint32_t i = b + threadIdx.x;
+    for (; i + uint32_t((kLoads - 1) * kThreads) < e; i += uint32_t(kLoads * kThreads)) {
+        f32x4 v[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    for (; i < e; i += kThreads) {
+        const f32x4 v = __builtin_nontemporal_load(p + i);
+        acc += (v.x + v.y) + (v.z + v.w);
+    }
+    acc = wave_sum_f32(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int k = 0; k < kThreads / 64; ++k) t += red[k];
         partial[blockIdx.x] = t;
     }
 }
@@ -1517,6 +1590,22 @@ lp_status launch_rows(const lp_plan &p, const float *logits, const float *next_t
 
 }  // namespace lp
 
+namespace lp {
+
+template <int kThreads>
+static void launch_stream_read_shape(uint32_t loads, dim3 grid, hipStream_t s, const float *x,
+                                     uint32_t row_len, uint32_t segs, float *partial) {
+    const dim3 block(kThreads);
+    switch (loads) {
+        case 1: hipLaunchKernelGGL((lp::dev::stream_read_shape_kernel<kThreads, 1>), grid, block, 0, s, x, row_len, segs, partial); break;
+        case 2: hipLaunchKernelGGL((lp::dev::stream_read_shape_kernel<kThreads, 2>), grid, block, 0, s, x, row_len, segs, partial); break;
+        case 4: hipLaunchKernelGGL((lp::dev::stream_read_shape_kernel<kThreads, 4>), grid, block, 0, s, x, row_len, segs, partial); break;
+        default: hipLaunchKernelGGL((lp::dev::stream_read_shape_kernel<kThreads, 8>), grid, block, 0, s, x, row_len, segs, partial); break;
+    }
+}
+
+}  // namespace lp
+
 extern "C" {
 
 lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const float *next_token_logits,
@@ -1649,6 +1738,28 @@ lp_status lp_merge_shards(const lp_plan *plan, uint32_t num_shards, const uint64
     ma.out_id = out_token_ids;
     if (!lp::launch_for_slots(*plan, lp::Launch::kMerge, dim3(1), s, ra, ma, plan->waves, plan->depth))
         return LP_ERR_UNSUPPORTED;
+    LP_HIP_TRY(hipGetLastError());
+    return LP_OK;
+}
+
+lp_status lp_bench_stream_read_shape(const float *x, uint32_t rows, uint32_t row_len,
+                                     uint32_t segments, uint32_t threads, uint32_t loads,
+                                     float *partial_out, void *stream) {
+    if (rows == 0) return LP_OK;
+    if (x == nullptr || partial_out == nullptr) return LP_ERR_NULL_ARG;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0 || (row_len & 3u) != 0 || row_len == 0)
+        return LP_ERR_UNSUPPORTED;
+    if (segments < 1 || segments > 64 || uint64_t(rows) * segments >= (1ull << 31))
+        return LP_ERR_UNSUPPORTED;
+    if (loads != 1 && loads != 2 && loads != 4 && loads != 8) return LP_ERR_UNSUPPORTED;
+    const dim3 grid(rows * segments);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (threads) {
+        case 256: lp::launch_stream_read_shape<256>(loads, grid, s, x, row_len, segments, partial_out); break;
+        case 512: lp::launch_stream_read_shape<512>(loads, grid, s, x, row_len, segments, partial_out); break;
+        case 1024: lp::launch_stream_read_shape<1024>(loads, grid, s, x, row_len, segments, partial_out); break;
+        default: return LP_ERR_UNSUPPORTED;
+    }
     LP_HIP_TRY(hipGetLastError());
     return LP_OK;
 }

@@ -898,3 +898,20 @@ def test_compute_descriptors_either_side_of_the_zero_copy_limit(R, rows):
     ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, rows=sample)
     assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, ref, f"rows={rows}", rows=sample)
     plan.close()
+
+
+@pytest.mark.parametrize("segs,threads,loads", [(1, 512, 4), (1, 256, 1), (2, 1024, 8), (4, 256, 2),
+                                                (3, 512, 8)])
+def test_stream_read_shapes_sum_rows(R, segs, threads, loads):
+    """The plain-read probe in its launch shapes reads every float of each
+    row once: the per-share sums add up to the row sums."""
+    log(f"stream read shape segs={segs} threads={threads} loads={loads}")
+    rng = np.random.default_rng(segs * 100 + loads)
+    rows, row_len = 37, 128256 + 4 * 97
+    x = _dev(rng.standard_normal((rows, row_len)).astype(np.float32))
+    partial = torch.full((rows * segs,), float("nan"), dtype=torch.float32, device="cuda")
+    R.binding.stream_read_shape_launcher(x, rows, row_len, segs, threads, loads, partial)()
+    torch.cuda.synchronize()
+    got = partial.view(rows, segs).double().sum(dim=1).cpu().numpy()
+    want = x.double().sum(dim=1).cpu().numpy()
+    assert np.all(np.abs(got - want) < 1e-3 * np.sqrt(row_len)), (got - want)

@@ -425,7 +425,9 @@ struct RowArgs {
 // carries no more than fp64 rounding, and the one rounding to fp32 at the
 // end is the only one of size (a few lanes per row: the cost is nil).
 __device__ __forceinline__ float logprob(float x, float M, float temp, float ln_s) {
-    return float((double(x) - double(M)) / double(temp) - double(ln_s));
+    const double d = double(x) - double(M);
+    // temperature 1 (a wave-uniform test) divides by nothing: d / 1 is d
+    return float((temp == 1.0f ? d : d / double(temp)) - double(ln_s));
 }
 
 // One output row of kK + 1 columns: lanes 0..kK-1 the ranked slots, lane kK
@@ -493,13 +495,17 @@ __device__ __forceinline__ void write_row(float *out_lp, uint32_t *out_id, uint6
         if (keep < listed) listed = keep;
     }
     const float ln_s = logf(S);
-    if (lane < kK) {
-        const bool valid = uint32_t(lane) < listed && key != 0;
-        out_lp[o * kC + lane] = valid ? logprob(key_value(key), M, temp, ln_s) : -INFINITY;
-        out_id[o * kC + lane] = valid ? key_id(key) : kPadId;
-    } else if (lane == kK) {
-        out_lp[o * kC + lane] = chosen_kept ? logprob(x_chosen, M, temp, ln_s) : -INFINITY;
-        out_id[o * kC + lane] = chosen;
+    // lanes 0..kK-1 the ranked slots, lane kK the chosen token: one pass, so
+    // the fp64 arithmetic runs once for all of them
+    const bool ranked = lane < kK;
+    const bool valid = ranked ? (uint32_t(lane) < listed && key != 0) : chosen_kept;
+    const float x = ranked ? key_value(key) : x_chosen;
+    const uint32_t id = ranked ? (valid ? key_id(key) : kPadId) : chosen;
+    float lp = -INFINITY;
+    if (valid) lp = logprob(x, M, temp, ln_s);
+    if (lane <= kK) {
+        out_lp[o * kC + lane] = lp;
+        out_id[o * kC + lane] = id;
     }
 }
 
@@ -1009,24 +1015,27 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // maxima; with every wave ranking, decode at 7 slots went 24.5 -> 23.7
     // us and the 4-row batch (16 waves) 9.0 -> 8.5 us, same box.
     //
-    // The workgroup's (M, S) comes from two plain reductions instead of
-    // pairwise (m, s) merges (two exponentials each): the wave maxima of m
-    // before the first barrier, then the workgroup maximum M, every lane's
-    // s scaled to it, and a wave sum.  The last wave's path after its last
-    // chunk loses a dozen dependent merge steps.
+    // The workgroup's (M, S) comes from plain reductions instead of pairwise
+    // (m, s) merges (two exponentials each): before the first barrier each
+    // wave takes the maximum of its lanes' m and the sum of their s scaled to
+    // it (one exponential per lane); after the second, wave 0 combines the
+    // waves' pairs the same way.  Between the barriers only the ranking is
+    // left (with the one-pass epilogue of write_row: 520 rows of 32000 15.62
+    // -> 15.37 us, decode 22.84 -> 22.74 us, same box).
     if (lane < kK) s_keys[wave * kK + lane] = list;
-    const float mw = wave_max_f32(m);
-    if (lane == 0) s_m[wave] = mw;
+    {
+        const float mw = wave_max_f32(m);
+        const float mws = (mw == -INFINITY) ? 0.0f : mw;
+        const float sw = wave_sum_f32(s * fast_exp2((m - mws) * c));   // lanes that saw no finite value: s = 0
+        if (lane == 0) {
+            s_m[wave] = mw;
+            s_s[wave] = sw;
+        }
+    }
     constexpr int kN = kWaves * kK;
     static_assert(kN <= kThreads, "one key per thread");
     if (wave == 0 && lane < kK) s_top[lane] = 0ull;
     __syncthreads();
-    {
-        const float M = first_lanes_max_f32<kWaves>(lane < kWaves ? s_m[lane] : -INFINITY);
-        const float Ms = (M == -INFINITY) ? 0.0f : M;
-        const float sw = wave_sum_f32(s * fast_exp2((m - Ms) * c));   // lanes that saw no finite value: s = 0
-        if (lane == 0) s_s[wave] = sw;
-    }
     if (tid < kN) {
         const uint64_t key = s_keys[tid];
         if (key != 0) {
@@ -1048,8 +1057,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __syncthreads();
     if (wave != 0) return;
     const uint64_t top = lane < kK ? s_top[lane] : 0ull;
-    const float M = first_lanes_max_f32<kWaves>(lane < kWaves ? s_m[lane] : -INFINITY);
-    const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] : 0.0f);
+    const float mi = lane < kWaves ? s_m[lane] : -INFINITY;
+    const float M = first_lanes_max_f32<kWaves>(mi);
+    const float Ms = (M == -INFINITY) ? 0.0f : M;
+    const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] * fast_exp2((mi - Ms) * c) : 0.0f);
 
     if (!a.records) {
         write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, temp, c, x_chosen, d.chosen);

@@ -34,7 +34,8 @@ Beside it, each on the same run:
                   timed output rows from their logits copied back, and the
                   line reports how many were checked and how many differ.
 
-The headline takes exactly W untimed warmup steps.  Every other leg (the
+The headline takes exactly W untimed warmup steps (without --warmup, about
+100 ms of launches: 4000 for decode, 5 for the prefill batch).  Every other leg (the
 decode record, lp_compute_ragged, the probe) keeps launching untimed for at
 least 100 ms first: after an idle spell the first milliseconds of short
 launches run slower than the steady state.
@@ -69,6 +70,10 @@ DEFAULT_WORKLOAD = "prefill_echo_large"
 SUB_WORKLOAD = "decode_peaked"
 DEFAULT_STEPS = {"no_echo_next_token": 200, "ragged_echo_mix": 200, "decode_peaked": 200,
                  "prefill_echo_large": 20, "tie_edge_stress": 30}
+# untimed warmup steps when --warmup is not given: about 100 ms of launches,
+# after which short launches run at their steady-state rate
+DEFAULT_WARMUP = {"no_echo_next_token": 10000, "ragged_echo_mix": 6000, "decode_peaked": 4000,
+                  "prefill_echo_large": 5, "tie_edge_stress": 5}
 MAX_CPU_WORKERS = 16          # the host share of one GPU on the GPU machines
 CPU_BUDGET_S = 8.0            # oracle seconds per CPU leg (one core, then all cores)
 CPU_ROWS_PER_WORKER = 24      # rows a worker draws and then runs in repeated passes
@@ -517,7 +522,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps before the K timed ones (default: about 100 ms "
+                         "of launches of the workload, 5 for the large batches)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--split", type=int, default=None, help="force the plan's split")
     ap.add_argument("--waves", type=int, default=None, help="force waves per workgroup (4|8|16)")
@@ -595,12 +602,13 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+    warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP.get(args.workload, 5)
     if args.probe_sweep:
         probe_sweep(R, torch, dev, stream, case, args)
         return
 
     main_rec, plan, info, base, lp, ids, ws, copies = measure(
-        R, torch, dev, stream, case, args, steps, args.warmup, probe=not args.no_probe,
+        R, torch, dev, stream, case, args, steps, warmup, probe=not args.no_probe,
         warm_s=0.0)
     ms_per_step = main_rec["ms_per_step"]
     read_rows = main_rec["read_rows"]
@@ -614,7 +622,7 @@ def main():
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -676,7 +684,7 @@ def main():
         if args.top_n is not None:
             dcase.top_n = np.where(np.asarray(dcase.top_n) > 0, args.top_n, 0).astype(np.int32)
         drec, dplan, dinfo, dbase, dlp, dids, _, dcopies = measure(
-            R, torch, dev, stream, dcase, args, DEFAULT_STEPS[SUB_WORKLOAD], args.warmup,
+            R, torch, dev, stream, dcase, args, DEFAULT_STEPS[SUB_WORKLOAD], warmup,
             probe=not args.no_probe)
         dtraffic = stored_traffic(dcase.name, dinfo, algorithmic_bytes(dinfo, dcase.vocab))
         drec["traffic"] = dtraffic
@@ -855,7 +863,7 @@ def write_profile(workload, trace_dir, fetch_dir, write_dir, split=None, waves=N
 def write_counter_table(workload, name, dirs):
     """profiles/<name>.txt: for each rocprofv3 --pmc output directory (one
     run each, of `bench.py --workload <workload> --no-cpu-baseline
-    --no-decode --steps 50`), the per-dispatch mean of every counter, for
+    --no-decode --steps 50 --warmup 5`), the per-dispatch mean of every counter, for
     the log-probability kernels and the plain-read probe."""
     rows = {}
     cmds = []
@@ -868,7 +876,8 @@ def write_counter_table(workload, name, dirs):
             names.add(r["Counter_Name"])
             rows.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
         cmds.append(f"rocprofv3 --pmc {' '.join(sorted(names))} --output-format csv -d <dir> -o <name> "
-                    f"-- python bench.py --workload {workload} --no-cpu-baseline --no-decode --steps 50")
+                    f"-- python bench.py --workload {workload} --no-cpu-baseline --no-decode --steps 50 "
+                    f"--warmup 5")
     with open(os.path.join(PROFILES, f"{name}.txt"), "w") as f:
         f.write(f"rocprofv3 counters: {workload} (per-dispatch mean over the run's dispatches)\n")
         for c in cmds:

@@ -454,6 +454,10 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
     if probe and case.vocab % 4 == 0 and read_rows > 0:
         rec["probe"] = bench_probe(copies, n_copies, read_rows, case.vocab, steps, stream, torch,
                                    dev, R, ms_per_step * 1e3)
+        best = stored_probe_best(case.name) if args.levels == 3 and args.top_n is None else None
+        if best is not None:
+            best["kernel_time_over_best"] = ms_per_step * 1e3 / best["us"]
+            rec["probe"]["sweep_best"] = best
     return rec, plan, info, base, lp, ids, ws, copies
 
 
@@ -763,6 +767,24 @@ def stored_traffic(workload, info, alg):
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def stored_probe_best(workload):
+    """The fastest plain-read shape in the committed sweep for this workload
+    (profiles/probe_sweep_<workload>.txt, written from `bench.py
+    --probe-sweep`), as {"us", "frac", "shape"}; None without one."""
+    import re
+
+    path = os.path.join(PROFILES, f"probe_sweep_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            m = re.match(r"fastest: (.*): ([0-9.]+) us, ([0-9.]+) of 8 TB/s", line.strip())
+            if m:
+                return {"us": float(m.group(2)), "frac": float(m.group(3)), "shape": m.group(1),
+                        "source": f"profiles/probe_sweep_{workload}.txt"}
+    return None
 
 
 def _read_csv(path):

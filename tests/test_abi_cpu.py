@@ -447,3 +447,28 @@ def test_deterministic_flag_round_trips():
     assert plan.info()["deterministic"] == 1
     plan.set_deterministic(False)
     assert plan.info()["deterministic"] == 0
+
+
+def test_stream_read_shapes_are_checked_before_any_hip_call():
+    """The plain-read probe refuses shapes it has no kernel for, a misaligned
+    buffer and a null pointer before any HIP call (so this runs without a
+    GPU); zero rows is a no-op."""
+    lib = binding.load()
+    names = {0: "LP_OK", 1: "LP_ERR_NULL_ARG", 8: "LP_ERR_UNSUPPORTED"}
+    fake = 1 << 20                       # 16-byte aligned, never dereferenced
+
+    def st(x, rows, row_len, segs, threads, loads, partial=fake):
+        return names.get(lib.lp_bench_stream_read_shape(x, rows, row_len, segs, threads, loads,
+                                                        partial, None), "other")
+
+    assert binding.status_string(8) == "LP_ERR_UNSUPPORTED"
+    assert st(fake, 0, 1024, 1, 512, 4) == "LP_OK"
+    assert st(None, 4, 1024, 1, 512, 4) == "LP_ERR_NULL_ARG"
+    assert st(fake, 4, 1024, 1, 512, 4, partial=None) == "LP_ERR_NULL_ARG"
+    assert st(fake + 4, 4, 1024, 1, 512, 4) == "LP_ERR_UNSUPPORTED"   # misaligned
+    assert st(fake, 4, 1022, 1, 512, 4) == "LP_ERR_UNSUPPORTED"       # row_len % 4
+    for segs, threads, loads in ((0, 512, 4), (65, 512, 4), (1, 384, 4), (1, 2048, 4),
+                                 (1, 512, 3), (1, 512, 16), (1, 512, 0)):
+        assert st(fake, 4, 1024, segs, threads, loads) == "LP_ERR_UNSUPPORTED", (segs, threads,
+                                                                                loads)
+    assert st(fake, 1 << 26, 1024, 64, 512, 4) == "LP_ERR_UNSUPPORTED"  # rows * segs >= 2^31

@@ -162,6 +162,9 @@ __device__ __forceinline__ uint64_t lds_load_relaxed(const uint64_t *p) {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// s_waitcnt immediate on gfx9-family parts: vmcnt(0), expcnt(7), lgkmcnt(15)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kAuxNontemporal = 2;         // cache-policy bit of the buffer load: nt
 
@@ -666,13 +669,17 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // LSE update for one chunk; returns the lane's chunk max
-    auto lse_chunk = [&](const f32x4 (&x)[kU]) __attribute__((always_inline)) {
-        // 16 values in 8 three-input maxima, a float4 at a time as they arrive
+    // the lane's chunk max: 16 values in 8 three-input maxima, a float4 at a
+    // time as they arrive
+    auto chunk_max = [&](const f32x4 (&x)[kU]) __attribute__((always_inline)) {
         float cm = max_nan_free(max_nan_free(x[0].x, x[0].y), max_nan_free(x[0].z, x[0].w));
 #pragma unroll
         for (int u = 1; u < kU; ++u)
             cm = max_nan_free(max_nan_free(max_nan_free(cm, x[u].x), x[u].y), max_nan_free(x[u].z, x[u].w));
+        return cm;
+    };
+    // the LSE update for a chunk whose lane max is cm
+    auto lse_from = [&](const f32x4 (&x)[kU], float cm) __attribute__((always_inline)) {
         const float mn = fmaxf(m, cm);
         const float ms = (mn == -INFINITY) ? 0.0f : mn;
         float acc[kU];
@@ -684,6 +691,10 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         const float csum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         s = s * fast_exp2((m - ms) * c) + csum;
         m = mn;
+    };
+    auto lse_chunk = [&](const f32x4 (&x)[kU]) __attribute__((always_inline)) {
+        const float cm = chunk_max(x);
+        lse_from(x, cm);
         return cm;
     };
 
@@ -974,19 +985,65 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
         // every wait for loads in flight must be stricter.  The shared bound
         // is read before each chunk's arithmetic, so that its latency hides
         // there.
-        while (cb[1 % kDepth] < nchunks) {
-#pragma unroll
-            for (int dd = 1; dd <= kDepth; ++dd) {
-                if (cb[dd % kDepth] < nchunks) {
+        if constexpr (kDepth == 1 && kK >= 31 && kWaves == 16) {
+            // One chunk in flight per wave, in two buffers taken in turn: once
+            // a chunk has arrived (its lane maxima are the first use) the
+            // next chunk goes into the other buffer, whose chunk is done, and
+            // only then does the arithmetic start, so the load is in flight
+            // while the wave computes instead of after it.  It pays where a
+            // chunk's work is long and a CU holds one workgroup: 31 and 63
+            // slots at 16 waves (decode, 256 rows of 128256: levels 5 26.92
+            // -> 26.51 us, levels 6 29.99 -> 29.59 us).  With 7 slots, or
+            // several workgroups per CU, the extra bytes in flight cost more
+            // than the overlap gains (decode at levels 3 22.78 -> 23.18 us,
+            // 520 rows of 32000 at 8 waves 15.63 -> 17.39 us).
+            f32x4 yb[kU];
+            uint32_t cy = 0;
+            auto refill_after = [&](f32x4 (&x)[kU], uint32_t &held, uint32_t prev) __attribute__((always_inline)) {
+                held = kDyn ? uint32_t(__builtin_amdgcn_readfirstlane(int(gv))) : prev + uint32_t(kWaves);
+                // the chunk being worked on has arrived: the only vector
+                // loads in flight are its own (vmcnt(0); expcnt and lgkmcnt
+                // left at their maxima, so nothing else is waited for)
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                refill(x, held);
+                if constexpr (kDyn) gv = grab();
+            };
+            while (cb[0] < nchunks) {
+                {
                     const uint64_t shared = lds_load_relaxed(&s_T);
-                    const float cm = lse_chunk(xb[dd % kDepth]);
+                    const float cm = chunk_max(xb[0]);
+                    refill_after(yb, cy, cb[0]);
+                    lse_from(xb[0], cm);
                     T = umax64(T, uniform64(shared));
-                    topk_chunk(xb[dd % kDepth], cb[dd % kDepth], cm);
+                    topk_chunk(xb[0], cb[0], cm);
                 }
-                refill_next(xb[dd % kDepth], cb[dd % kDepth]);
+                if (cy < nchunks) {
+                    const uint64_t shared = lds_load_relaxed(&s_T);
+                    const float cm = chunk_max(yb);
+                    refill_after(xb[0], cb[0], cy);
+                    lse_from(yb, cm);
+                    T = umax64(T, uniform64(shared));
+                    topk_chunk(yb, cy, cm);
+                } else {
+                    cb[0] = cy;   // past the end: every later index is too
+                }
+            }
+        } else {
+            while (cb[1 % kDepth] < nchunks) {
+#pragma unroll
+                for (int dd = 1; dd <= kDepth; ++dd) {
+                    if (cb[dd % kDepth] < nchunks) {
+                        const uint64_t shared = lds_load_relaxed(&s_T);
+                        const float cm = lse_chunk(xb[dd % kDepth]);
+                        T = umax64(T, uniform64(shared));
+                        topk_chunk(xb[dd % kDepth], cb[dd % kDepth], cm);
+                    }
+                    refill_next(xb[dd % kDepth], cb[dd % kDepth]);
+                }
             }
         }
     }
+
     if constexpr (kBulk) {
         // the keys still pending: merged, or a few inserted one at a time
         if (pending > kBulkFewKeys) {

@@ -131,7 +131,7 @@ def _levels_batch(seed, vocab, levels, rows_per_req=(1, 4, 1, 6, 2, 3)):
 @pytest.mark.parametrize("levels", [0, 1, 2, 4, 5, 6])
 @pytest.mark.parametrize("vocab", [3, 77, 1027, 40001])
 @pytest.mark.parametrize("split,waves,depth", [(None, None, None), (1, 4, 1), (3, 8, 2), (1, 16, 2),
-                                               (16, 4, 2)])
+                                               (16, 4, 2), (1, 16, 1), (2, 16, 1)])
 def test_levels(R, levels, vocab, split, waves, depth):
     """[MAX] log_probabilities_ragged_graph: 2**levels columns, top_n up to
     2**levels - 1, every heap depth the library serves."""
@@ -915,3 +915,20 @@ def test_stream_read_shapes_sum_rows(R, segs, threads, loads):
     got = partial.view(rows, segs).double().sum(dim=1).cpu().numpy()
     want = x.double().sum(dim=1).cpu().numpy()
     assert np.all(np.abs(got - want) < 1e-3 * np.sqrt(row_len)), (got - want)
+
+
+@pytest.mark.parametrize("levels", [5, 6])
+@pytest.mark.parametrize("vocab", [15 * 1024, 16 * 1024, 17 * 1024 + 5, 33 * 1024 + 3, 128256])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_two_buffer_stream_at_large_k(R, levels, vocab, deterministic):
+    """31 and 63 slots at 16 waves one chunk deep stream through two buffers
+    taken in turn: chunk counts below, at and just past one per wave, and a
+    decode-width row, in both chunk orders, against the oracle."""
+    log(f"two-buffer stream levels={levels} vocab={vocab} deterministic={deterministic}")
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(vocab + levels, vocab, levels,
+                                                                   rows_per_req=(1, 3, 1, 2))
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
+    for split in (1, 2):
+        got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
+                          split, 16, 1, levels=levels, deterministic=deterministic)
+        assert_parity(*got, ref, f"two-buffer levels={levels} vocab={vocab} split={split}")

@@ -587,6 +587,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ uint64_t s_T;
     __shared__ uint64_t s_pub[kWaves];
     __shared__ float s_m[kWaves], s_s[kWaves];
+    __shared__ float s_ms2[2];
     __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
     constexpr bool kBulk = kK >= kBulkMinK;
     __shared__ uint64_t s_cand[kBulk ? kWaves * kWave : 1];   // per wave: gathered keys not yet merged
@@ -1076,8 +1077,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // The workgroup's (M, S) comes from plain reductions instead of pairwise
     // (m, s) merges (two exponentials each): before the first barrier each
     // wave takes the maximum of its lanes' m and the sum of their s scaled to
-    // it (one exponential per lane); after the second, wave 0 combines the
-    // waves' pairs the same way.  Between the barriers only the ranking is
+    // it (one exponential per lane); between the barriers the last wave
+    // combines the waves' pairs the same way.  Between the barriers only the ranking is
     // left (with the one-pass epilogue of write_row: 520 rows of 32000 15.62
     // -> 15.37 us, decode 22.84 -> 22.74 us, same box).
     if (lane < kK) s_keys[wave * kK + lane] = list;
@@ -1094,6 +1095,20 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     static_assert(kN <= kThreads, "one key per thread");
     if (wave == 0 && lane < kK) s_top[lane] = 0ull;
     __syncthreads();
+    // The last wave (idle in the ranking at up to 15 slots) combines the
+    // waves' (max, sum) pairs while the others rank, so that wave 0 only
+    // reads the result after the second barrier (decode 22.64 -> 22.53 us,
+    // the 4-row batch 8.13 -> 8.01 us, same box).
+    if (wave == kWaves - 1) {
+        const float mi = lane < kWaves ? s_m[lane] : -INFINITY;
+        const float M = first_lanes_max_f32<kWaves>(mi);
+        const float Ms = (M == -INFINITY) ? 0.0f : M;
+        const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] * fast_exp2((mi - Ms) * c) : 0.0f);
+        if (lane == 0) {
+            s_ms2[0] = M;
+            s_ms2[1] = S;
+        }
+    }
     if (tid < kN) {
         const uint64_t key = s_keys[tid];
         if (key != 0) {
@@ -1115,10 +1130,8 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __syncthreads();
     if (wave != 0) return;
     const uint64_t top = lane < kK ? s_top[lane] : 0ull;
-    const float mi = lane < kWaves ? s_m[lane] : -INFINITY;
-    const float M = first_lanes_max_f32<kWaves>(mi);
-    const float Ms = (M == -INFINITY) ? 0.0f : M;
-    const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] * fast_exp2((mi - Ms) * c) : 0.0f);
+    const float M = s_ms2[0];
+    const float S = s_ms2[1];
 
     if (!a.records) {
         write_row<kK>(a.out_lp, a.out_id, o, lane, top, d.top_n, M, S, temp, c, x_chosen, d.chosen);

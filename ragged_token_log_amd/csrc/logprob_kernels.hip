@@ -15,7 +15,8 @@
 //  * Each row (or row segment, or vocabulary shard) is one workgroup of 4, 8
 //    or 16 waves.  Waves take interleaved chunks of 64 lanes x kU float4,
 //    read with nontemporal buffer loads, one or two chunks in flight per
-//    wave.  Per chunk a lane reduces its 16 values to a chunk max and updates
+//    wave (two buffers taken in turn at 31+ slots with 16 waves one deep).
+//    Per chunk a lane reduces its 16 values to a chunk max and updates
 //    a running (m, s) with s = sum 2^((x - m) log2(e) / T), the subtraction
 //    first.
 //  * Ranking uses a 64-bit order key: the fp32 bits mapped to an unsigned
@@ -28,11 +29,11 @@
 //    slots also the waves' published keys).  A chunk whose lane maxima stay
 //    below T costs one compare; the few columns that beat it enter their
 //    keys one at a time, or at 63 slots are gathered and merged in bulk.
-//  * The waves' lists and (m, s) pairs meet in LDS; every wave ranks its
-//    share of the keys, and wave 0 writes lp = (x - M) / T - ln S for the K
-//    best and for the chosen token, or, for segments and shards, a record of
-//    (M, S, K keys, chosen logit) that a second kernel (one wave per row)
-//    merges.
+//  * The waves' lists and (max, sum) pairs meet in LDS; the waves rank the
+//    keys against all the lists while the last wave combines the pairs, and
+//    wave 0 writes lp = (x - M) / T - ln S for the K best and for the chosen
+//    token, or, for segments and shards, a record of (M, S, K keys, chosen
+//    logit) that a second kernel (one wave per row) merges.
 //
 // No MFMA: there is no contraction here.
 #include <hip/hip_runtime.h>

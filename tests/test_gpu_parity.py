@@ -932,3 +932,51 @@ def test_two_buffer_stream_at_large_k(R, levels, vocab, deterministic):
         got = run_library(R, torch, off, _dev(logits), _dev(ntl), tokens, sampled, top_n, echo,
                           split, 16, 1, levels=levels, deterministic=deterministic)
         assert_parity(*got, ref, f"two-buffer levels={levels} vocab={vocab} split={split}")
+
+
+def test_staging_slots_reused_across_streams(R):
+    """Staging slots finish out of order: a long launch on one stream holds
+    the oldest slot while many short ones on a second stream finish and are
+    reused (the pool looks past a busy first slot).  Every short call writes
+    its own outputs and they all match the oracle; so do sampled rows of the
+    long one."""
+    dev = torch.device("cuda")
+    slow, fast = torch.cuda.Stream(), torch.cuda.Stream()
+    # the long launch: 12000 rows of 32000 read through the zero-copy path
+    rng = np.random.default_rng(77)
+    n_long, v_long = 12000, 32000
+    long_logits = torch.from_numpy(rng.standard_normal((n_long, v_long), dtype=np.float32) * 2).to(dev)
+    long_off = np.array([0, n_long], np.uint32)
+    long_tok = rng.integers(0, v_long, n_long).astype(np.uint32)
+    long_smp = rng.integers(0, v_long, 1).astype(np.uint32)
+    long_plan = R.Plan(long_off, [1], [7], v_long, True)
+    with torch.cuda.stream(slow):
+        llp, lids, lws = R.alloc_outputs(long_plan, dev, torch)
+    torch.cuda.synchronize()
+    # the short calls: 40 small batches, each with its own inputs and outputs
+    shorts = []
+    for i in range(40):
+        off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(900 + i, 1000 + 37 * i, 3,
+                                                                       rows_per_req=(1, 2, 1, 3))
+        plan = R.Plan(off, echo, top_n, ntl.shape[1], True)
+        with torch.cuda.stream(fast):
+            lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+        shorts.append(((off, logits, ntl, tokens, sampled, top_n, echo), plan, _dev(logits),
+                       _dev(ntl), lp, ids, ws))
+    torch.cuda.synchronize()
+    long_plan.compute(long_logits, None, long_tok, long_smp, llp, lids, lws, slow)
+    for c, plan, lg, nt, lp, ids, ws in shorts:
+        plan.compute(lg, nt, c[3], c[4], lp, ids, ws, fast)
+    torch.cuda.synchronize()
+    for i, (c, plan, lg, nt, lp, ids, ws) in enumerate(shorts):
+        ref = oracle(*c)
+        assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off.copy(), ref,
+                      f"short call {i} beside a long one")
+        plan.close()
+    tasks = LO.row_tasks(long_off, [1], [7], long_tok, long_smp, True)
+    for r in (0, 1, 4321, n_long - 1):
+        t = tasks[r]
+        want_lp, want_ids = LO.compute_row(long_logits[t.src_row].cpu().numpy(), t.chosen, t.top_n, 8)
+        assert np.array_equal(lids[r].cpu().numpy(), want_ids), r
+        assert_lp_close(llp[r].cpu().numpy(), want_lp, f"long row {r}")
+    long_plan.close()

@@ -493,22 +493,25 @@ def bench_shards(args, case, plan, info, copies, n_copies, torch, dev, stream, w
     ids = torch.empty(lp.shape, dtype=torch.uint32, device=dev)
     torch.cuda.synchronize()
 
+    rec_calls = [[plan.shard_records_launcher(bounds[k][0], t if case.has_logits else None,
+                                              None if case.has_logits else t, rec[k], ws, stream)
+                  for k, t in enumerate(copy_shards)] for copy_shards in shards]
+    merge = plan.merge_launcher(S, rec, lp, ids, ws, stream)
+
     def records(i, k):
-        t = shards[i % len(shards)][k]
-        plan.shard_records(bounds[k][0], t if case.has_logits else None,
-                           None if case.has_logits else t, rec[k], ws, stream)
+        rec_calls[i % len(rec_calls)][k]()
 
     steps = 50
     for i in range(3):
         records(i, 0)
-    plan.merge_shards(S, rec, lp, ids, ws, stream)
+    merge()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     ev[0].record(stream)
     for i in range(steps):
         records(i, i % S)
     ev[1].record(stream)
     for i in range(steps):
-        plan.merge_shards(S, rec, lp, ids, ws, stream)
+        merge()
     ev[2].record(stream)
     torch.cuda.synchronize()
     rec_us = ev[0].elapsed_time(ev[1]) * 1e3 / steps

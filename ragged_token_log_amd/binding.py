@@ -204,8 +204,10 @@ class Plan:
         self.has_logits = bool(has_logits)
         self.out_off = out_off
         self.out_rows = int(rows.value)
+        self.logits_rows = int(logits_rows)
         self.input_row_offsets = off
         self._columns = None
+        self.record_words = int(self.info()["record_words"])   # fixed by the levels
 
     def _token_arrays(self, tokens, sampled_tokens):
         """The host id arrays as the library reads them: tokens (T =
@@ -311,6 +313,20 @@ class Plan:
         return toks, vals, counts
 
     # ---------------------------------------------------------------- device work
+    def _check_buffers(self, logits, next_token_logits, out_logprobs, out_token_ids):
+        """The kernels read and write these tensors through bare pointers, so
+        each given one must be a contiguous GPU tensor of the right element
+        type holding at least what the plan reads or writes (LP_ERR_SHAPE
+        otherwise); a missing one is left to the library (LP_ERR_NULL_ARG)."""
+        src = logits if self.has_logits else next_token_logits
+        rows = self.logits_rows if self.has_logits else self.batch
+        _check_device_tensor(src, "logits" if self.has_logits else "next_token_logits",
+                             (4,), rows * self.vocab)
+        if self.out_rows > 0:
+            n = self.out_rows * self.columns
+            _check_device_tensor(out_logprobs, "out_logprobs", (4,), n, floating=True)
+            _check_device_tensor(out_token_ids, "out_token_ids", (4,), n, floating=False)
+
     def stage(self, tokens, sampled_tokens, workspace, stream=None):
         tok, smp = self._token_arrays(tokens, sampled_tokens)
         _check(self._lib.lp_stage_ragged(self._h, _ptr(tok, ctypes.c_uint32),
@@ -320,6 +336,7 @@ class Plan:
 
     def launch(self, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
                stream=None):
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         _check(self._lib.lp_launch_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
                                           _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
                                           _dev_ptr(workspace), _nbytes(workspace),
@@ -331,6 +348,7 @@ class Plan:
         its ctypes arguments converted once (for tight launch loops).  It
         holds references to the tensors, so their memory cannot go back to
         the caching allocator while the callable exists."""
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         fn = self._lib.lp_launch_ragged
         args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _dev_ptr(out_logprobs),
                 _dev_ptr(out_token_ids), _dev_ptr(workspace), ctypes.c_uint64(_nbytes(workspace)),
@@ -351,6 +369,7 @@ class Plan:
         checked and converted once; it keeps the host id arrays and the
         tensors alive."""
         tok, smp = self._token_arrays(tokens, sampled_tokens)
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         fn = self._lib.lp_compute_ragged
         args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _ptr(tok), _ptr(smp),
                 _dev_ptr(out_logprobs), _dev_ptr(out_token_ids), _dev_ptr(workspace),
@@ -367,6 +386,7 @@ class Plan:
     def compute(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
                 out_token_ids, workspace, stream=None):
         tok, smp = self._token_arrays(tokens, sampled_tokens)
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         _check(self._lib.lp_compute_ragged(self._h, _dev_ptr(logits), _dev_ptr(next_token_logits),
                                            _ptr(tok, ctypes.c_uint32), _ptr(smp, ctypes.c_uint32),
                                            _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
@@ -379,6 +399,7 @@ class Plan:
         fixed device workspace (at most 4 MiB of workspace; no allocation).
         Returns after the descriptor copy; the kernels run on ``stream``."""
         tok, smp = self._token_arrays(tokens, sampled_tokens)
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         _check(self._lib.lp_compute_ragged_noalloc(self._h, _dev_ptr(logits),
                                                    _dev_ptr(next_token_logits),
                                                    _ptr(tok, ctypes.c_uint32),
@@ -387,27 +408,80 @@ class Plan:
                                                    _stream_ptr(stream)),
                "lp_compute_ragged_noalloc")
 
+    def _shard_args(self, vocab_begin, shard_logits, shard_next_token_logits, records, workspace,
+                    stream):
+        t = shard_logits if self.has_logits else shard_next_token_logits
+        if t is None or t.dim() != 2:
+            raise LogprobError(3, "the shard's logits must be a 2-D tensor")
+        width = int(t.shape[1])
+        rows = self.logits_rows if self.has_logits else self.batch
+        _check_device_tensor(t, "shard logits", (4,), rows * width, floating=True)
+        if self.out_rows > 0:
+            _check_device_tensor(records, "records", (8, 4, 2, 1),
+                                 self.out_rows * self.record_words * 8, as_bytes=True)
+        return (self._h, int(vocab_begin), width, _dev_ptr(shard_logits),
+                _dev_ptr(shard_next_token_logits), _dev_ptr(records), _dev_ptr(workspace),
+                ctypes.c_uint64(_nbytes(workspace)), _stream_ptr(stream))
+
     def shard_records(self, vocab_begin: int, shard_logits, shard_next_token_logits, records,
                       workspace, stream=None):
         """lp_shard_records: one record per output row for the vocabulary
         shard [vocab_begin, vocab_begin + width) whose logits (rows of
         ``width`` fp32, the shard's columns only) are given; ``records`` is a
         device tensor of out_rows * record_words 8-byte words."""
-        t = shard_logits if self.has_logits else shard_next_token_logits
-        width = int(t.shape[1])
-        _check(self._lib.lp_shard_records(self._h, int(vocab_begin), width, _dev_ptr(shard_logits),
-                                          _dev_ptr(shard_next_token_logits), _dev_ptr(records),
-                                          _dev_ptr(workspace), _nbytes(workspace),
-                                          _stream_ptr(stream)), "lp_shard_records")
+        _check(self._lib.lp_shard_records(*self._shard_args(vocab_begin, shard_logits,
+                                                            shard_next_token_logits, records,
+                                                            workspace, stream)),
+               "lp_shard_records")
+
+    def shard_records_launcher(self, vocab_begin: int, shard_logits, shard_next_token_logits,
+                               records, workspace, stream=None):
+        """A zero-argument callable doing lp_shard_records with these buffers,
+        checked and converted once (for tight launch loops)."""
+        fn = self._lib.lp_shard_records
+        args = self._shard_args(vocab_begin, shard_logits, shard_next_token_logits, records,
+                                workspace, stream)
+        keep = (shard_logits, shard_next_token_logits, records, workspace, self)
+
+        def launch():
+            st = fn(*args)
+            if st != 0:
+                _check(st, "lp_shard_records")
+            return keep
+        return launch
+
+    def _merge_args(self, num_shards, records, out_logprobs, out_token_ids, workspace, stream):
+        if self.out_rows > 0:
+            _check_device_tensor(records, "records", (8, 4, 2, 1),
+                                 int(num_shards) * self.out_rows * self.record_words * 8,
+                                 as_bytes=True)
+        self._check_buffers(None, None, out_logprobs, out_token_ids)
+        return (self._h, int(num_shards), _dev_ptr(records), _dev_ptr(out_logprobs),
+                _dev_ptr(out_token_ids), _dev_ptr(workspace), ctypes.c_uint64(_nbytes(workspace)),
+                _stream_ptr(stream))
 
     def merge_shards(self, num_shards: int, records, out_logprobs, out_token_ids, workspace,
                      stream=None):
         """lp_merge_shards over records laid out (num_shards, out_rows,
         record_words) in a device tensor."""
-        _check(self._lib.lp_merge_shards(self._h, int(num_shards), _dev_ptr(records),
-                                         _dev_ptr(out_logprobs), _dev_ptr(out_token_ids),
-                                         _dev_ptr(workspace), _nbytes(workspace),
-                                         _stream_ptr(stream)), "lp_merge_shards")
+        _check(self._lib.lp_merge_shards(*self._merge_args(num_shards, records, out_logprobs,
+                                                           out_token_ids, workspace, stream)),
+               "lp_merge_shards")
+
+    def merge_launcher(self, num_shards: int, records, out_logprobs, out_token_ids, workspace,
+                       stream=None):
+        """A zero-argument callable doing lp_merge_shards with these buffers,
+        checked and converted once."""
+        fn = self._lib.lp_merge_shards
+        args = self._merge_args(num_shards, records, out_logprobs, out_token_ids, workspace, stream)
+        keep = (records, out_logprobs, out_token_ids, workspace, self)
+
+        def launch():
+            st = fn(*args)
+            if st != 0:
+                _check(st, "lp_merge_shards")
+            return keep
+        return launch
 
     def close(self):
         if self._h is not None and self._h.value:
@@ -425,6 +499,27 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def _check_device_tensor(t, name, itemsizes, need, floating=None, as_bytes=False):
+    """A contiguous GPU tensor whose element size is in ``itemsizes`` (and
+    floating point or not, when ``floating`` says) holding at least ``need``
+    elements (bytes with ``as_bytes``); None passes (the library reports
+    it).  LP_ERR_SHAPE otherwise."""
+    if t is None:
+        return
+    if getattr(t, "device", None) is None or t.device.type != "cuda":
+        raise LogprobError(3, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise LogprobError(3, f"{name} must be contiguous")
+    if t.element_size() not in itemsizes:
+        raise LogprobError(3, f"{name} has {t.element_size()}-byte elements")
+    if floating is not None and t.is_floating_point() != floating:
+        raise LogprobError(3, f"{name} must be {'float32' if floating else 'an integer type'}")
+    have = t.numel() * t.element_size() if as_bytes else t.numel()
+    if have < need:
+        raise LogprobError(3, f"{name} holds {have} {'bytes' if as_bytes else 'elements'}, "
+                              f"the plan needs {need}")
 
 
 def _nbytes(t) -> int:

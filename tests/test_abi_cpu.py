@@ -472,3 +472,22 @@ def test_stream_read_shapes_are_checked_before_any_hip_call():
         assert st(fake, 4, 1024, segs, threads, loads) == "LP_ERR_UNSUPPORTED", (segs, threads,
                                                                                 loads)
     assert st(fake, 1 << 26, 1024, 64, 512, 4) == "LP_ERR_UNSUPPORTED"  # rows * segs >= 2^31
+
+
+def test_device_buffers_are_checked_before_any_hip_call():
+    """The binding hands the kernels bare pointers, so it refuses host
+    tensors, non-contiguous ones and ones of the wrong element type before
+    any HIP call (LP_ERR_SHAPE); a missing buffer is left to the library."""
+    import torch
+
+    plan = R.Plan([0, 3, 5], [1, 0], [3, 2], 100, True)
+    host_logits = torch.zeros(5, 100)
+    _expect("LP_ERR_SHAPE", lambda: plan.launch(host_logits, None, None, None, None))
+    _expect("LP_ERR_SHAPE", lambda: plan.launcher(host_logits, None, None, None, None))
+    _expect("LP_ERR_SHAPE", lambda: plan.compute(host_logits, None, np.arange(5), [1, 2], None,
+                                                 None, None))
+    _expect("LP_ERR_SHAPE", lambda: plan.compute_noalloc(host_logits, None, np.arange(5), [1, 2],
+                                                         None, None))
+    with pytest.raises(binding.LogprobError):
+        binding._check_device_tensor(torch.zeros(4, 4).t(), "x", (4,), 16)
+    binding._check_device_tensor(None, "x", (4,), 16)   # missing: the library reports it

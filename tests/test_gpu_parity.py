@@ -980,3 +980,31 @@ def test_staging_slots_reused_across_streams(R):
         assert np.array_equal(lids[r].cpu().numpy(), want_ids), r
         assert_lp_close(llp[r].cpu().numpy(), want_lp, f"long row {r}")
     long_plan.close()
+
+
+def test_short_or_mistyped_device_buffers_are_refused(R):
+    """Device buffers smaller than the plan reads or writes, of the wrong
+    element type or not contiguous are refused (LP_ERR_SHAPE) before any
+    kernel runs; the same call with the right buffers matches the oracle."""
+    off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(4242, 3001, 3)
+    plan = R.Plan(off, echo, top_n, ntl.shape[1], True)
+    dev = torch.device("cuda")
+    lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+    lg, nt = _dev(logits), _dev(ntl)
+    bad = [
+        (lg[:-1], nt, lp, ids),                                    # one logits row short
+        (lg.double(), nt, lp, ids),                                # fp64 logits
+        (torch.empty(lg.shape[1], lg.shape[0], device=dev).t(), nt, lp, ids),   # not contiguous
+        (lg, nt, lp[:-1], ids),                                    # one output row short
+        (lg, nt, lp, ids.view(torch.float32)),                     # ids as floats
+        (lg, nt, lp.view(torch.int32), ids),                       # logprobs as integers
+    ]
+    for k, (a, b, c, d) in enumerate(bad):
+        with pytest.raises(R.LogprobError) as e:
+            plan.compute(a, b, tokens, sampled, c, d, ws)
+        assert e.value.name == "LP_ERR_SHAPE", (k, e.value.name)
+    plan.compute(lg, nt, tokens, sampled, lp, ids, ws)
+    torch.cuda.synchronize()
+    ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo)
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off.copy(), ref, "after refusals")
+    plan.close()

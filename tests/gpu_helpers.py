@@ -68,6 +68,26 @@ def assert_parity(lp, ids, out_off, ref, where, rows=None):
     assert_lp_close(lp[sel], ref_lp[sel], where)
 
 
+def assert_close_rel(got, want, where):
+    """Logprobs at a temperature T != 1: |lp| reaches |x - max| / T.  The
+    kernels divide by T in fp64, so the value carries the same few-1e-7 error
+    as at T = 1 before its one rounding to fp32; where |lp| >= 128 an fp32 ulp
+    exceeds 1e-5, and the two roundings (oracle, kernel) may then land one ulp
+    apart.  The bound is 1e-5, plus one ulp of the expected value where
+    |lp| >= 128 (NaN and infinities exactly)."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(nan, np.isnan(got)), where
+    inf = np.isinf(want)
+    assert np.array_equal(got[inf], want[inf]), where
+    fin = ~nan & ~inf
+    mag = np.abs(want[fin])
+    tol = 1e-5 + np.where(mag >= 128.0, np.spacing(mag), 0.0)
+    d = np.abs(got[fin].astype(np.float64) - want[fin])
+    assert np.all(d <= tol), (where, float(d.max()), float(np.abs(want[fin]).max()))
+
+
 def oracle(offsets, logits, ntl, tokens, sampled, top_n, echo, rows=None, levels=3):
     return LO.compute_log_probabilities_ragged(offsets, logits, ntl, tokens, sampled,
                                                list(top_n), list(echo), rows=rows, levels=levels)

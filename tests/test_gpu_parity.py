@@ -10,7 +10,8 @@ import pytest
 
 import gen
 import oracle.logprob_oracle as LO
-from tests.gpu_helpers import (DeviceRows, assert_lp_close, assert_parity, check_all_rows_properties,
+from tests.gpu_helpers import (DeviceRows, assert_close_rel, assert_lp_close, assert_parity,
+                               check_all_rows_properties,
                                log, oracle, run_library)
 from tests.gpu_helpers import special_rows as _special_rows
 
@@ -172,26 +173,6 @@ def test_levels_direct_rows(R, levels):
         assert_parity(*got, ref, f"direct levels={levels} split={split}")
 
 
-def _assert_close_rel(got, want, where):
-    """Logprobs at a temperature T != 1: |lp| reaches |x - max| / T.  The
-    kernels divide by T in fp64, so the value carries the same few-1e-7 error
-    as at T = 1 before its one rounding to fp32; where |lp| >= 128 an fp32 ulp
-    exceeds 1e-5, and the two roundings (oracle, kernel) may then land one ulp
-    apart.  The bound is 1e-5, plus one ulp of the expected value where
-    |lp| >= 128 (NaN and infinities exactly)."""
-    got = np.asarray(got, np.float32)
-    want = np.asarray(want, np.float32)
-    nan = np.isnan(want)
-    assert np.array_equal(nan, np.isnan(got)), where
-    inf = np.isinf(want)
-    assert np.array_equal(got[inf], want[inf]), where
-    fin = ~nan & ~inf
-    mag = np.abs(want[fin])
-    tol = 1e-5 + np.where(mag >= 128.0, np.spacing(mag), 0.0)
-    d = np.abs(got[fin].astype(np.float64) - want[fin])
-    assert np.all(d <= tol), (where, float(d.max()), float(np.abs(want[fin]).max()))
-
-
 @pytest.mark.parametrize("levels", [3, 5])
 @pytest.mark.parametrize("vocab", [1027, 40001])
 @pytest.mark.parametrize("split", [None, 3, 16])
@@ -209,7 +190,7 @@ def test_temperature(R, levels, vocab, split):
     torch.cuda.synchronize()
     assert np.array_equal(out_off, ref[2])
     assert np.array_equal(ids.cpu().numpy(), ref[1]), "ids"
-    _assert_close_rel(lp.cpu().numpy(), ref[0], f"temperature levels={levels} split={split}")
+    assert_close_rel(lp.cpu().numpy(), ref[0], f"temperature levels={levels} split={split}")
 
 
 @pytest.mark.parametrize("levels", [1, 3, 5, 6])
@@ -235,7 +216,7 @@ def test_top_k_front_end(R, levels, vocab, split):
     torch.cuda.synchronize()
     assert np.array_equal(out_off, ref[2])
     assert np.array_equal(ids.cpu().numpy(), ref[1]), "ids"
-    _assert_close_rel(lp.cpu().numpy(), ref[0], f"top-k levels={levels} split={split}")
+    assert_close_rel(lp.cpu().numpy(), ref[0], f"top-k levels={levels} split={split}")
 
 
 @pytest.mark.parametrize("top_k", [1, 3, 7])
@@ -270,7 +251,7 @@ def test_temperature_decode_shape(R):
                                                         c.sampled, c.top_n, c.echo, temperature=T)
         torch.cuda.synchronize()
         assert np.array_equal(ids.cpu().numpy(), ref[1])
-        _assert_close_rel(lp.cpu().numpy(), ref[0], f"decode T={T}")
+        assert_close_rel(lp.cpu().numpy(), ref[0], f"decode T={T}")
 
 
 def _shard_bounds(vocab, n_shards, rng):
@@ -604,7 +585,7 @@ def test_extreme_values(R, temperature):
                                                           sampled, top_n, echo, temperature=temps)
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ref[1])
-    _assert_close_rel(lp.cpu().numpy(), ref[0], f"extreme values T={temperature}")
+    assert_close_rel(lp.cpu().numpy(), ref[0], f"extreme values T={temperature}")
 
 
 def test_staging_pool_two_threads(R):

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle.logprob_oracle as LO
-from tests.gpu_helpers import assert_parity, log, oracle, run_library, special_rows
+from tests.gpu_helpers import assert_close_rel, assert_parity, log, oracle, run_library, special_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +84,38 @@ def test_random_plan(R, i):
                       c["split"], c["waves"], c["depth"], levels=c["levels"],
                       deterministic=c["deterministic"])
     assert_parity(*got, ref, f"random case {i}")
+
+
+N_OPTION_CASES = 48
+
+
+@pytest.mark.parametrize("i", range(N_OPTION_CASES))
+def test_random_plan_with_options(R, i):
+    """The same draws with per-request temperatures (some 1, some far from
+    it) and top-k front ends (0 = off, up to the heap cap), through the torch
+    front end: ids and offsets bit for bit, logprobs within 1e-5 (plus one
+    ulp where |lp| >= 128, as the temperature tests allow)."""
+    c = _draw_case(1000 + i)
+    rng = np.random.default_rng(5000 + i)
+    batch = len(c["top_n"])
+    cap = LO.max_top_n(c["levels"])
+    temps = rng.choice(np.array([1.0, 0.25, 0.7, 1.0, 1.9, 6.0], np.float32), batch)
+    top_k = rng.integers(0, cap + 1, batch) if cap > 0 else np.zeros(batch, int)
+    top_k[rng.random(batch) < 0.4] = 0
+    echo = c["echo"] if c["has_logits"] else np.zeros_like(c["echo"])
+    log(f"random option case {i}: levels={c['levels']} vocab={c['vocab']} rows={int(c['off'][-1])} "
+        f"shape={(c['waves'], c['depth'], c['split'])} temps={temps.tolist()} top_k={top_k.tolist()}")
+    logits = c["logits"] if c["has_logits"] else None
+    ref = LO.compute_log_probabilities_ragged(c["off"], logits, c["ntl"], c["tokens"], c["sampled"],
+                                              list(c["top_n"]), list(echo), levels=c["levels"],
+                                              batch_temperature=temps, batch_top_k=top_k)
+    dl = torch.from_numpy(c["logits"]).cuda() if c["has_logits"] else None
+    dn = torch.from_numpy(np.ascontiguousarray(c["ntl"])).cuda()
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        c["off"], dl, dn, c["tokens"], c["sampled"], c["top_n"], echo, split=c["split"],
+        waves=c["waves"], depth=c["depth"], levels=c["levels"], temperature=temps, top_k=top_k,
+        deterministic=c["deterministic"])
+    torch.cuda.synchronize()
+    assert np.array_equal(out_off, ref[2]), f"option case {i}: offsets"
+    assert np.array_equal(ids.cpu().numpy(), ref[1]), f"option case {i}: ids"
+    assert_close_rel(lp.cpu().numpy(), ref[0], f"option case {i}")

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     __shared__ uint64_t s_top[kK];
     __shared__ uint64_t s_T;
     __shared__ uint64_t s_pub[kWaves];
-    __shared__ float s_m[kWaves], s_s[kWaves];
+    __shared__ float2 s_lms[kWaves * kWave];   // every lane's (m, s)
     __shared__ float s_ms2[2];
     __shared__ uint32_t s_next;   // next chunk index to hand out (kDyn)
     constexpr bool kBulk = kK >= kBulkMinK;
@@ -1076,35 +1076,37 @@ __global__ __launch_bounds__(kWaves * kWave) void row_kernel(RowArgs a) {
     // us and the 4-row batch (16 waves) 9.0 -> 8.5 us, same box.
     //
     // The workgroup's (M, S) comes from plain reductions instead of pairwise
-    // (m, s) merges (two exponentials each): before the first barrier each
-    // wave takes the maximum of its lanes' m and the sum of their s scaled to
-    // it (one exponential per lane); between the barriers the last wave
-    // combines the waves' pairs the same way.  Between the barriers only the ranking is
+    // (m, s) merges (two exponentials each): before the first barrier every
+    // lane stores its (m, s), and between the barriers the last wave takes
+    // the maximum M of them all and the sum of every s scaled to M (one
+    // exponential per stored pair), while the other waves rank.  Between the barriers only the ranking is
     // left (with the one-pass epilogue of write_row: 520 rows of 32000 15.62
     // -> 15.37 us, decode 22.84 -> 22.74 us, same box).
     if (lane < kK) s_keys[wave * kK + lane] = list;
-    {
-        const float mw = wave_max_f32(m);
-        const float mws = (mw == -INFINITY) ? 0.0f : mw;
-        const float sw = wave_sum_f32(s * fast_exp2((m - mws) * c));   // lanes that saw no finite value: s = 0
-        if (lane == 0) {
-            s_m[wave] = mw;
-            s_s[wave] = sw;
-        }
-    }
+    s_lms[wave * kWave + lane] = make_float2(m, s);
     constexpr int kN = kWaves * kK;
     static_assert(kN <= kThreads, "one key per thread");
     if (wave == 0 && lane < kK) s_top[lane] = 0ull;
     __syncthreads();
-    // The last wave (idle in the ranking at up to 15 slots) combines the
-    // waves' (max, sum) pairs while the others rank, so that wave 0 only
-    // reads the result after the second barrier (decode 22.64 -> 22.53 us,
-    // the 4-row batch 8.13 -> 8.01 us, same box).
+    // The last wave (idle in the ranking at up to 15 slots) reduces the
+    // lanes' pairs while the others rank, so that neither the last wave to
+    // finish its stream nor wave 0 after the second barrier spends time on
+    // them (same box: decode 22.64 -> 22.53 us with the waves' own
+    // reductions still before the barrier, 22.55 -> 22.37 us without them;
+    // the 4-row batch 8.13 -> 8.01 -> 7.61 us).
     if (wave == kWaves - 1) {
-        const float mi = lane < kWaves ? s_m[lane] : -INFINITY;
-        const float M = first_lanes_max_f32<kWaves>(mi);
+        float2 v[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v[w] = s_lms[w * kWave + lane];
+        float ml = v[0].x;
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) ml = fmaxf(ml, v[w].x);
+        const float M = wave_max_f32(ml);
         const float Ms = (M == -INFINITY) ? 0.0f : M;
-        const float S = first_lanes_sum_f32<kWaves>(lane < kWaves ? s_s[lane] * fast_exp2((mi - Ms) * c) : 0.0f);
+        float sl = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sl += v[w].y * fast_exp2((v[w].x - Ms) * c);   // s = 0 where m = -inf
+        const float S = wave_sum_f32(sl);
         if (lane == 0) {
             s_ms2[0] = M;
             s_ms2[1] = S;

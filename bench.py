@@ -19,14 +19,17 @@ the short decode launches.
 
 Beside it, each on the same run:
   compute_ragged  lp_compute_ragged per step: the descriptors built on the
-                  host, uploaded over PCIe, then the launch.  Median, p10 and
-                  p90 of the event intervals on the stream.  This is the
-                  PCIe-inclusive rate; it is never `value`.
+                  host, uploaded over PCIe (or, up to 16384 rows, read by the
+                  kernels from pinned host memory), then the launch.  Median,
+                  p10 and p90 of the event intervals on the stream.  This is
+                  the PCIe-inclusive rate; it is never `value`.
   decode          the decode batch (256 rows of 128256, one boosted token per
                   row, top_n 7), measured the same way with its own roofline
                   fraction.
   probe           a plain streaming read of as many rows of the same width on
-                  the same copies: the practical ceiling for these bytes.
+                  the same copies: the practical ceiling for these bytes;
+                  beside it the fastest shape of the committed 36-shape
+                  sweep (`--probe-sweep`, profiles/probe_sweep_<workload>.txt).
   cpu_baseline    the CPU oracle on the host, run before the GPU is touched:
                   one process, then one process per available core (at most
                   16), each on rows of the same workload drawn on the host.
@@ -35,10 +38,10 @@ Beside it, each on the same run:
                   line reports how many were checked and how many differ.
 
 The headline takes exactly W untimed warmup steps (without --warmup, about
-100 ms of launches: 4000 for decode, 5 for the prefill batch).  Every other leg (the
-decode record, lp_compute_ragged, the probe) keeps launching untimed for at
-least 100 ms first: after an idle spell the first milliseconds of short
-launches run slower than the steady state.
+100 ms of launches: 4000 for decode, 5 for the prefill batch).  Every other
+leg (the decode record, lp_compute_ragged, the probe) keeps launching untimed
+for at least 100 ms first: after an idle spell the first milliseconds of
+short launches run slower than the steady state.
 
 Workloads that fit the 256 MB Infinity Cache are timed while cycling through
 copies of the logits whose read rows total at least 1 GiB.

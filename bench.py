@@ -29,7 +29,8 @@ Beside it, each on the same run:
   probe           a plain streaming read of as many rows of the same width on
                   the same copies: the practical ceiling for these bytes;
                   beside it the fastest shape of the committed 36-shape
-                  sweep (`--probe-sweep`, profiles/probe_sweep_<workload>.txt).
+                  sweep (`--probe-sweep`, profiles/probe_sweep_<workload>.txt),
+                  as recorded there and timed again in this run.
   cpu_baseline    the CPU oracle on the host, run before the GPU is touched:
                   one process, then one process per available core (at most
                   16), each on rows of the same workload drawn on the host.
@@ -461,6 +462,19 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
         if best is not None:
             best["kernel_time_over_best"] = ms_per_step * 1e3 / best["us"]
             rec["probe"]["sweep_best"] = best
+            if "segments" in best:
+                # the sweep's fastest shape, timed again here on this machine
+                segs, thr, loads = best["segments"], best["threads"], best["loads"]
+                partial = torch.empty(read_rows * segs, dtype=torch.float32, device=dev)
+                pl = [R.binding.stream_read_shape_launcher(c, read_rows, case.vocab, segs, thr, loads,
+                                                           partial, stream) for c in copies]
+                _warm(pl, n_copies, 3, SUB_WARM_S, torch)
+                us = _grouped_ms(pl, n_copies, steps, stream, torch) * 1e3
+                gbs = read_bytes / (us * 1e-6) / 1e9
+                rec["probe"]["best_shape_live"] = {
+                    "us": us, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                    "kernel_time_over_best": ms_per_step * 1e3 / us,
+                    "note": "the sweep's fastest plain-read shape, timed in this run"}
     return rec, plan, info, base, lp, ids, ws, copies
 
 
@@ -788,8 +802,13 @@ def stored_probe_best(workload):
         for line in f:
             m = re.match(r"fastest: (.*): ([0-9.]+) us, ([0-9.]+) of 8 TB/s", line.strip())
             if m:
-                return {"us": float(m.group(2)), "frac": float(m.group(3)), "shape": m.group(1),
-                        "source": f"profiles/probe_sweep_{workload}.txt"}
+                shape = re.match(r"(\d+) segment\(s\), (\d+) threads, (\d+) load\(s\) per thread",
+                                 m.group(1))
+                rec = {"us": float(m.group(2)), "frac": float(m.group(3)), "shape": m.group(1),
+                       "source": f"profiles/probe_sweep_{workload}.txt"}
+                if shape:
+                    rec["segments"], rec["threads"], rec["loads"] = (int(g) for g in shape.groups())
+                return rec
     return None
 
 

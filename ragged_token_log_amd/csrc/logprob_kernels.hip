@@ -1385,30 +1385,32 @@ constexpr unsigned kStagingFlags = hipHostMallocMapped | hipHostMallocCoherent;
 
 static std::mutex g_staging_mutex;
 static std::vector<std::unique_ptr<StagingSlot>> g_staging;
-// Slots in flight, in the order their events were recorded.  Work on one
-// stream completes in that order, so a call retires the finished slots from
-// the front with one event query each; querying every slot of the pool on
-// every call (as an earlier version did) cost the host 0.08 us per slot, and
-// a host that runs ahead of the GPU keeps hundreds in flight.
-static std::deque<StagingSlot *> g_inflight;
+// Slots in flight, one queue per (device, stream) in the order their events
+// were recorded.  Work on one stream completes in that order, so a call
+// retires the finished slots from the front of each queue with one event
+// query each, and a queue whose front is busy holds nothing finished; a
+// host that runs ahead of the GPU keeps hundreds of slots in flight, and an
+// event query costs it about 0.06 us.  Should a stream handle be reused by a
+// new stream, its queue may hold a finished slot behind a busy one: that
+// slot is retired later, never early, since every slot is retired on its
+// own event.
+struct InFlight {
+    int device;
+    hipStream_t stream;
+    std::deque<StagingSlot *> slots;
+};
+static std::vector<InFlight> g_inflight;
 
-static void retire_front() {
-    while (!g_inflight.empty() && hipEventQuery(g_inflight.front()->done) == hipSuccess) {
-        g_inflight.front()->in_flight = false;
-        g_inflight.pop_front();
-    }
-}
-
-// Every finished slot, wherever it sits in the queue (streams complete in
-// their own orders): the fallback when the front is still busy.
-static void retire_all() {
-    for (auto it = g_inflight.begin(); it != g_inflight.end();) {
-        if (hipEventQuery((*it)->done) == hipSuccess) {
-            (*it)->in_flight = false;
-            it = g_inflight.erase(it);
-        } else {
-            ++it;
+static void retire_fronts() {
+    for (auto q = g_inflight.begin(); q != g_inflight.end();) {
+        while (!q->slots.empty() && hipEventQuery(q->slots.front()->done) == hipSuccess) {
+            q->slots.front()->in_flight = false;
+            q->slots.pop_front();
         }
+        if (q->slots.empty())
+            q = g_inflight.erase(q);   // streams come and go: keep only busy queues
+        else
+            ++q;
     }
 }
 
@@ -1416,7 +1418,7 @@ static void retire_all() {
 // smaller one grown to `bytes`, or a new one.
 static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) {
     std::lock_guard<std::mutex> lock(g_staging_mutex);
-    retire_front();
+    retire_fronts();
     StagingSlot *fit = nullptr, *small = nullptr;
     auto pick = [&]() {
         fit = small = nullptr;
@@ -1431,10 +1433,6 @@ static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) 
         }
     };
     pick();
-    if (fit == nullptr && !g_inflight.empty()) {
-        retire_all();
-        pick();
-    }
     if (fit == nullptr && small != nullptr) {
         void *h = nullptr;
         LP_HIP_TRY(hipHostMalloc(&h, bytes, kStagingFlags));
@@ -1468,14 +1466,22 @@ static lp_status staging_acquire(uint64_t bytes, int device, StagingSlot **out) 
     return LP_OK;
 }
 
-// Gives a slot back.  `recorded`: its event was recorded after the last
-// work that reads it, so it joins the in-flight queue; otherwise nothing
-// was enqueued on it since it was taken and it is free at once.
-static void staging_release(StagingSlot *sl, bool recorded) {
+// Gives a slot back.  `recorded`: its event was recorded on `stream` after
+// the last work that reads it, so it joins that stream's in-flight queue;
+// otherwise nothing was enqueued on it since it was taken and it is free at
+// once.
+static void staging_release(StagingSlot *sl, bool recorded, hipStream_t stream) {
     std::lock_guard<std::mutex> lock(g_staging_mutex);
     if (recorded) {
         try {
-            g_inflight.push_back(sl);
+            InFlight *q = nullptr;
+            for (auto &f : g_inflight)
+                if (f.device == sl->device && f.stream == stream) q = &f;
+            if (q == nullptr) {
+                g_inflight.push_back(InFlight{sl->device, stream, {}});
+                q = &g_inflight.back();
+            }
+            q->slots.push_back(sl);
         } catch (...) {
             return;   // no room to track it: it stays taken for good
         }
@@ -1671,7 +1677,7 @@ lp_status lp_stage_ragged(const lp_plan *plan, const uint32_t *tokens, const uin
     }
     // recorded exactly when the copy was enqueued (a failed enqueue leaves
     // nothing reading the slot)
-    lp::staging_release(slot, st == LP_OK && e == hipSuccess);
+    lp::staging_release(slot, st == LP_OK && e == hipSuccess, s);
     if (st != LP_OK) return st;
     LP_HIP_TRY(e);
     return LP_OK;
@@ -1789,7 +1795,7 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const floa
     hipError_t e = hipSuccess;
     if (st == LP_OK) e = hipHostGetDevicePointer(&desc, slot->host, 0);
     if (st != LP_OK || e != hipSuccess) {   // nothing enqueued reads the slot
-        lp::staging_release(slot, false);
+        lp::staging_release(slot, false, s);
         if (st != LP_OK) return st;
         LP_HIP_TRY(e);
     }
@@ -1801,7 +1807,7 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const floa
     st = lp::launch_rows(*plan, logits, next_token_logits, out_logprobs, out_token_ids, workspace,
                          desc, s, slot->done);
     if (st == LP_OK) {
-        lp::staging_release(slot, true);
+        lp::staging_release(slot, true, s);
         return LP_OK;
     }
     e = hipEventRecord(slot->done, s);
@@ -1809,7 +1815,7 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits, const floa
         lp::g_last_hip_error = int(e);
         return st != LP_OK ? st : LP_ERR_HIP;
     }
-    lp::staging_release(slot, true);
+    lp::staging_release(slot, true, s);
     return st;
 }
 

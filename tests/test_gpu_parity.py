@@ -963,6 +963,50 @@ def test_staging_slots_reused_across_streams(R):
     long_plan.close()
 
 
+def test_staging_slots_not_refilled_under_queued_kernels(R):
+    """Back-to-back lp_compute_ragged calls on one stream, each with its own
+    sampled tokens and so its own descriptors, enqueued far faster than the
+    GPU runs them (1024 rows of 131072 per call, read in place from the
+    pinned staging slots): a slot is refilled only once the kernel that reads
+    it has ended.  Every queued call's outputs equal those of the same call
+    run alone, bit for bit (deterministic chunk order), and sampled rows of
+    the first and last calls match the oracle."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(4711)
+    B, V, calls = 1024, 131072, 24
+    ntl_host = (rng.standard_normal((B, V), dtype=np.float32) * 2).astype(np.float32)
+    ntl = _dev(ntl_host)
+    off = np.arange(B + 1, dtype=np.uint32)
+    plan = R.Plan(off, np.zeros(B, bool), np.full(B, 7, np.int32), V, False)
+    plan.set_deterministic(True)
+    assert plan.info()["out_rows"] <= 16384          # the in-place descriptor path
+    sampled = [rng.integers(0, V, B).astype(np.uint32) for _ in range(calls)]
+    stream = torch.cuda.current_stream()
+    alone = []
+    for i in range(calls):
+        lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+        plan.compute(None, ntl, None, sampled[i], lp, ids, ws, stream)
+        torch.cuda.synchronize()
+        alone.append((lp.cpu().numpy(), ids.cpu().numpy()))
+    queued = [R.alloc_outputs(plan, dev, torch) for _ in range(calls)]
+    fns = [plan.computer(None, ntl, None, sampled[i], *queued[i], stream) for i in range(calls)]
+    torch.cuda.synchronize()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    for i in range(calls):
+        lp, ids, _ = queued[i]
+        assert np.array_equal(ids.cpu().numpy(), alone[i][1]), f"call {i}: ids"
+        assert np.array_equal(lp.cpu().numpy().view(np.uint32), alone[i][0].view(np.uint32)), \
+            f"call {i}: logprobs"
+    for i in (0, calls - 1):
+        for r in (0, 517, B - 1):
+            want_lp, want_ids = LO.compute_row(ntl_host[r], int(sampled[i][r]), 7, 8)
+            assert np.array_equal(alone[i][1][r], want_ids), (i, r)
+            assert_lp_close(alone[i][0][r], want_lp, f"call {i} row {r}")
+    plan.close()
+
+
 def test_short_or_mistyped_device_buffers_are_refused(R):
     """Device buffers smaller than the plan reads or writes, of the wrong
     element type or not contiguous are refused (LP_ERR_SHAPE) before any

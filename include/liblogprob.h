@@ -270,10 +270,14 @@ lp_status lp_compute_ragged(const lp_plan *plan, const float *logits,
  * levels, about 262000 output rows without a split).  Other arguments as for
  * lp_compute_ragged; `stream` a hipStream_t (NULL = default stream).
  *
- * Because the host array is not pinned, the descriptor copy is synchronous:
- * the call returns after the stream has finished its earlier work and the
- * copy, then enqueues the kernels and does not wait for them.  Calls are
- * serialised by a lock while they build and copy.  Every call on one GPU
+ * Plans of up to 1984 output rows send their descriptors in the arguments
+ * of up to 8 launches of a small copy kernel (248 descriptors each), which
+ * the runtime takes when it enqueues them: the call waits for nothing.
+ * Larger plans copy them from the host array, which is not pinned, so that
+ * copy is synchronous: the call returns after the stream has finished its
+ * earlier work and the copy, then enqueues the kernels and does not wait
+ * for them.  Calls are serialised by a lock while they build and send the
+ * descriptors.  Every call on one GPU
  * shares that GPU's array and leaves its last contents there: calls whose
  * kernels overlap on one GPU (on different streams) race; calls on one
  * stream are ordered.

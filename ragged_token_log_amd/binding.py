@@ -397,7 +397,9 @@ class Plan:
                         out_token_ids, stream=None):
         """lp_compute_ragged_noalloc: the same computation with the library's
         fixed device workspace (at most 4 MiB of workspace; no allocation).
-        Returns after the descriptor copy; the kernels run on ``stream``."""
+        Up to 1984 output rows the descriptors go in launch arguments and the
+        call waits for nothing; larger plans return after a synchronous
+        descriptor copy.  The kernels run on ``stream``."""
         tok, smp = self._token_arrays(tokens, sampled_tokens)
         self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
         _check(self._lib.lp_compute_ragged_noalloc(self._h, _dev_ptr(logits),

@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <deque>
@@ -1272,6 +1273,27 @@ __global__ __launch_bounds__(256) void pad_kernel(float *out_lp, uint32_t *out_i
     }
 }
 
+// Descriptors carried in the launch's own arguments, copied into device
+// memory: the runtime copies kernel arguments when the launch is enqueued,
+// so the host array they came from is free again at once, with no pinned
+// memory and no wait.  248 descriptors and the header make 3984 bytes of
+// arguments, inside the 4 KB that kernel arguments may take; the kernel
+// reads them from the argument segment with one 16-byte load per thread.
+constexpr uint32_t kUploadRows = 248;
+
+struct DescUpload {
+    RowDesc d[kUploadRows];
+    RowDesc *dst;              // the first of `count` descriptors to write
+    uint32_t count;            // 1..kUploadRows
+    uint32_t pad;
+};
+static_assert(sizeof(DescUpload) <= 4096, "kernel arguments are limited to 4 KB");
+
+__global__ __launch_bounds__(256) void desc_upload_kernel(const DescUpload u) {
+    const uint32_t t = threadIdx.x;
+    if (t < u.count) u.dst[t] = u.d[t];
+}
+
 // ------------------------------------------------------------------ streaming-read probe
 
 // One workgroup of 8 waves per row of row_len floats (16-byte aligned rows),
@@ -1610,12 +1632,18 @@ static lp_status check_workspace(const lp_plan *plan, const void *ws, uint64_t w
 // For callers that cannot allocate: the workspace (descriptors, then split
 // records) lives in a fixed device array of kNoAllocScratchBytes, `scratch`
 // below, one copy per GPU the library runs on; the descriptors are built in a
-// fixed host array of the same size and copied from there.  In host code the
+// fixed host array of the same size and sent from there, in the arguments of
+// upload launches for plans of up to kMaxUploadLaunches of them, else by a
+// synchronous copy.  In host code the
 // array's name is only a stand-in: its device address comes from
 // hipGetSymbolAddress, asked once per device with that device current, and is
 // what the kernels and the copy receive.
 constexpr uint64_t kNoAllocScratchBytes = 4ull << 20;
 constexpr int kMaxDevices = 64;
+// Plans of up to this many launches of dev::desc_upload_kernel (1984 rows)
+// send their descriptors in kernel arguments; larger ones copy them from
+// the host array synchronously.
+constexpr uint64_t kMaxUploadLaunches = 8;
 
 static std::mutex g_noalloc_mutex;                 // guards both arrays below
 static void *g_scratch_dev[kMaxDevices] = {};      // device address of `scratch`, per device
@@ -1838,11 +1866,27 @@ lp_status lp_compute_ragged_noalloc(const lp_plan *plan, const float *logits,
         if (st != LP_OK) return st;
         st = lp::build_descriptors(*plan, tokens, sampled_tokens, lp::g_noalloc_desc);
         if (st != LP_OK) return st;
-        // the host array is not pinned: the copy is synchronous, and the
-        // stream is drained before the array may be refilled
-        LP_HIP_TRY(hipMemcpyWithStream(ws, lp::g_noalloc_desc, plan->out_rows * sizeof(lp::RowDesc),
-                                       hipMemcpyHostToDevice, s));
-        LP_HIP_TRY(hipStreamSynchronize(s));
+        if (plan->out_rows <= uint64_t(lp::dev::kUploadRows) * lp::kMaxUploadLaunches) {
+            // up to 248 descriptors per launch, carried in its arguments:
+            // nothing waits, and the host array may be refilled at once
+            lp::dev::DescUpload u;
+            std::memset(&u, 0, sizeof(u));
+            for (uint64_t first = 0; first < plan->out_rows; first += lp::dev::kUploadRows) {
+                const uint64_t n = std::min<uint64_t>(lp::dev::kUploadRows, plan->out_rows - first);
+                std::memcpy(u.d, lp::g_noalloc_desc + first, n * sizeof(lp::RowDesc));
+                u.dst = static_cast<lp::RowDesc *>(ws) + first;
+                u.count = static_cast<uint32_t>(n);
+                hipLaunchKernelGGL(lp::dev::desc_upload_kernel, dim3(1), dim3(256), 0, s, u);
+                LP_HIP_TRY(hipGetLastError());
+            }
+        } else {
+            // the host array is not pinned: the copy is synchronous, and the
+            // stream is drained before the array may be refilled
+            LP_HIP_TRY(hipMemcpyWithStream(ws, lp::g_noalloc_desc,
+                                           plan->out_rows * sizeof(lp::RowDesc),
+                                           hipMemcpyHostToDevice, s));
+            LP_HIP_TRY(hipStreamSynchronize(s));
+        }
     }
     return lp_launch_ragged(plan, logits, next_token_logits, out_logprobs, out_token_ids, ws,
                             lp::kNoAllocScratchBytes, stream);

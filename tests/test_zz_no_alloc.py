@@ -2,7 +2,10 @@
 allocation) against lp_compute_ragged on the same inputs, through the C ABI:
 two calls in a row, the second on a smaller batch, then a third of another
 shape; ids bit for bit, log-probabilities within 1e-5, and both against the
-oracle."""
+oracle.  Plans of up to 1984 output rows send their descriptors in the
+arguments of up to 8 upload launches (248 each) and do not wait; larger ones
+copy them synchronously: both sides of that limit, and the waiting, are
+checked."""
 import numpy as np
 import pytest
 
@@ -86,3 +89,51 @@ def test_noalloc_refuses_plans_beyond_its_workspace(R):
     with pytest.raises(R.LogprobError) as e:
         plan.compute_noalloc(logits, logits[:1], np.zeros(n, np.uint32), [0], lp, ids)
     assert e.value.name == "LP_ERR_WORKSPACE"
+
+
+def _next_token_case(rows, vocab, seed):
+    """`rows` one-row requests over next-token logits only (no echo)."""
+    c = gen.decode_peaked(seed=seed, batch=rows, vocab=vocab)
+    c.top_n = np.random.default_rng(seed).integers(0, 8, rows).astype(np.int32)
+    return c
+
+
+@pytest.mark.parametrize("rows", [248, 249, 700, 1984, 1985])
+def test_noalloc_upload_launch_counts(R, rows):
+    """One launch of descriptors (248 rows), one more row (two launches),
+    three with a short last one (700), the most sent in launch arguments
+    (1984 = 8 x 248) and one past it (1985: the synchronous copy)."""
+    _check(R, _next_token_case(rows, 3001, 60 + rows), f"{rows} rows")
+
+
+def test_noalloc_waits_only_past_the_launch_argument_limit(R):
+    """With about 12 ms of reads queued ahead on the stream, a call of 1984
+    rows returns before they end (its descriptors travel in launch
+    arguments); a call of 1985 rows copies them synchronously and returns
+    only after the stream has drained.  Both results match lp_compute_ragged."""
+    stream = torch.cuda.current_stream()
+    x = torch.zeros(8192 * 131072, dtype=torch.float32, device="cuda")    # 4 GiB
+    partial = torch.empty(8192, dtype=torch.float32, device="cuda")
+    read = R.binding.stream_read_launcher(x, 8192, 131072, partial, stream)
+    for rows, waits in ((1984, False), (1985, True)):
+        case = _next_token_case(rows, 2003, 90 + rows)
+        ntl = _dev(gen.next_token_rows(case, gen.host_logits(case)))
+        plan = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, False)
+        lp1, ids1, ws = R.alloc_outputs(plan, ntl.device, torch)
+        plan.compute(None, ntl, None, case.sampled, lp1, ids1, ws, stream)
+        lp2 = torch.full_like(lp1, float("nan"))
+        ids2 = torch.full_like(ids1, 0xAAAAAAAA)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            read()
+        ahead = torch.cuda.Event()
+        ahead.record(stream)
+        plan.compute_noalloc(None, ntl, None, case.sampled, lp2, ids2, stream)
+        drained = ahead.query()
+        torch.cuda.synchronize()
+        log(f"{rows} rows: the queued reads had ended when the call returned: {drained}")
+        assert drained == waits, rows
+        assert np.array_equal(ids2.cpu().numpy(), ids1.cpu().numpy()), rows
+        assert_parity(lp2.cpu().numpy(), ids2.cpu().numpy(), plan.out_off,
+                      (lp1.cpu().numpy(), ids1.cpu().numpy(), plan.out_off), f"{rows} rows")
+        plan.close()

@@ -235,6 +235,11 @@ lp_status lp_stage_ragged(const lp_plan *plan, const uint32_t *tokens,
  * synchronisation.  Launches that share a workspace must be ordered (same
  * stream): split launches keep partial results there.  Device buffers must stay alive
  * until the stream reaches the end of the enqueued work.
+ *
+ * It enqueues kernels and nothing else (no copy, no memset, no event), so it
+ * may be captured into a HIP graph: the kernels read the logits and the
+ * descriptors at replay time, so a caller stages each step's descriptors
+ * with lp_stage_ragged (outside the graph, on the replay stream) and replays.
  */
 lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
                            const float *next_token_logits, float *out_logprobs,

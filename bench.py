@@ -19,7 +19,7 @@ the short decode launches.
 
 Beside it, each on the same run:
   compute_ragged  lp_compute_ragged per step: the descriptors built on the
-                  host, uploaded over PCIe (or, up to 16384 rows, read by the
+                  host, uploaded over PCIe (or, up to 262144 rows, read by the
                   kernels from pinned host memory), then the launch.  Median,
                   p10 and p90 of the event intervals on the stream.  This is
                   the PCIe-inclusive rate; it is never `value`.
@@ -439,7 +439,7 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
     rec["frac"] = rec["gbs"] / HBM_PEAK_GBS
     if extras:
         # lp_compute_ragged per step: host descriptors, their upload (or, up
-        # to 16384 rows, the kernels' reads of them in pinned host memory),
+        # to 262144 rows, the kernels' reads of them in pinned host memory),
         # the launch
         comp = [plan.computer(*srcs(c), case.tokens, case.sampled, lp, ids, ws, stream)
                 for c in copies]
@@ -449,7 +449,7 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
         rec["compute_ragged"] = dict(cs, rows_per_s=read_rows / (cs["median_us"] * 1e-6),
                                      gbs=alg / (cs["median_us"] * 1e-6) / 1e9,
                                      note="lp_compute_ragged per step (host descriptor build, "
-                                          "upload or, up to 16384 rows, reads from pinned host "
+                                          "upload or, up to 262144 rows, reads from pinned host "
                                           "memory, launch); event interval on the stream")
         # leave the resident descriptors in place for the parity check
         plan.stage(case.tokens, case.sampled, ws, stream)

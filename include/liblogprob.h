@@ -249,7 +249,7 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
 /*
  * lp_compute_ragged -- the descriptors of this call, then the kernels: the
  * results of lp_stage_ragged followed by lp_launch_ragged, with the same
- * arguments and errors.  For plans of at most 16384 output rows the kernels
+ * arguments and errors.  For plans of at most 262144 output rows the kernels
  * read the descriptors straight from the library's pinned host staging
  * memory and no copy precedes them; the workspace then holds only split
  * records, and its descriptor area is left unwritten (a later

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 96
+N_CASES = 1000
 
 
 @pytest.fixture(scope="module")
@@ -86,7 +86,7 @@ def test_random_plan(R, i):
     assert_parity(*got, ref, f"random case {i}")
 
 
-N_OPTION_CASES = 48
+N_OPTION_CASES = 400
 
 
 @pytest.mark.parametrize("i", range(N_OPTION_CASES))

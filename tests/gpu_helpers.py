@@ -27,6 +27,42 @@ class DeviceRows:
         return self.t[int(r)].cpu().numpy()
 
 
+def shard_bounds(vocab, n_shards, rng):
+    """Uneven vocabulary ranges covering [0, vocab) once each."""
+    cuts = sorted(rng.choice(np.arange(1, vocab), size=n_shards - 1, replace=False).tolist())
+    b = [0] + cuts + [vocab]
+    return list(zip(b[:-1], b[1:]))
+
+
+def run_sharded(R, torch, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds,
+                top_k=None):
+    """The batch through the vocabulary-shard path: each shard's columns (as
+    their own contiguous device arrays) to lp_shard_records, the records
+    stacked, then lp_merge_shards; returns host (lp, ids, out_off)."""
+    dev = torch.device("cuda")
+    has_logits = logits is not None
+    plan = R.Plan(off, echo, top_n, ntl.shape[1], has_logits, levels=levels)
+    if top_k is not None:
+        plan.set_top_k(top_k)
+    words = plan.info()["record_words"]
+    lp, ids, ws = R.alloc_outputs(plan, dev, torch)
+    stream = torch.cuda.current_stream()
+    plan.stage(tokens, sampled, ws, stream)
+    records = torch.zeros((len(bounds), plan.out_rows, words), dtype=torch.int64, device=dev)
+
+    def cols(x, b, e):
+        return torch.from_numpy(np.ascontiguousarray(x[:, b:e])).cuda()
+
+    for k, (b, e) in enumerate(bounds):
+        sl = cols(logits, b, e) if has_logits else None
+        plan.shard_records(b, sl, cols(ntl, b, e), records[k], ws, stream)
+    plan.merge_shards(len(bounds), records, lp, ids, ws, stream)
+    torch.cuda.synchronize()
+    out = lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off.copy()
+    plan.close()
+    return out
+
+
 def run_library(R, torch, offsets, logits, ntl, tokens, sampled, top_n, echo, split=None,
                 waves=None, depth=None, levels=3, deterministic=False):
     lp, ids, out_off = R.compute_log_probabilities_ragged(

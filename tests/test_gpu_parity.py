@@ -12,7 +12,7 @@ import gen
 import oracle.logprob_oracle as LO
 from tests.gpu_helpers import (DeviceRows, assert_close_rel, assert_lp_close, assert_parity,
                                check_all_rows_properties,
-                               log, oracle, run_library)
+                               log, oracle, run_library, run_sharded, shard_bounds)
 from tests.gpu_helpers import special_rows as _special_rows
 
 pytestmark = pytest.mark.gpu
@@ -254,33 +254,9 @@ def test_temperature_decode_shape(R):
         assert_close_rel(lp.cpu().numpy(), ref[0], f"decode T={T}")
 
 
-def _shard_bounds(vocab, n_shards, rng):
-    """Uneven vocabulary ranges covering [0, vocab) once each."""
-    cuts = sorted(rng.choice(np.arange(1, vocab), size=n_shards - 1, replace=False).tolist())
-    b = [0] + cuts + [vocab]
-    return list(zip(b[:-1], b[1:]))
-
-
 def _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds, top_k=None):
-    dev = torch.device("cuda")
-    has_logits = logits is not None
-    plan = R.Plan(off, echo, top_n, ntl.shape[1], has_logits, levels=levels)
-    if top_k is not None:
-        plan.set_top_k(top_k)
-    words = plan.info()["record_words"]
-    lp, ids, ws = R.alloc_outputs(plan, dev, torch)
-    stream = torch.cuda.current_stream()
-    plan.stage(tokens, sampled, ws, stream)
-    records = torch.zeros((len(bounds), plan.out_rows, words), dtype=torch.int64, device=dev)
-    for k, (b, e) in enumerate(bounds):
-        sl = _dev(logits[:, b:e]) if has_logits else None
-        sn = _dev(ntl[:, b:e])
-        plan.shard_records(b, sl, sn, records[k], ws, stream)
-    plan.merge_shards(len(bounds), records, lp, ids, ws, stream)
-    torch.cuda.synchronize()
-    out = lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off.copy()
-    plan.close()
-    return out
+    return run_sharded(R, torch, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds,
+                       top_k)
 
 
 @pytest.mark.parametrize("levels", [1, 3, 5])
@@ -291,7 +267,7 @@ def test_vocab_shards(R, levels, n_shards):
     vocab = 40001
     off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(11 * n_shards + levels, vocab,
                                                                    levels)
-    bounds = _shard_bounds(vocab, n_shards, np.random.default_rng(n_shards))
+    bounds = shard_bounds(vocab, n_shards, np.random.default_rng(n_shards))
     log(f"vocab shards levels={levels} shards={bounds}")
     ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
     got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds)
@@ -307,7 +283,7 @@ def test_vocab_shards_edges(R, vocab, n_shards, levels):
     """Shards narrower than one 16-byte load, one shard per id, 64 shards,
     the deepest heap with fewer ids than slots."""
     off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(vocab + n_shards, vocab, levels)
-    bounds = _shard_bounds(vocab, n_shards, np.random.default_rng(vocab))
+    bounds = shard_bounds(vocab, n_shards, np.random.default_rng(vocab))
     log(f"shard edges vocab={vocab} shards={n_shards} levels={levels}")
     ref = oracle(off, logits, ntl, tokens, sampled, top_n, echo, levels=levels)
     got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds)
@@ -321,7 +297,7 @@ def test_vocab_shards_top_k(R, levels):
     off, logits, ntl, tokens, sampled, top_n, echo = _levels_batch(41 + levels, vocab, levels)
     cap = LO.max_top_n(levels)
     top_k = np.array([1, cap, 2, 0, cap // 2, 3])[: len(top_n)]
-    bounds = _shard_bounds(vocab, 4, np.random.default_rng(levels))
+    bounds = shard_bounds(vocab, 4, np.random.default_rng(levels))
     ref = LO.compute_log_probabilities_ragged(off, logits, ntl, tokens, sampled, list(top_n),
                                               list(echo), levels=levels, batch_top_k=top_k)
     got = _run_sharded(R, off, logits, ntl, tokens, sampled, top_n, echo, levels, bounds, top_k)

@@ -7,13 +7,16 @@ token), and, for some cases, a forced kernel shape (waves, depth, segments)
 or the deterministic chunk order.  Ids and offsets must match the oracle bit
 for bit and logprobs within 1e-5.  The draws cover the paths a fixed grid can
 miss: large-K bulk merges with keys still pending at a wave's end, seeds over
-two chunks, segments of a few elements, rows shorter than one chunk.
+two chunks, segments of a few elements, rows shorter than one chunk.  The
+same draws also go through the options (temperatures, top-k front ends) and
+through the vocabulary-shard path (records per shard, then the merge).
 """
 import numpy as np
 import pytest
 
 import oracle.logprob_oracle as LO
-from tests.gpu_helpers import assert_close_rel, assert_parity, log, oracle, run_library, special_rows
+from tests.gpu_helpers import (assert_close_rel, assert_parity, log, oracle, run_library,
+                               run_sharded, shard_bounds, special_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +122,33 @@ def test_random_plan_with_options(R, i):
     assert np.array_equal(out_off, ref[2]), f"option case {i}: offsets"
     assert np.array_equal(ids.cpu().numpy(), ref[1]), f"option case {i}: ids"
     assert_close_rel(lp.cpu().numpy(), ref[0], f"option case {i}")
+
+
+N_SHARD_CASES = 200
+
+
+@pytest.mark.parametrize("i", range(N_SHARD_CASES))
+def test_random_plan_through_vocab_shards(R, i):
+    """The same draws through the vocabulary-shard path: 1 to 16 uneven
+    shards (as many as the merge takes at the draw's heap depth), records
+    per shard, then the merge, some with a top-k front end: ids and offsets
+    bit for bit, logprobs within 1e-5 (plus one ulp where |lp| >= 128)."""
+    c = _draw_case(2000 + i)
+    rng = np.random.default_rng(7000 + i)
+    echo = c["echo"] if c["has_logits"] else np.zeros_like(c["echo"])
+    logits = c["logits"] if c["has_logits"] else None
+    cap = LO.max_top_n(c["levels"])
+    most = min(64, 1024 // max(cap, 1), c["vocab"])
+    n = int(rng.integers(1, min(most, 16) + 1))
+    bounds = shard_bounds(c["vocab"], n, rng) if n > 1 else [(0, c["vocab"])]
+    top_k = rng.integers(0, cap + 1, len(c["top_n"])) if cap > 0 and rng.random() < 0.4 else None
+    log(f"random shard case {i}: levels={c['levels']} vocab={c['vocab']} rows={int(c['off'][-1])} "
+        f"shards={len(bounds)} top_k={top_k is not None}")
+    ref = LO.compute_log_probabilities_ragged(c["off"], logits, c["ntl"], c["tokens"], c["sampled"],
+                                              list(c["top_n"]), list(echo), levels=c["levels"],
+                                              batch_top_k=top_k)
+    got = run_sharded(R, torch, c["off"], logits, c["ntl"], c["tokens"], c["sampled"], c["top_n"],
+                      echo, c["levels"], bounds, top_k)
+    assert np.array_equal(got[2], ref[2]), f"shard case {i}: offsets"
+    assert np.array_equal(got[1], ref[1]), f"shard case {i}: ids"
+    assert_close_rel(got[0], ref[0], f"shard case {i}")

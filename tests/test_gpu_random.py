@@ -152,3 +152,32 @@ def test_random_plan_through_vocab_shards(R, i):
     assert np.array_equal(got[2], ref[2]), f"shard case {i}: offsets"
     assert np.array_equal(got[1], ref[1]), f"shard case {i}: ids"
     assert_close_rel(got[0], ref[0], f"shard case {i}")
+
+
+N_STAGED_CASES = 100
+
+
+@pytest.mark.parametrize("i", range(N_STAGED_CASES))
+def test_random_plan_staged_then_launched(R, i):
+    """The same draws through lp_stage_ragged (descriptors uploaded into the
+    workspace) and lp_launch_ragged, the path a caller takes to keep
+    descriptors resident or to capture the launch: against the oracle."""
+    c = _draw_case(3000 + i)
+    echo = c["echo"] if c["has_logits"] else np.zeros_like(c["echo"])
+    logits = c["logits"] if c["has_logits"] else None
+    ref = oracle(c["off"], logits, c["ntl"], c["tokens"], c["sampled"], c["top_n"], echo,
+                 levels=c["levels"])
+    plan = R.Plan(c["off"], echo, c["top_n"], c["vocab"], c["has_logits"], levels=c["levels"])
+    if c["split"]:
+        plan.set_split(c["split"])
+        plan.set_waves(c["waves"])
+        plan.set_depth(c["depth"])
+    plan.set_deterministic(c["deterministic"])
+    dl = torch.from_numpy(c["logits"]).cuda() if c["has_logits"] else None
+    dn = torch.from_numpy(np.ascontiguousarray(c["ntl"])).cuda()
+    lp, ids, ws = R.alloc_outputs(plan, dn.device, torch)
+    plan.stage(c["tokens"], c["sampled"], ws)
+    plan.launch(dl, dn, lp, ids, ws)
+    torch.cuda.synchronize()
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, ref, f"staged case {i}")
+    plan.close()

@@ -137,3 +137,32 @@ def test_noalloc_waits_only_past_the_launch_argument_limit(R):
         assert_parity(lp2.cpu().numpy(), ids2.cpu().numpy(), plan.out_off,
                       (lp1.cpu().numpy(), ids1.cpu().numpy(), plan.out_off), f"{rows} rows")
         plan.close()
+
+
+@pytest.mark.parametrize("i", range(100))
+def test_noalloc_random_plans(R, i):
+    """Seeded random plans (row widths from a few entries to past 128K,
+    degenerate rows, heap depths 0-6, forced shapes and splits) through the
+    no-allocation entry point, one after another on the same fixed
+    workspace: against the oracle."""
+    from tests.test_gpu_random import _draw_case
+
+    c = _draw_case(4000 + i)
+    echo = c["echo"] if c["has_logits"] else np.zeros_like(c["echo"])
+    logits = c["logits"] if c["has_logits"] else None
+    ref = oracle(c["off"], logits, c["ntl"], c["tokens"], c["sampled"], c["top_n"], echo,
+                 levels=c["levels"])
+    plan = R.Plan(c["off"], echo, c["top_n"], c["vocab"], c["has_logits"], levels=c["levels"])
+    if c["split"]:
+        plan.set_split(c["split"])
+        plan.set_waves(c["waves"])
+        plan.set_depth(c["depth"])
+    plan.set_deterministic(c["deterministic"])
+    dl = _dev(c["logits"]) if c["has_logits"] else None
+    dn = _dev(c["ntl"])
+    lp = torch.full((plan.out_rows, plan.columns), float("nan"), device="cuda")
+    ids = torch.full((plan.out_rows, plan.columns), 0xAAAAAAAA, dtype=torch.uint32, device="cuda")
+    plan.compute_noalloc(dl, dn, c["tokens"], c["sampled"], lp, ids)
+    torch.cuda.synchronize()
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, ref, f"noalloc random {i}")
+    plan.close()

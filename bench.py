@@ -47,11 +47,17 @@ short launches run slower than the steady state.
 Workloads that fit the 256 MB Infinity Cache are timed while cycling through
 copies of the logits whose read rows total at least 1 GiB.
 
-Prints one JSON line (N = 1; more GPUs are not supported by this build).
+Prints one JSON line (N = 1: the benchmark drives one GPU).
 
     python bench.py --cpu-full
 times the oracle on every workload in full on the host (all cores) and
 prints one JSON line per workload.
+
+    python bench.py --workload W --write-profile TRACE_DIR FETCH_DIR WRITE_DIR
+    python bench.py --workload W --write-counter-table NAME DIR [DIR ...]
+    python bench.py --write-default-trace TRACE_DIR BENCH_LOG
+write the committed summaries under profiles/ from rocprofv3 csv output
+(each summary names the rocprofv3 command that made it).
 """
 from __future__ import annotations
 
@@ -582,12 +588,18 @@ def main():
     ap.add_argument("--write-counter-table", nargs="+", metavar="ARG",
                     help="NAME DIR [DIR ...]: write profiles/NAME.txt, the per-dispatch mean of "
                          "every counter in these rocprofv3 --pmc runs of this workload, per kernel")
+    ap.add_argument("--write-default-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="write profiles/bench_default_trace.txt from a kernel-trace run of the "
+                         "default bench line and that run's output")
     ap.add_argument("--write-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/row_kernel_<workload>_{trace,counters}.txt from a "
                          "kernel-trace run and FETCH_SIZE / WRITE_SIZE runs of this workload")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.write_default_trace:
+        write_default_trace(*args.write_default_trace)
         return
     if args.write_profile:
         write_profile(args.workload, *args.write_profile, split=args.split, waves=args.waves)
@@ -596,9 +608,9 @@ def main():
         write_counter_table(args.workload, args.write_counter_table[0], args.write_counter_table[1:])
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU per process; --gpus must be 1 "
-                                   "(rows shard across GPUs with no exchange, but the "
-                                   "multi-GPU path is not built)", "n_gpus": args.gpus}),
+        print(json.dumps({"error": "the benchmark drives one GPU; --gpus must be 1 (rows "
+                                   "shard across GPUs with no exchange, but no multi-GPU "
+                                   "path is provided)", "n_gpus": args.gpus}),
               flush=True)
         sys.exit(2)
 
@@ -905,6 +917,47 @@ def write_profile(workload, trace_dir, fetch_dir, write_dir, split=None, waves=N
         f.write(f"algorithmic_bytes_per_launch: {alg}\n")
         f.write(f"traffic_over_algorithmic: {traffic / alg:.4f}\n")
     print(f"wrote profiles for {workload}: traffic/algorithmic = {traffic / alg:.4f}")
+
+
+def write_default_trace(trace_dir, bench_log):
+    """profiles/bench_default_trace.txt: the kernel-trace statistics of one
+    rocprofv3 run of the default bench line (`bench.py` with no flags) and
+    that run's JSON line, the row kernel of each workload matched by its
+    shape (slot count, waves, depth) as the line reports it."""
+    with open(bench_log, encoding="utf-8") as f:
+        line = [x for x in f if x.startswith("{")][-1]
+    d = json.loads(line)
+    legs = [("prefill_echo_large", d["config"], d["roofline"]["algorithmic_bytes_per_launch"]),
+            ("decode_peaked", d["decode"], d["decode"]["algorithmic_bytes_per_launch"])]
+    out = ["rocprofv3 kernel trace of the default bench line (prefill_echo_large, with the "
+           "decode_peaked sub-record)",
+           "command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o default "
+           "-- python3 bench.py",
+           f"kernel_source_sha256: {kernel_source_hash()}"]
+    for r in _kernel_rows(trace_dir, "kernel_stats.csv"):
+        name = r["Name"]
+        if not any(t in name for t in ("row_kernel", "stream_read_kernel", "merge_kernel")):
+            continue
+        avg = float(r["AverageNs"])
+        out.append(f"kernel: {name}")
+        out.append(f"  calls={r['Calls']} avg_ns={avg:.0f} min_ns={r['MinNs']} max_ns={r['MaxNs']}")
+        for wl, cfg, alg in legs:
+            k = (1 << int(cfg["levels"])) - 1
+            if f"row_kernel<{k}, {int(cfg['waves'])}, {int(cfg['depth'])}," in name:
+                out.append(f"  workload {wl}: algorithmic_bytes_per_launch={alg}  GB/s at avg = "
+                           f"{alg / avg:.1f}  fraction of 8 TB/s = {alg / avg / HBM_PEAK_GBS:.4f}")
+                break
+        else:
+            if "stream_read_kernel" in name:
+                out.append("  (the plain-read probe over both workloads' rows: calls of both "
+                           "sizes averaged together)")
+    out.append(f"bench line of the same run: headline avg_launch_us = "
+               f"{d['roofline']['avg_launch_us']:.1f} (frac {d['roofline']['frac']:.4f}); decode "
+               f"ms_per_step = {d['decode']['ms_per_step'] * 1e3:.2f} us (frac "
+               f"{d['decode']['frac']:.4f})")
+    with open(os.path.join(PROFILES, "bench_default_trace.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def write_counter_table(workload, name, dirs):

@@ -254,11 +254,12 @@ lp_status lp_launch_ragged(const lp_plan *plan, const float *logits,
  * memory and no copy precedes them; the workspace then holds only split
  * records, and its descriptor area is left unwritten (a later
  * lp_launch_ragged on this workspace needs its own lp_stage_ragged).
- * Larger plans stage into the workspace as lp_stage_ragged does.  Either
- * way the staging buffer goes back to the pool once the call's last kernel
- * has ended (an event recorded by that kernel's launch), so in the steady
- * state the call neither allocates nor waits; since it records events, it
- * is not meant to be captured into a HIP graph (lp_launch_ragged is).
+ * Larger plans stage into the workspace as lp_stage_ragged does.  The
+ * staging buffer goes back to the pool once what reads it has ended: the
+ * call's last kernel (an event recorded by that kernel's launch) when read
+ * in place, else the copy.  In the steady state the call neither allocates
+ * nor waits; since it records events, it is not meant to be captured into
+ * a HIP graph (lp_launch_ragged is).
  */
 lp_status lp_compute_ragged(const lp_plan *plan, const float *logits,
                             const float *next_token_logits, const uint32_t *tokens,

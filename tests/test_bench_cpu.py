@@ -1,7 +1,8 @@
 """Host logic of bench.py (no GPU): the algorithmic bytes it prices a launch
 at, the kernel-source hash that ties stored counters to the kernels, the
 lookups of stored traffic and of the plain-read sweep's fastest shape, the
-writer of the default-trace summary, and the one-GPU refusal.  Fixture files
+writers of the profile summaries (traffic scaled by the copy probe), and the
+one-GPU refusal.  Fixture files
 are written to a temporary directory, so the committed profiles are only
 read, never changed."""
 import json
@@ -129,3 +130,41 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     d = json.loads(r.stdout.strip().splitlines()[-1])
     assert d["n_gpus"] == 2 and "one GPU" in d["error"]
+
+
+def test_write_profile_scales_counters_by_the_copy_probe(tmp_path, monkeypatch):
+    """Traffic = the row kernel's FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, averaged) each scaled by 256 MiB over what the same counter
+    read for the 256 MiB device copy; the summaries carry the source hash,
+    the plan's shape and the algorithmic bytes that stored_traffic checks."""
+    import ragged_token_log_amd as R
+
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    wl = "ragged_echo_mix"
+    kname = "void lp::dev::row_kernel<7, 8, 1, false, true>(lp::dev::RowArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    dirs = {}
+    for d, (kvals, cval) in {"fetch": ((32000.0, 33000.0), 131072.0),
+                             "write": ((40.0, 44.0), 262144.0)}.items():
+        p = tmp_path / d
+        p.mkdir()
+        rows = [f'"{kname}","{d.upper()}_SIZE",{v}' for v in kvals] + [f'"{copy}","X",{cval}']
+        (p / f"{d}_counter_collection.csv").write_text(
+            '"Kernel_Name","Counter_Name","Counter_Value"\n' + "\n".join(rows) + "\n",
+            encoding="utf-8")
+        dirs[d] = str(p)
+    t = tmp_path / "trace"
+    t.mkdir()
+    (t / "trace_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        f'"{kname}",200,1,15000,60,14000,17000,0\n', encoding="utf-8")
+    bench.write_profile(wl, str(t), dirs["fetch"], dirs["write"])
+    case = gen.WORKLOADS[wl]()
+    info = R.Plan(case.offsets, case.echo, case.top_n, case.vocab, case.has_logits).info()
+    alg = bench.algorithmic_bytes(info, case.vocab)
+    want = 32500.0 * 1024 * (bench.COPY_PROBE_BYTES / (131072.0 * 1024)) + \
+        42.0 * 1024 * (bench.COPY_PROBE_BYTES / (262144.0 * 1024))
+    assert bench.stored_traffic(wl, info, alg) == pytest.approx(round(want), abs=1)
+    text = (tmp_path / "profiles" / f"row_kernel_{wl}_trace.txt").read_text(encoding="utf-8")
+    assert f"algorithmic GB/s at avg = {alg / 15000:.1f}" in text

@@ -601,6 +601,46 @@ def test_staging_pool_two_threads(R):
     assert not errors, errors[0]
 
 
+def test_one_plan_shared_by_two_threads(R):
+    """Read-only calls on one plan may overlap: two host threads compute with
+    the same plan at once, each on its own stream with its own outputs and
+    workspace and its own sampled tokens, 25 calls each; every result
+    matches the oracle for that thread's tokens."""
+    import threading
+
+    off, logits, ntl, tokens, sampled0, top_n, echo = _levels_batch(808, 7001, 3,
+                                                                    rows_per_req=(3, 1, 4, 2))
+    rng = np.random.default_rng(809)
+    sampled = [sampled0, rng.integers(0, ntl.shape[1], len(sampled0)).astype(np.uint32)]
+    refs = [oracle(off, logits, ntl, tokens, sampled[k], top_n, echo) for k in range(2)]
+    plan = R.Plan(off, echo, top_n, ntl.shape[1], True)
+    dl, dn = _dev(logits), _dev(ntl)
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(k):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                lp, ids, ws = R.alloc_outputs(plan, dl.device, torch)
+                for it in range(25):
+                    plan.compute(dl, dn, tokens, sampled[k], lp, ids, ws, stream)
+                    stream.synchronize()
+                    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, refs[k],
+                                  f"thread {k} call {it}")
+        except Exception as e:          # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    assert not any(t.is_alive() for t in threads), "a worker did not finish"
+    assert not errors, errors[0]
+    plan.close()
+
+
 @pytest.mark.parametrize("direct", [False, True])
 def test_deterministic_and_split_independent(R, direct):
     """With lp_plan_set_deterministic the outputs repeat bit for bit; by

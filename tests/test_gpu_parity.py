@@ -390,11 +390,11 @@ def _full_size(R, c, n_sample, seed):
 
 
 def test_prefill_echo_large_full_size(R):
-    _full_size(R, gen.prefill_echo_large(), 40, 41)
+    _full_size(R, gen.prefill_echo_large(), 600, 41)
 
 
 def test_tie_edge_stress_full_size(R):
-    _full_size(R, gen.tie_edge_stress(), 60, 51)
+    _full_size(R, gen.tie_edge_stress(), 400, 51)
 
 
 _BEYOND_2P24 = {}

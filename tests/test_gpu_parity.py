@@ -389,6 +389,37 @@ def _full_size(R, c, n_sample, seed):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("levels", [5, 6])
+@pytest.mark.parametrize("name,n_sample", [("decode_peaked", 256), ("ragged_echo_mix", 520),
+                                           ("tie_edge_stress", 200)])
+def test_full_size_at_large_k(R, name, n_sample, levels):
+    """The named workloads at full size with every read request asking for
+    all 31 or 63 ranked slots (bulk merges, the published bound, the
+    two-buffer stream at 16 waves): every row of decode and the ragged mix,
+    200 sampled rows of the tie workload, against the oracle."""
+    c = gen.WORKLOADS[name]()
+    cap = (1 << levels) - 1
+    top_n = np.where(np.asarray(c.top_n) > 0, cap, 0).astype(np.int32)
+    dev = torch.device("cuda")
+    logits = gen.device_logits(c, dev, torch)
+    ntl = logits.index_select(0, torch.from_numpy(c.offsets[1:].astype(np.int64) - 1).to(dev))
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        c.offsets, logits if c.has_logits else None, ntl, c.tokens, c.sampled, top_n, c.echo,
+        levels=levels)
+    torch.cuda.synchronize()
+    nrows = lp.shape[0]
+    rng = np.random.default_rng(levels)
+    rows = sorted(set(rng.choice(nrows, size=min(n_sample, nrows), replace=False).tolist())
+                  | {0, nrows - 1})
+    log(f"{name} at levels {levels}: {len(rows)} of {nrows} rows compared")
+    ref = oracle(c.offsets, DeviceRows(logits) if c.has_logits else None, DeviceRows(ntl),
+                 c.tokens, c.sampled, top_n, c.echo, levels=levels, rows=rows)
+    assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), out_off, ref, f"{name} levels {levels}",
+                  rows=rows)
+    del logits, ntl, lp, ids
+    torch.cuda.empty_cache()
+
+
 def test_prefill_echo_large_full_size(R):
     _full_size(R, gen.prefill_echo_large(), 600, 41)
 

@@ -23,6 +23,8 @@ Beside it, each on the same run:
                   kernels from pinned host memory), then the launch.  Median,
                   p10 and p90 of the event intervals on the stream.  This is
                   the PCIe-inclusive rate; it is never `value`.
+  compute_noalloc lp_compute_ragged_noalloc per step, the same way (plans
+                  whose workspace fits its fixed 4 MiB).
   decode          the decode batch (256 rows of 128256, one boosted token per
                   row, top_n 7), measured the same way with its own roofline
                   fraction.
@@ -351,6 +353,8 @@ def _warm(calls, n_copies, steps, min_s, torch):
         torch.cuda.synchronize()
 
 
+NOALLOC_WORKSPACE_BYTES = 4 << 20   # lp_compute_ragged_noalloc's fixed workspace
+
 PROBE_SHAPES = [(segs, threads, loads) for segs in (1, 2, 4) for threads in (256, 512, 1024)
                 for loads in (1, 2, 4, 8)]
 
@@ -457,6 +461,21 @@ def measure(R, torch, dev, stream, case, args, steps, warmup, probe=True, extras
                                      note="lp_compute_ragged per step (host descriptor build, "
                                           "upload or, up to 262144 rows, reads from pinned host "
                                           "memory, launch); event interval on the stream")
+        # lp_compute_ragged_noalloc per step, where the plan fits its fixed
+        # workspace: up to 1984 rows the descriptors go in upload launches
+        # and the call waits for nothing; larger plans copy them
+        # synchronously, so the host waits for the stream at every call
+        if int(info["workspace_bytes"]) <= NOALLOC_WORKSPACE_BYTES:
+            na = [plan.noalloc_computer(*srcs(c), case.tokens, case.sampled, lp, ids, stream)
+                  for c in copies]
+            _warm(na, n_copies, 3, SUB_WARM_S, torch)
+            nper, _ = _timed_calls(na, n_copies, steps, stream, torch)
+            ns = _stats_us(nper)
+            rec["compute_noalloc"] = dict(
+                ns, rows_per_s=read_rows / (ns["median_us"] * 1e-6),
+                note="lp_compute_ragged_noalloc per step (the library's fixed workspace; up to "
+                     "1984 rows descriptors in upload-kernel arguments, else a synchronous "
+                     "copy); event interval on the stream")
         # leave the resident descriptors in place for the parity check
         plan.stage(case.tokens, case.sampled, ws, stream)
         launch[0]()
@@ -680,7 +699,7 @@ def main():
     }
     result["config"]["temperature"] = args.temperature if args.temperature is not None else 1.0
     result["config"]["top_k"] = args.top_k
-    for k in ("compute_ragged", "probe"):
+    for k in ("compute_ragged", "compute_noalloc", "probe"):
         if k in main_rec:
             result[k] = main_rec[k]
 

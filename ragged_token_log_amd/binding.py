@@ -410,6 +410,25 @@ class Plan:
                                                    _stream_ptr(stream)),
                "lp_compute_ragged_noalloc")
 
+    def noalloc_computer(self, logits, next_token_logits, tokens, sampled_tokens, out_logprobs,
+                         out_token_ids, stream=None):
+        """A zero-argument callable doing lp_compute_ragged_noalloc with these
+        buffers, its arguments checked and converted once (for timing loops);
+        it keeps the host id arrays and the tensors alive."""
+        tok, smp = self._token_arrays(tokens, sampled_tokens)
+        self._check_buffers(logits, next_token_logits, out_logprobs, out_token_ids)
+        fn = self._lib.lp_compute_ragged_noalloc
+        args = (self._h, _dev_ptr(logits), _dev_ptr(next_token_logits), _ptr(tok), _ptr(smp),
+                _dev_ptr(out_logprobs), _dev_ptr(out_token_ids), _stream_ptr(stream))
+        keep = (tok, smp, logits, next_token_logits, out_logprobs, out_token_ids, self)
+
+        def compute():
+            st = fn(*args)
+            if st != 0:
+                _check(st, "lp_compute_ragged_noalloc")
+            return keep
+        return compute
+
     def _shard_args(self, vocab_begin, shard_logits, shard_next_token_logits, records, workspace,
                     stream):
         t = shard_logits if self.has_logits else shard_next_token_logits

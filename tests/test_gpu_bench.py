@@ -36,6 +36,7 @@ def test_bench_line_on_a_small_workload():
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert d["value"] == pytest.approx(d["config"]["read_rows"] / (d["ms_per_step"] * 1e-3))
     assert d["compute_ragged"]["median_us"] > 0 and d["probe"]["us"] > 0
+    assert d["compute_noalloc"]["median_us"] > 0
     assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
     checks = d["cpu_baseline"]["timed_rows_check"]
     assert checks and all(c["mismatches"] == 0 and c["rows_checked"] > 0 for c in checks)

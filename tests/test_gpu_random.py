@@ -181,3 +181,55 @@ def test_random_plan_staged_then_launched(R, i):
     torch.cuda.synchronize()
     assert_parity(lp.cpu().numpy(), ids.cpu().numpy(), plan.out_off, ref, f"staged case {i}")
     plan.close()
+
+
+N_BATCH_CASES = 20
+
+
+@pytest.mark.parametrize("i", range(N_BATCH_CASES))
+def test_random_serving_batch(R, i):
+    """Serving-sized batches: 16-200 requests of 1-64 rows, vocabularies of
+    7919 to 151936, echo on about half the requests (or next-token logits
+    only), top_n and heap depth drawn, per-request temperatures and top-k
+    front ends on some; the device draws the logits.  Offsets bit for bit
+    and 64 sampled rows (plus the first and last) against the oracle."""
+    from tests.gpu_helpers import DeviceRows
+
+    rng = np.random.default_rng(600000 + i)
+    B = int(rng.integers(16, 201))
+    V = int(rng.choice([32000, 50257, 128256, 151936, 7919]))
+    levels = int(rng.integers(1, 7))
+    cap = LO.max_top_n(levels)
+    lengths = rng.integers(1, 65, B)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    T = int(off[-1])
+    has_logits = bool(rng.random() < 0.8)
+    echo = (rng.random(B) < 0.5) if has_logits else np.zeros(B, bool)
+    top_n = rng.integers(0, cap + 1, B)
+    temps = rng.choice(np.array([1.0, 0.5, 0.8, 1.5, 3.0], np.float32), B) \
+        if rng.random() < 0.3 else None
+    top_k = rng.integers(0, cap + 1, B) if rng.random() < 0.3 else None
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(600000 + i)
+    logits = torch.randn((T if has_logits else B, V), generator=g, device=dev) * 2.0
+    ntl = logits.index_select(0, torch.from_numpy(off[1:].astype(np.int64) - 1).to(dev)) \
+        if has_logits else logits
+    tokens = rng.integers(0, V, T).astype(np.uint32)
+    sampled = rng.integers(0, V, B).astype(np.uint32)
+    log(f"serving batch {i}: B={B} V={V} levels={levels} rows={T} logits={has_logits} "
+        f"temps={temps is not None} top_k={top_k is not None}")
+    lp, ids, out_off = R.compute_log_probabilities_ragged(
+        off, logits if has_logits else None, ntl, tokens, sampled, top_n, echo, levels=levels,
+        temperature=temps, top_k=top_k)
+    torch.cuda.synchronize()
+    nrows = lp.shape[0]
+    rows = sorted(set(rng.choice(nrows, size=min(64, nrows), replace=False).tolist())
+                  | {0, nrows - 1})
+    ref = LO.compute_log_probabilities_ragged(
+        off, DeviceRows(logits) if has_logits else None, DeviceRows(ntl), tokens, sampled,
+        list(top_n), list(echo), levels=levels, rows=rows, batch_temperature=temps,
+        batch_top_k=top_k)
+    assert np.array_equal(out_off, ref[2]), f"serving batch {i}: offsets"
+    assert np.array_equal(ids.cpu().numpy()[rows], ref[1][rows]), f"serving batch {i}: ids"
+    assert_close_rel(lp.cpu().numpy()[rows], ref[0][rows], f"serving batch {i}")
